@@ -1,0 +1,98 @@
+"""Sequential Markov draft loop, oracle side.
+
+Follows the DSparkSpeculator API page: ``_sample_sequential`` (the base draft
+logits are ordered (request, step) and the previous token of step 0 is the
+request's anchor, the input id at query offset 0), ``_sample_markov_chain``
+(for each step: embed the previous token, project the embedding into a
+vocabulary-wide Markov bias, add it to that step's base logits, sample, and
+feed the sample back as the previous token) and ``_sample_logits`` (the draw
+for predicted position P is keyed by P-1, temperature is applied, and the
+biased logits are stored into the draft-logits cache at column = step).
+
+Readings where the pages are silent (each listed in the design doc):
+
+* the Markov embedding of token x is row x of a bf16 matrix w1[V, r], with no
+  scale or normalisation, and the bias is w2[V, r] @ embedding (PR #65007,
+  Part 1, gives w2's shape [draft_vocab, markov_rank] and dtype bf16);
+* the bias is kept at full precision and the biased logit z = base + bias is
+  rounded once to float32;
+* the cache stores z before temperature, rounded to the cache dtype;
+* score s = z / T + g for T > 0 and s = z for a greedy (T = 0) request, in
+  float32 because the pages' Gumbel noise is float32 by default (PR #65007,
+  the fp64 Gumbel option listed under Part 1's unsupported configurations);
+* the winner is the first NaN, otherwise the first maximum (``argmax_rule``).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .core import argmax_rule, bf16_rne, bf16_to_f64, top_two_margin
+from .noise import SALT_DRAFT, gumbel_row
+
+
+def _logsumexp(x64: np.ndarray) -> float:
+    if np.isnan(x64).any():
+        return float("nan")
+    m = x64.max()
+    if not np.isfinite(m):
+        return float(m)
+    return float(m + np.log(np.exp(x64 - m).sum()))
+
+
+def draft_loop(base, base_dtype: str, w1_bits, w2_bits, anchor_tokens, anchor_pos, seeds, temperature,
+               cache_dtype: str, K: int | None = None, teacher=None, want_scores: bool = False) -> dict:
+    """Run the K-step Markov draft loop for every request.
+
+    base: [B, >=K, V] float32, or uint16 bf16 bit patterns when base_dtype is "bf16";
+    w1_bits, w2_bits: [V, r] uint16 bf16 bit patterns;
+    anchor_tokens [B], anchor_pos [B] (P0), seeds [B], temperature [B] (0 = greedy).
+    teacher: optional [B, K] tokens; when given, step k+1 uses teacher[:, k] as its
+    previous token instead of the oracle's own sample (each step then checks
+    independently against another implementation's tokens).
+
+    Returns tokens [B, K] int32, cache [B, K, V] (float32 or uint16 bf16 bits),
+    lse [B, K] float64 (log-sum-exp of cache / T; NaN for greedy rows) and
+    margin [B, K] float64 (top-two gap of the float32 scores).
+    """
+    base = np.asarray(base)
+    B, _, V = base.shape
+    K = base.shape[1] if K is None else int(K)
+    w1 = bf16_to_f64(w1_bits)
+    w2t = np.ascontiguousarray(bf16_to_f64(w2_bits).T)  # [r, V]
+    tokens = np.zeros((B, K), np.int32)
+    cache = np.zeros((B, K, V), np.uint16 if cache_dtype == "bf16" else np.float32)
+    lse = np.full((B, K), np.nan)
+    margin = np.zeros((B, K))
+    scores_out = np.zeros((B, K, V), np.float32) if want_scores else None
+    prev = np.asarray(anchor_tokens, dtype=np.int64).copy()
+    if (prev < 0).any() or (prev >= V).any():
+        raise ValueError("anchor token out of range")
+    for k in range(K):
+        emb = w1[prev]  # [B, r]: row gather (markov_embed)
+        bias = emb @ w2t  # [B, V]: markov_bias, exact products, float64 sums
+        row = bf16_to_f64(base[:, k]) if base_dtype == "bf16" else base[:, k].astype(np.float64)
+        z32 = (row + bias).astype(np.float32)  # one rounding
+        if cache_dtype == "bf16":
+            cbits = bf16_rne(z32)
+            cache[:, k] = cbits
+            cval = bf16_to_f64(cbits)
+        else:
+            cache[:, k] = z32
+            cval = z32.astype(np.float64)
+        for b in range(B):
+            T = np.float32(temperature[b])
+            if T > 0:
+                g32 = gumbel_row(int(seeds[b]), int(anchor_pos[b]) + k, SALT_DRAFT, V).astype(np.float32)
+                s = (z32[b] / T).astype(np.float32) + g32
+                lse[b, k] = _logsumexp(cval[b] / np.float64(T))
+            else:
+                s = z32[b]
+            tokens[b, k] = argmax_rule(s)
+            margin[b, k] = top_two_margin(s)
+            if want_scores:
+                scores_out[b, k] = s
+        prev = tokens[:, k].astype(np.int64) if teacher is None else np.asarray(teacher, np.int64)[:, k]
+    out = {"tokens": tokens, "cache": cache, "lse": lse, "margin": margin}
+    if want_scores:
+        out["scores"] = scores_out
+    return out
