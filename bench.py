@@ -1,0 +1,196 @@
+"""Benchmark of one draft + verify step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--batch 32]
+
+A step is one pass of the whole hot path over one batch: the K-step Markov
+draft loop (fused projection + sampling + cache write per step) followed by
+rejection verification, on synthetic inputs of the headline workload:
+V=200064, r=256 (w2 = 102 MB bf16), K=7, B=32, fp32 base logits, target and
+draft-logits cache. Inputs are resident in HBM before timing starts.
+
+Timing: W untimed steps, then S timed steps. Before each timed step a 512 MiB
+buffer is written so the Infinity Cache (MALL) and L2 hold none of the inputs
+(the target model's forward pass evicts them in serving); each step is timed
+with HIP events on the stream the kernels run on, and the flush is outside
+the events. The same steps run back to back without flushes are reported as
+`warm`. The fused Markov-step kernel is additionally timed per launch (events
+around each of its K launches) for the roofline entry.
+
+Prints one JSON line. One GPU only: --gpus N with N > 1 exits with an error.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "draft+verify tokens/s at V=200k,K=7,B=32; HBM GB/s % of MI355X peak"
+
+
+def algorithmic_bytes(B, K, V, r, s_base=4, s_cache=4, s_tgt=4):
+    """Bytes the method must move per step (each w2 byte once per Markov step)."""
+    draft_step = V * r * 2 + B * V * (s_base + s_cache)
+    draft = K * draft_step
+    verify = B * (K + 1) * V * s_tgt + B * V * (s_tgt + s_cache)
+    return draft_step, draft, verify
+
+
+def cpu_baseline(wl, n_req: int):
+    """The oracle, as it stands, on the first n_req requests of the workload."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+        ctx = threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover
+        ctx = None
+    rows = np.arange(n_req)
+    K = wl.K
+    t0 = time.perf_counter()
+    d = oracle.draft_loop(wl.draft_base[rows], wl.base_dtype, wl.w1, wl.w2, wl.anchor_tokens[rows],
+                          wl.anchor_pos[rows], wl.seeds[rows], wl.temperature[rows], wl.cache_dtype)
+    tgt = wl.target.reshape(wl.B, K + 1, wl.V)[rows].reshape(n_req * (K + 1), wl.V)
+    oracle.verify(tgt, d["cache"], wl.cache_dtype, d["tokens"], wl.temperature[rows],
+                  None if wl.top_p is None else wl.top_p[rows], wl.seeds[rows], wl.anchor_pos[rows])
+    dt = time.perf_counter() - t0
+    if ctx is not None:
+        ctx.unregister() if hasattr(ctx, "unregister") else None
+    return {"value": n_req * K / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_req} of the {wl.B} requests (all {K} draft steps + verification), "
+                      f"float64 NumPy, BLAS limited to 1 thread; {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--batch", type=int, default=32)
+    ap.add_argument("--cpu-sample", type=int, default=8, help="requests the CPU oracle baseline runs on")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true", help="do not flush caches between timed steps")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print("bench.py runs on one GPU only: the path is measured on a single MI355X "
+              "(no multi-GPU code is part of this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import markov_draft_sampling_amd as mds
+    import workloads
+
+    assert torch.cuda.is_available(), "no GPU"
+    dev = torch.device("cuda:0")
+    t_gen = time.perf_counter()
+    wl = workloads.make_workload(4, B=a.batch)
+    B, K, V, r = wl.B, wl.K, wl.V, wl.r
+    print(f"# workload V={V} r={r} K={K} B={B} generated in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr,
+          flush=True)
+
+    base = torch.from_numpy(wl.base).to(dev)  # [B, K+1, V]; the draft reads rows 0..K-1
+    target = torch.from_numpy(wl.target).to(dev)
+    w1 = torch.from_numpy(wl.w1.view(np.int16)).view(torch.bfloat16).to(dev)
+    w2 = torch.from_numpy(wl.w2.view(np.int16)).view(torch.bfloat16).to(dev)
+    anchor = torch.from_numpy(wl.anchor_tokens).to(dev)
+    apos = torch.from_numpy(wl.anchor_pos).to(dev)
+    temp = torch.from_numpy(wl.temperature).to(dev)
+    seeds = torch.from_numpy(wl.seeds).to(dev)
+    cache = torch.empty((B, K, V), dtype=torch.float32, device=dev)
+    toks = torch.empty((B, K), dtype=torch.int32, device=dev)
+    lse = torch.empty((B, K), dtype=torch.float32, device=dev)
+    out = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    nacc = torch.empty((B,), dtype=torch.int32, device=dev)
+    ws_d = mds.new_workspace(mds.draft_workspace_bytes(B, K, V, r), dev)
+    ws_v = mds.new_workspace(mds.verify_workspace_bytes(B, K, V, False, True), dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(events=None):
+        if events is None:
+            mds.markov_draft_loop(base, w1, w2, anchor, apos, temp, seeds, cache, toks, lse, workspace=ws_d)
+        else:
+            mds.markov_draft_loop_timed(base, w1, w2, anchor, apos, temp, seeds, cache, toks, lse, ws_d, events)
+        mds.rejection_verify(target, cache, toks, temp, seeds, apos, out, nacc, draft_lse=lse, workspace=ws_v)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    starts, ends = [ev() for _ in range(a.steps)], [ev() for _ in range(a.steps)]
+    kev = [[ev() for _ in range(2 * K)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        if not a.no_flush:
+            flush.fill_(i & 0xFF)
+        starts[i].record(stream)
+        step(kev[i])
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    kern_ms = np.array([[kev[i][2 * k].elapsed_time(kev[i][2 * k + 1]) for k in range(K)] for i in range(a.steps)])
+
+    # back to back, caches warm
+    w0, w1e = ev(), ev()
+    w0.record(stream)
+    for _ in range(a.steps):
+        step()
+    w1e.record(stream)
+    torch.cuda.synchronize()
+    warm_ms = w0.elapsed_time(w1e) / a.steps
+
+    ms = float(np.mean(step_ms))
+    tokens = B * K
+    draft_step_b, draft_b, verify_b = algorithmic_bytes(B, K, V, r)
+    kern_avg_ms = float(np.mean(kern_ms))
+    achieved = draft_step_b / (kern_avg_ms * 1e-3) / 1e9
+    step_gbps = (draft_b + verify_b) / (ms * 1e-3) / 1e9
+    acc_len = float((nacc.float() + 1).mean().item())
+    status = mds.workspace_status(ws_d) | mds.workspace_status(ws_v)
+
+    res = {
+        "metric": METRIC,
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"Markov draft loop + rejection verify, V={V} r={r} K={K} B={B}, fp32 base/target/"
+                               f"cache, bf16 w1/w2, T=1",
+                   "V": V, "r": r, "K": K, "B": B, "cache_flushed_between_steps": not a.no_flush},
+        "hbm": {"algorithmic_bytes_per_step": draft_b + verify_b, "achieved_GBps": step_gbps,
+                "peak_GBps": HBM_PEAK_GBPS, "frac": step_gbps / HBM_PEAK_GBPS},
+        "roofline": {"kernel": "draft_step_kernel (fused projection + sampling + cache write, one Markov step)",
+                     "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "bytes_per_launch": draft_step_b, "avg_launch_us": kern_avg_ms * 1e3,
+                     "launches": int(kern_ms.size)},
+        "warm": {"ms_per_step": warm_ms, "value": tokens / (warm_ms * 1e-3)},
+        "step_ms_p10_p50_p90": [float(np.percentile(step_ms, q)) for q in (10, 50, 90)],
+        "draft_ms": float(np.mean(kern_ms.sum(1))),
+        "acceptance_length": acc_len,
+        "status_word": status,
+        "timed_wall_s": wall,
+    }
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, min(a.cpu_sample, B))
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

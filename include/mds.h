@@ -1,0 +1,208 @@
+/*
+ * mds.h - C-ABI of the MI355X (gfx950) Markov draft-sampling library (libmds.so).
+ *
+ * The library runs the hot path of DSpark speculative decoding on one GPU:
+ *   1. the sequential Markov draft loop (DSparkSpeculator API page, methods
+ *      _sample_markov_chain / _sample_logits; vLLM PR #65007 "vocab-parallel
+ *      DSpark Markov sampling", section Part 1), and
+ *   2. rejection-sampling verification of the drafts, with optional exact
+ *      top-p on the target (PR #65007, Overview and Part 2; PR #63554 Notes
+ *      for greedy requests).
+ *
+ * Conventions for every entry point:
+ *   - All array arguments are DEVICE pointers owned by the caller. The library
+ *     allocates nothing, never synchronises the device, keeps no pointer after
+ *     returning, and enqueues all its work on `stream` (a hipStream_t passed
+ *     as void*; NULL means the default stream). Calls can be captured in a
+ *     HIP graph.
+ *   - Scalars (sizes, strides, dtypes) are validated on the host before
+ *     anything is launched; device memory is never dereferenced by the host.
+ *     On a validation failure nothing is enqueued and a negative MDS_ERR_*
+ *     code is returned; mds_last_error() then holds a message (per thread).
+ *   - Strides are in ELEMENTS of the array's dtype. Vector (16-byte) access is
+ *     used when pointers and strides allow it; any stride >= V works.
+ *   - Values derived from device data that are out of contract (an anchor or
+ *     draft token outside [0, V)) cannot be rejected on the host. The kernels
+ *     then substitute token 0 and set a bit in the workspace's sticky status
+ *     word (the first 4 bytes of the workspace, see MDS_STATUS_*). The
+ *     library never clears that word: the caller zeroes the workspace once
+ *     when allocating it and reads the word after a synchronisation.
+ *   - Logits must be finite or NaN; +-inf inputs are outside the contract.
+ *   - Outputs must not alias inputs; the cache must not alias base or target.
+ *   - Calls that share a workspace must be ordered (same stream).
+ */
+#ifndef MDS_H_
+#define MDS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MDS_ABI_VERSION 1
+
+/* return codes */
+#define MDS_OK 0
+#define MDS_ERR_INVALID_ARG (-1)      /* a size, stride, pointer or dtype is invalid */
+#define MDS_ERR_UNSUPPORTED (-2)      /* valid but not supported by this build (e.g. r not a multiple of 32) */
+#define MDS_ERR_WORKSPACE (-3)        /* workspace smaller than the matching *_workspace_bytes() */
+#define MDS_ERR_HIP (-4)              /* a HIP runtime call or kernel launch failed */
+
+/* element types */
+#define MDS_F32 0
+#define MDS_BF16 1
+
+/* sticky status bits (workspace word 0) */
+#define MDS_STATUS_BAD_ANCHOR 1u      /* an anchor token was outside [0, V); token 0 was used */
+#define MDS_STATUS_BAD_DRAFT 2u       /* a draft token given to verification was outside [0, V); token 0 was used */
+
+/* sampling salts: the draft salt is the pages' draft-noise salt (1 << 30) */
+#define MDS_SALT_DRAFT (1u << 30)
+#define MDS_SALT_ACCEPT 1u
+#define MDS_SALT_RESAMPLE 2u
+
+/* Version of this ABI (MDS_ABI_VERSION of the build). */
+int mds_abi_version(void);
+
+/* Static description of a return code. */
+const char* mds_status_string(int status);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* mds_last_error(void);
+
+/*
+ * Workspace sizes (bytes) for the two calls at the given sizes. Pure host
+ * functions: they need no GPU. Limits: 1 <= B <= 65535, 1 <= K <= 32,
+ * 2 <= V < 2^24, 32 <= r <= 512 with r % 32 == 0.
+ */
+int mds_draft_workspace_bytes(int B, int K, int V, int r, size_t* out_bytes);
+int mds_verify_workspace_bytes(int B, int K, int V, int has_top_p, int has_draft_lse, size_t* out_bytes);
+
+/*
+ * mds_markov_draft_loop - the K sequential Markov draft steps for B requests.
+ *
+ * For request b, with prev_0 = anchor_tokens[b] and P0 = anchor_pos[b], step
+ * k = 0..K-1 computes, for every column v < V
+ * (DSparkSpeculator API page, _sample_markov_chain and _sample_logits):
+ *   e          = w1[prev_k, 0:r]                          (Markov embedding)
+ *   bias[v]    = sum_j w2[v, j] * e[j]                    (Markov bias, fp32 accumulation)
+ *   z[v]       = float(base[b, k, v]) + bias[v]           (fp32)
+ *   cache[b,k,v] = z[v] rounded to the cache dtype         (pre-temperature biased logits)
+ *   s[v]       = z[v] / T_b + Gumbel(seed_b, P0 + k, v)   if T_b > 0; s[v] = z[v] if T_b == 0
+ *   token      = first NaN column of s, else first maximum (PR #65007, Part 1)
+ * and feeds token back as prev_{k+1}. The draw for the token at position
+ * P0+1+k is keyed by the position before it, P0+k; the Gumbel variate of
+ * column v is -log(-log u) with u = (2*(w >> 9) + 1) * 2^-24 and w = word
+ * (v & 3) of Philox4x32-10(counter = (v >> 2, lo32(P0+k), hi32(P0+k),
+ * MDS_SALT_DRAFT), key = (lo32(seed), hi32(seed))).
+ *
+ * Arguments (device pointers unless stated):
+ *   B, K, V, r            batch, draft steps, vocabulary, Markov rank (host ints)
+ *   base, base_dtype      base draft logits, MDS_F32 or MDS_BF16; element (b, k, v) at
+ *                         b*base_req_stride + k*base_step_stride + v
+ *   w1, w2                bf16 [V, r] row-major (row stride r), 4-byte aligned
+ *   anchor_tokens         int32 [B]   previous token of step 0
+ *   anchor_pos            int64 [B]   position P0 of the anchor token
+ *   temperature           float [B]   > 0 sampled request, == 0 greedy request
+ *   seeds                 int64 [B]   per-request seed
+ *   cache, cache_dtype    draft-logits cache (written), MDS_F32 or MDS_BF16; element
+ *                         (b, k, v) at b*cache_req_stride + k*cache_step_stride + v
+ *   draft_tokens          int32 [B, K] (written), row-major
+ *   draft_lse             float [B, K] (written, nullable): log-sum-exp over v of
+ *                         cache[b,k,v] / T_b, the normaliser of the draft distribution
+ *                         q_k that verification needs (NaN if the row holds NaN,
+ *                         unspecified for greedy requests)
+ *   workspace             >= mds_draft_workspace_bytes(B, K, V, r) bytes, 256-byte aligned
+ *   stream                hipStream_t as void*
+ */
+int mds_markov_draft_loop(int B, int K, int V, int r,
+                          const void* base, int base_dtype, int64_t base_req_stride, int64_t base_step_stride,
+                          const void* w1, const void* w2,
+                          const int32_t* anchor_tokens, const int64_t* anchor_pos,
+                          const float* temperature, const int64_t* seeds,
+                          void* cache, int cache_dtype, int64_t cache_req_stride, int64_t cache_step_stride,
+                          int32_t* draft_tokens, float* draft_lse,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mds_rejection_verify - verify the K drafts of B requests against the target.
+ *
+ * Target row j of request b (position P0+1+j) is at
+ * target + (b*(K+1) + j)*target_row_stride, j = 0..K.
+ * Greedy request (T_b == 0), PR #63554 Notes: a_j = first-NaN-else-first-max
+ * of target row j; drafts are accepted while draft[b,k] == a_k; the final
+ * token is a_n at the first mismatch n (a_K if all match); the cache is not read.
+ * Sampled request (T_b > 0), PR #65007 Overview/Part 2:
+ *   p_j = softmax(target row j / T_b), restricted when top_p[b] < 1 to the
+ *         smallest prefix in (logit desc, token id asc) order whose mass
+ *         reaches top_p[b], plus the row maximum, and renormalised;
+ *   q_k = softmax(cache[b,k,:] / T_b) (q from draft_lse when given);
+ *   draft k is accepted iff p_k(x) >= u_k * q_k(x), u_k = uniform of column 0
+ *         of the MDS_SALT_ACCEPT stream keyed (seed_b, P0+k);
+ *   at the first rejection j the final token is drawn from
+ *         max(0, p_j - q_j) normalised (from p_j if that is all zero, or if
+ *         q_j is NaN) and when all K are accepted from p_K: Gumbel-max over
+ *         log of that distribution plus noise of the MDS_SALT_RESAMPLE
+ *         stream keyed (seed_b, P0+j).
+ * Outputs: out_tokens int32 [B, K+1] = accepted drafts, the final token, then
+ * -1 padding; num_accepted int32 [B].
+ *
+ * Arguments:
+ *   target                float [B*(K+1), V] rows as above, target_row_stride >= V
+ *   cache, cache_dtype    as written by mds_markov_draft_loop (strides in elements)
+ *   draft_lse             float [B, K] from mds_markov_draft_loop, or NULL to recompute
+ *                         it from the cache (one extra read of the cache)
+ *   draft_tokens          int32 [B, K]
+ *   temperature, seeds, anchor_pos   as for the draft loop
+ *   top_p                 float [B] or NULL (off); a value >= 1 turns it off for that request
+ *   workspace             >= mds_verify_workspace_bytes(B, K, V, top_p != NULL,
+ *                         draft_lse != NULL) bytes, 256-byte aligned
+ */
+int mds_rejection_verify(int B, int K, int V,
+                         const float* target, int64_t target_row_stride,
+                         const void* cache, int cache_dtype, int64_t cache_req_stride, int64_t cache_step_stride,
+                         const float* draft_lse, const int32_t* draft_tokens,
+                         const float* temperature, const float* top_p,
+                         const int64_t* seeds, const int64_t* anchor_pos,
+                         int32_t* out_tokens, int32_t* num_accepted,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mds_markov_draft_loop_timed - mds_markov_draft_loop that also records
+ * events[2*k] before and events[2*k+1] after the step-k kernel (k = 0..K-1)
+ * on `stream`, so a caller can measure the fused step kernel alone.
+ * events: host array of 2*K hipEvent_t (as void*), created by the caller.
+ */
+int mds_markov_draft_loop_timed(int B, int K, int V, int r,
+                                const void* base, int base_dtype, int64_t base_req_stride, int64_t base_step_stride,
+                                const void* w1, const void* w2,
+                                const int32_t* anchor_tokens, const int64_t* anchor_pos,
+                                const float* temperature, const int64_t* seeds,
+                                void* cache, int cache_dtype, int64_t cache_req_stride, int64_t cache_step_stride,
+                                int32_t* draft_tokens, float* draft_lse,
+                                void* workspace, size_t workspace_bytes, void* stream, void* const* events);
+
+/*
+ * mds_debug_noise - test hook: writes for n columns cols[i] the Philox word
+ * and the float32 Gumbel variate of the stream (seed, pos_key, salt) exactly as
+ * the sampling kernels compute them. cols int32 [n], words uint32 [n],
+ * gumbel float [n] (device pointers). Used by the tests to compare the device
+ * noise with an independent implementation.
+ */
+int mds_debug_noise(int n, const int32_t* cols, int64_t seed, int64_t pos_key, uint32_t salt,
+                    uint32_t* words, float* gumbel, void* stream);
+
+/*
+ * mds_debug_gumbel - test hook: the float32 Gumbel variate the kernels derive
+ * from each given 32-bit word (device arrays of n elements). Only the top 23
+ * bits of a word matter, so 2^23 words cover every possible variate.
+ */
+int mds_debug_gumbel(int n, const uint32_t* words, float* gumbel, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MDS_H_ */

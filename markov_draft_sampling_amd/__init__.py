@@ -1,0 +1,249 @@
+"""Python binding of libmds.so, the MI355X Markov draft-sampling library.
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+libmds.so. Tensors are torch CUDA (ROCm) tensors; the calls enqueue work on
+the current torch stream (or the given one) and return without synchronising.
+The C entry points are declared in include/mds.h; the functions here carry
+the same names without the ``mds_`` prefix.
+
+The library must have been built in-tree (``python -m
+markov_draft_sampling_amd.build``); importing this module does not build it,
+and every call fails with an error if it is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "F32", "BF16", "MdsError", "library_path", "abi_version", "draft_workspace_bytes", "verify_workspace_bytes",
+    "new_workspace", "workspace_status", "markov_draft_loop", "markov_draft_loop_timed", "rejection_verify",
+    "debug_noise", "debug_gumbel", "STATUS_BAD_ANCHOR", "STATUS_BAD_DRAFT", "SALT_DRAFT", "SALT_ACCEPT",
+    "SALT_RESAMPLE",
+]
+
+F32, BF16 = 0, 1
+STATUS_BAD_ANCHOR, STATUS_BAD_DRAFT = 1, 2
+SALT_DRAFT, SALT_ACCEPT, SALT_RESAMPLE = 1 << 30, 1, 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class MdsError(RuntimeError):
+    pass
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libmds.so")
+
+
+_c_int, _c_i64, _c_sz, _vp = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+
+_SIGS = {
+    "mds_abi_version": ([], _c_int),
+    "mds_status_string": ([_c_int], ctypes.c_char_p),
+    "mds_last_error": ([], ctypes.c_char_p),
+    "mds_draft_workspace_bytes": ([_c_int, _c_int, _c_int, _c_int, ctypes.POINTER(_c_sz)], _c_int),
+    "mds_verify_workspace_bytes": ([_c_int, _c_int, _c_int, _c_int, _c_int, ctypes.POINTER(_c_sz)], _c_int),
+    "mds_markov_draft_loop": ([_c_int] * 4 + [_vp, _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int,
+                                              _c_i64, _c_i64, _vp, _vp, _vp, _c_sz, _vp], _c_int),
+    "mds_markov_draft_loop_timed": ([_c_int] * 4 + [_vp, _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                    _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _c_sz, _vp, _vp], _c_int),
+    "mds_rejection_verify": ([_c_int] * 3 + [_vp, _c_i64, _vp, _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp,
+                                             _vp, _vp, _vp, _c_sz, _vp], _c_int),
+    "mds_debug_noise": ([_c_int, _vp, _c_i64, _c_i64, ctypes.c_uint32, _vp, _vp, _vp], _c_int),
+    "mds_debug_gumbel": ([_c_int, _vp, _vp, _vp], _c_int),
+}
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise MdsError(f"{path} is missing: build it with `python -m markov_draft_sampling_amd.build`")
+        lib = ctypes.CDLL(path)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = res
+        _LIB = lib
+    return _LIB
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        lib = _lib()
+        msg = lib.mds_last_error().decode()
+        raise MdsError(f"{what}: {lib.mds_status_string(rc).decode()} ({rc}): {msg}")
+
+
+def abi_version() -> int:
+    return _lib().mds_abi_version()
+
+
+def draft_workspace_bytes(B: int, K: int, V: int, r: int) -> int:
+    out = _c_sz()
+    _check(_lib().mds_draft_workspace_bytes(B, K, V, r, ctypes.byref(out)), "draft_workspace_bytes")
+    return out.value
+
+
+def verify_workspace_bytes(B: int, K: int, V: int, has_top_p: bool, has_draft_lse: bool) -> int:
+    out = _c_sz()
+    _check(_lib().mds_verify_workspace_bytes(B, K, V, int(has_top_p), int(has_draft_lse), ctypes.byref(out)),
+           "verify_workspace_bytes")
+    return out.value
+
+
+def new_workspace(nbytes: int, device=None):
+    """A zeroed uint8 device buffer usable as a workspace (zeroed once: the
+    library never clears its sticky status word)."""
+    import torch
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device or "cuda")
+
+
+def workspace_status(ws) -> int:
+    """The sticky status word (MDS_STATUS_* bits); synchronises on the read."""
+    return int(ws[:4].view(dtype=__import__("torch").int32).item())
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise MdsError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else _vp(t.data_ptr())
+
+
+def _stream(stream, device):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return _vp(s.cuda_stream)
+
+
+def _need(cond, msg):
+    if not cond:
+        raise MdsError(msg)
+
+
+def _draft_args(base, w1, w2, anchor_tokens, anchor_pos, temperature, seeds, cache, draft_tokens, draft_lse,
+                workspace):
+    import torch
+    _need(base.is_cuda, "tensors must be on the GPU")
+    _need(base.dim() == 3 and base.stride(2) == 1, "base must be [B, >=K, V] with unit column stride")
+    _need(cache.dim() == 3 and cache.stride(2) == 1, "cache must be [B, K, V] with unit column stride")
+    B, K = draft_tokens.shape
+    V = base.shape[2]
+    _need(base.shape[0] == B and base.shape[1] >= K, "base must hold K rows per request")
+    _need(tuple(cache.shape) == (B, K, V), "cache must be [B, K, V]")
+    _need(w1.dtype == torch.bfloat16 and w2.dtype == torch.bfloat16, "w1 and w2 must be bf16")
+    _need(w1.is_contiguous() and w2.is_contiguous() and w1.shape == w2.shape and w1.shape[0] == V,
+          "w1 and w2 must be contiguous [V, r]")
+    _need(anchor_tokens.dtype == torch.int32 and anchor_tokens.numel() == B, "anchor_tokens must be int32 [B]")
+    _need(anchor_pos.dtype == torch.int64 and anchor_pos.numel() == B, "anchor_pos must be int64 [B]")
+    _need(temperature.dtype == torch.float32 and temperature.numel() == B, "temperature must be float32 [B]")
+    _need(seeds.dtype == torch.int64 and seeds.numel() == B, "seeds must be int64 [B]")
+    _need(draft_tokens.dtype == torch.int32 and draft_tokens.is_contiguous(), "draft_tokens must be int32 [B, K]")
+    for t in (anchor_tokens, anchor_pos, temperature, seeds):
+        _need(t.is_contiguous(), "per-request arrays must be contiguous")
+    if draft_lse is not None:
+        _need(draft_lse.dtype == torch.float32 and draft_lse.is_contiguous() and draft_lse.numel() == B * K,
+              "draft_lse must be float32 [B, K]")
+    _need(workspace.dtype == torch.uint8 and workspace.is_contiguous(), "workspace must be a contiguous uint8 tensor")
+    r = w1.shape[1]
+    return (B, K, V, r, _ptr(base), _dtype_code(base), base.stride(0), base.stride(1), _ptr(w1), _ptr(w2),
+            _ptr(anchor_tokens), _ptr(anchor_pos), _ptr(temperature), _ptr(seeds), _ptr(cache), _dtype_code(cache),
+            cache.stride(0), cache.stride(1), _ptr(draft_tokens), _ptr(draft_lse), _ptr(workspace),
+            workspace.numel())
+
+
+def markov_draft_loop(base, w1, w2, anchor_tokens, anchor_pos, temperature, seeds, cache, draft_tokens,
+                      draft_lse=None, workspace=None, stream=None):
+    """Run the K-step Markov draft loop (mds_markov_draft_loop); K = draft_tokens.shape[1].
+
+    Writes cache [B, K, V], draft_tokens [B, K] int32 and, if given,
+    draft_lse [B, K] float32. Returns the workspace used.
+    """
+    B, K = draft_tokens.shape
+    if workspace is None:
+        workspace = new_workspace(draft_workspace_bytes(B, K, base.shape[2], w1.shape[1]), base.device)
+    args = _draft_args(base, w1, w2, anchor_tokens, anchor_pos, temperature, seeds, cache, draft_tokens, draft_lse,
+                       workspace)
+    _check(_lib().mds_markov_draft_loop(*args, _stream(stream, base.device)), "markov_draft_loop")
+    return workspace
+
+
+def markov_draft_loop_timed(base, w1, w2, anchor_tokens, anchor_pos, temperature, seeds, cache, draft_tokens,
+                            draft_lse, workspace, events, stream=None):
+    """markov_draft_loop recording events[2k] / events[2k+1] around step kernel k.
+
+    events: list of 2*K torch.cuda.Event(enable_timing=True), recorded on the
+    stream the kernels run on.
+    """
+    B, K = draft_tokens.shape
+    _need(len(events) == 2 * K, "need 2*K events")
+    args = _draft_args(base, w1, w2, anchor_tokens, anchor_pos, temperature, seeds, cache, draft_tokens, draft_lse,
+                       workspace)
+    arr = (_vp * (2 * K))(*[_vp(e.cuda_event) for e in events])
+    _check(_lib().mds_markov_draft_loop_timed(*args, _stream(stream, base.device), arr), "markov_draft_loop_timed")
+    return workspace
+
+
+def rejection_verify(target, cache, draft_tokens, temperature, seeds, anchor_pos, out_tokens, num_accepted,
+                     draft_lse=None, top_p=None, workspace=None, stream=None):
+    """Rejection-sampling verification (mds_rejection_verify).
+
+    target: float32 [B*(K+1), V] (unit column stride); cache as written by the
+    draft loop; writes out_tokens [B, K+1] int32 and num_accepted [B] int32.
+    """
+    import torch
+    B, K = draft_tokens.shape
+    V = target.shape[1]
+    _need(target.is_cuda and target.dtype == torch.float32, "target must be a float32 GPU tensor")
+    _need(target.dim() == 2 and target.shape[0] == B * (K + 1) and target.stride(1) == 1,
+          "target must be [B*(K+1), V] with unit column stride")
+    _need(cache.dim() == 3 and tuple(cache.shape) == (B, K, V) and cache.stride(2) == 1, "cache must be [B, K, V]")
+    _need(out_tokens.dtype == torch.int32 and out_tokens.is_contiguous() and out_tokens.numel() == B * (K + 1),
+          "out_tokens must be int32 [B, K+1]")
+    _need(num_accepted.dtype == torch.int32 and num_accepted.numel() == B, "num_accepted must be int32 [B]")
+    _need(draft_tokens.dtype == torch.int32 and draft_tokens.is_contiguous(), "draft_tokens must be int32 [B, K]")
+    if top_p is not None:
+        _need(top_p.dtype == torch.float32 and top_p.numel() == B and top_p.is_contiguous(), "top_p: float32 [B]")
+    if draft_lse is not None:
+        _need(draft_lse.dtype == torch.float32 and draft_lse.numel() == B * K, "draft_lse: float32 [B, K]")
+    if workspace is None:
+        workspace = new_workspace(verify_workspace_bytes(B, K, V, top_p is not None, draft_lse is not None),
+                                  target.device)
+    rc = _lib().mds_rejection_verify(B, K, V, _ptr(target), target.stride(0), _ptr(cache), _dtype_code(cache),
+                                     cache.stride(0), cache.stride(1), _ptr(draft_lse), _ptr(draft_tokens),
+                                     _ptr(temperature), _ptr(top_p), _ptr(seeds), _ptr(anchor_pos), _ptr(out_tokens),
+                                     _ptr(num_accepted), _ptr(workspace), workspace.numel(),
+                                     _stream(stream, target.device))
+    _check(rc, "rejection_verify")
+    return workspace
+
+
+def debug_noise(cols, seed: int, pos_key: int, salt: int):
+    """Device Philox words and float32 Gumbel variates for int32 columns `cols`."""
+    import torch
+    _need(cols.is_cuda and cols.dtype == torch.int32 and cols.is_contiguous(), "cols must be int32 on the GPU")
+    words = torch.empty(cols.numel(), dtype=torch.int32, device=cols.device)
+    g = torch.empty(cols.numel(), dtype=torch.float32, device=cols.device)
+    _check(_lib().mds_debug_noise(cols.numel(), _ptr(cols), int(seed), int(pos_key), int(salt), _ptr(words), _ptr(g),
+                                  _stream(None, cols.device)), "debug_noise")
+    return words, g
+
+
+def debug_gumbel(words):
+    """float32 Gumbel variates the kernels derive from 32-bit words (int32 tensor)."""
+    import torch
+    _need(words.is_cuda and words.dtype == torch.int32 and words.is_contiguous(), "words must be int32 on the GPU")
+    g = torch.empty(words.numel(), dtype=torch.float32, device=words.device)
+    _check(_lib().mds_debug_gumbel(words.numel(), _ptr(words), _ptr(g), _stream(None, words.device)), "debug_gumbel")
+    return g

@@ -1,0 +1,299 @@
+// extern "C" entry points of libmds.so: argument validation on the host,
+// workspace layout, and the kernel sequence on the caller's stream. See
+// include/mds.h for the contract of each call.
+#include <string>
+
+#include "../../include/mds.h"
+#include "mds_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return MDS_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_sizes(int B, int K, int V) {
+  if (B < 1 || B > 65535) return fail(MDS_ERR_INVALID_ARG, "B must be in [1, 65535]");
+  if (K < 1 || K > 32) return fail(MDS_ERR_INVALID_ARG, "K must be in [1, 32]");
+  if (V < 2 || V >= (1 << 24)) return fail(MDS_ERR_INVALID_ARG, "V must be in [2, 2^24)");
+  return MDS_OK;
+}
+
+int check_rank(int r) {
+  if (r < 32 || r > 512) return fail(MDS_ERR_INVALID_ARG, "r must be in [32, 512]");
+  if (r % 32) return fail(MDS_ERR_UNSUPPORTED, "r must be a multiple of 32");
+  return MDS_OK;
+}
+
+// rows (b, k) of a [B, K, V] view must not overlap when written
+bool rows_disjoint(int B, int K, int V, long long rs, long long ss) {
+  if (rs < 0 || ss < 0) return false;
+  if (B == 1 && K == 1) return true;
+  if (B == 1) return ss >= V;
+  if (K == 1) return rs >= V;
+  return (ss >= V && rs >= (long long)(K - 1) * ss + V) || (rs >= V && ss >= (long long)(B - 1) * rs + V);
+}
+
+bool vec_ok(const void* p, int dtype, long long rs, long long ss) {
+  return aligned(p, dtype == MDS_BF16 ? 8 : 16) && rs % 4 == 0 && ss % 4 == 0;
+}
+
+struct DraftLayout {
+  int G, nMT;
+  size_t keys, qpart, total;
+};
+
+DraftLayout draft_layout(int B, int K, int V) {
+  DraftLayout L;
+  L.nMT = (V + 15) / 16;
+  L.G = mds::draft_slabs(V);
+  L.keys = kAlign;
+  L.qpart = L.keys + up((size_t)K * B * 8);
+  L.total = L.qpart + up((size_t)K * B * L.G * sizeof(float2));
+  return L;
+}
+
+struct VerifyLayout {
+  int NC;
+  size_t tpart, qpart, qlse, topp, req, rpart, total;
+};
+
+VerifyLayout verify_layout(int B, int K, int V, bool top_p, bool has_lse) {
+  VerifyLayout L;
+  L.NC = (V + mds::kStatsChunk - 1) / mds::kStatsChunk;
+  size_t o = kAlign;
+  L.tpart = o;
+  o += up((size_t)B * (K + 1) * L.NC * sizeof(mds::StatPart));
+  L.qpart = has_lse ? 0 : o;
+  if (!has_lse) o += up((size_t)B * K * L.NC * sizeof(mds::StatPart));
+  L.qlse = 0;
+  L.topp = top_p ? o : 0;
+  if (top_p) o += up((size_t)B * (K + 1) * sizeof(mds::TopP));
+  L.req = o;
+  o += up((size_t)B * sizeof(mds::ReqState));
+  L.rpart = o;
+  o += up((size_t)B * L.NC * sizeof(mds::ResPart));
+  L.total = o;
+  return L;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(MDS_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+int draft_impl(int B, int K, int V, int r, const void* base, int base_dtype, int64_t base_rs, int64_t base_ss,
+               const void* w1, const void* w2, const int32_t* anchor, const int64_t* anchor_pos,
+               const float* temperature, const int64_t* seeds, void* cache, int cache_dtype, int64_t cache_rs,
+               int64_t cache_ss, int32_t* draft_tokens, float* draft_lse, void* workspace, size_t ws_bytes,
+               void* stream, void* const* events) {
+  int rc;
+  if ((rc = check_sizes(B, K, V)) || (rc = check_rank(r))) return rc;
+  if (!base || !w1 || !w2 || !anchor || !anchor_pos || !temperature || !seeds || !cache || !draft_tokens ||
+      !workspace)
+    return fail(MDS_ERR_INVALID_ARG, "a required pointer is NULL");
+  if ((base_dtype != MDS_F32 && base_dtype != MDS_BF16) || (cache_dtype != MDS_F32 && cache_dtype != MDS_BF16))
+    return fail(MDS_ERR_INVALID_ARG, "dtype must be MDS_F32 or MDS_BF16");
+  if (base_rs < 0 || base_ss < 0) return fail(MDS_ERR_INVALID_ARG, "base strides must be >= 0");
+  if (!rows_disjoint(B, K, V, cache_rs, cache_ss))
+    return fail(MDS_ERR_INVALID_ARG, "cache strides make rows overlap or are shorter than V");
+  if (!aligned(w1, 16) || !aligned(w2, 16)) return fail(MDS_ERR_INVALID_ARG, "w1 and w2 must be 16-byte aligned");
+  if (!aligned(workspace, kAlign)) return fail(MDS_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const DraftLayout L = draft_layout(B, K, V);
+  if (ws_bytes < L.total) return fail(MDS_ERR_WORKSPACE, "workspace too small for the draft loop");
+  unsigned char* ws = (unsigned char*)workspace;
+  hipStream_t st = (hipStream_t)stream;
+  mds::DraftStepArgs a{};
+  a.B = B;
+  a.K = K;
+  a.V = V;
+  a.r = r;
+  a.G = L.G;
+  a.nMT = L.nMT;
+  a.base_bf16 = base_dtype == MDS_BF16;
+  a.cache_bf16 = cache_dtype == MDS_BF16;
+  a.vec_base = vec_ok(base, base_dtype, base_rs, base_ss);
+  a.vec_cache = vec_ok(cache, cache_dtype, cache_rs, cache_ss);
+  a.base = base;
+  a.base_rs = base_rs;
+  a.base_ss = base_ss;
+  a.w1 = (const uint16_t*)w1;
+  a.w2 = (const uint16_t*)w2;
+  a.anchor = anchor;
+  a.anchor_pos = (const long long*)anchor_pos;
+  a.temp = temperature;
+  a.seeds = (const long long*)seeds;
+  a.cache = cache;
+  a.cache_rs = cache_rs;
+  a.cache_ss = cache_ss;
+  a.keys = (unsigned long long*)(ws + L.keys);
+  a.qpart = (float2*)(ws + L.qpart);
+  a.status = (uint32_t*)ws;
+  hipError_t e = mds::launch_draft_init(a.keys, K * B, st);
+  if (e != hipSuccess) return hip_fail(e, "draft init launch");
+  for (int k = 0; k < K; ++k) {
+    a.k = k;
+    if (events && (e = hipEventRecord((hipEvent_t)events[2 * k], st)) != hipSuccess)
+      return hip_fail(e, "event record");
+    if ((e = mds::launch_draft_step(a, st)) != hipSuccess) return hip_fail(e, "draft step launch");
+    if (events && (e = hipEventRecord((hipEvent_t)events[2 * k + 1], st)) != hipSuccess)
+      return hip_fail(e, "event record");
+  }
+  mds::DraftFinalArgs f{B, K, L.G, a.keys, a.qpart, temperature, draft_tokens, draft_lse};
+  if ((e = mds::launch_draft_finalize(f, st)) != hipSuccess) return hip_fail(e, "draft finalize launch");
+  return ok();
+}
+
+}  // namespace
+
+namespace mds {
+int draft_slabs(int V) {
+  const int nMT = (V + 15) / 16;
+  int G = (nMT + kDraftMinTilesPerSlab - 1) / kDraftMinTilesPerSlab;
+  if (G > kDraftMaxSlabs) G = kDraftMaxSlabs;
+  if (G > 64) G &= ~7;  // a multiple of the 8 XCDs
+  return G < 1 ? 1 : G;
+}
+}  // namespace mds
+
+extern "C" {
+
+int mds_abi_version(void) { return MDS_ABI_VERSION; }
+
+const char* mds_status_string(int status) {
+  switch (status) {
+    case MDS_OK: return "ok";
+    case MDS_ERR_INVALID_ARG: return "invalid argument";
+    case MDS_ERR_UNSUPPORTED: return "unsupported argument";
+    case MDS_ERR_WORKSPACE: return "workspace too small";
+    case MDS_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* mds_last_error(void) { return g_last_error.c_str(); }
+
+int mds_draft_workspace_bytes(int B, int K, int V, int r, size_t* out_bytes) {
+  int rc;
+  if ((rc = check_sizes(B, K, V)) || (rc = check_rank(r))) return rc;
+  if (!out_bytes) return fail(MDS_ERR_INVALID_ARG, "out_bytes is NULL");
+  *out_bytes = draft_layout(B, K, V).total;
+  return ok();
+}
+
+int mds_verify_workspace_bytes(int B, int K, int V, int has_top_p, int has_draft_lse, size_t* out_bytes) {
+  int rc;
+  if ((rc = check_sizes(B, K, V))) return rc;
+  if (!out_bytes) return fail(MDS_ERR_INVALID_ARG, "out_bytes is NULL");
+  *out_bytes = verify_layout(B, K, V, has_top_p != 0, has_draft_lse != 0).total;
+  return ok();
+}
+
+int mds_markov_draft_loop(int B, int K, int V, int r, const void* base, int base_dtype, int64_t base_req_stride,
+                          int64_t base_step_stride, const void* w1, const void* w2, const int32_t* anchor_tokens,
+                          const int64_t* anchor_pos, const float* temperature, const int64_t* seeds, void* cache,
+                          int cache_dtype, int64_t cache_req_stride, int64_t cache_step_stride,
+                          int32_t* draft_tokens, float* draft_lse, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return draft_impl(B, K, V, r, base, base_dtype, base_req_stride, base_step_stride, w1, w2, anchor_tokens,
+                    anchor_pos, temperature, seeds, cache, cache_dtype, cache_req_stride, cache_step_stride,
+                    draft_tokens, draft_lse, workspace, workspace_bytes, stream, nullptr);
+}
+
+int mds_markov_draft_loop_timed(int B, int K, int V, int r, const void* base, int base_dtype,
+                                int64_t base_req_stride, int64_t base_step_stride, const void* w1, const void* w2,
+                                const int32_t* anchor_tokens, const int64_t* anchor_pos, const float* temperature,
+                                const int64_t* seeds, void* cache, int cache_dtype, int64_t cache_req_stride,
+                                int64_t cache_step_stride, int32_t* draft_tokens, float* draft_lse, void* workspace,
+                                size_t workspace_bytes, void* stream, void* const* events) {
+  if (!events) return fail(MDS_ERR_INVALID_ARG, "events is NULL");
+  return draft_impl(B, K, V, r, base, base_dtype, base_req_stride, base_step_stride, w1, w2, anchor_tokens,
+                    anchor_pos, temperature, seeds, cache, cache_dtype, cache_req_stride, cache_step_stride,
+                    draft_tokens, draft_lse, workspace, workspace_bytes, stream, events);
+}
+
+int mds_rejection_verify(int B, int K, int V, const float* target, int64_t target_row_stride, const void* cache,
+                         int cache_dtype, int64_t cache_req_stride, int64_t cache_step_stride,
+                         const float* draft_lse, const int32_t* draft_tokens, const float* temperature,
+                         const float* top_p, const int64_t* seeds, const int64_t* anchor_pos, int32_t* out_tokens,
+                         int32_t* num_accepted, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc;
+  if ((rc = check_sizes(B, K, V))) return rc;
+  if (!target || !cache || !draft_tokens || !temperature || !seeds || !anchor_pos || !out_tokens || !num_accepted ||
+      !workspace)
+    return fail(MDS_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (cache_dtype != MDS_F32 && cache_dtype != MDS_BF16)
+    return fail(MDS_ERR_INVALID_ARG, "cache dtype must be MDS_F32 or MDS_BF16");
+  if (target_row_stride < V) return fail(MDS_ERR_INVALID_ARG, "target_row_stride must be >= V");
+  if (cache_req_stride < 0 || cache_step_stride < 0) return fail(MDS_ERR_INVALID_ARG, "cache strides must be >= 0");
+  if (!aligned(workspace, kAlign)) return fail(MDS_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const VerifyLayout L = verify_layout(B, K, V, top_p != nullptr, draft_lse != nullptr);
+  if (workspace_bytes < L.total) return fail(MDS_ERR_WORKSPACE, "workspace too small for verification");
+  unsigned char* ws = (unsigned char*)workspace;
+  hipStream_t st = (hipStream_t)stream;
+  mds::VerifyArgs a{};
+  a.B = B;
+  a.K = K;
+  a.V = V;
+  a.NC = L.NC;
+  a.target = target;
+  a.target_rs = target_row_stride;
+  a.vec_target = aligned(target, 16) && target_row_stride % 4 == 0;
+  a.cache = cache;
+  a.cache_bf16 = cache_dtype == MDS_BF16;
+  a.vec_cache = vec_ok(cache, cache_dtype, cache_req_stride, cache_step_stride);
+  a.cache_rs = cache_req_stride;
+  a.cache_ss = cache_step_stride;
+  a.draft_lse = draft_lse;
+  a.draft = draft_tokens;
+  a.temp = temperature;
+  a.top_p = top_p;
+  a.seeds = (const long long*)seeds;
+  a.anchor_pos = (const long long*)anchor_pos;
+  a.out_tokens = out_tokens;
+  a.num_accepted = num_accepted;
+  a.tpart = (mds::StatPart*)(ws + L.tpart);
+  a.qpart = draft_lse ? nullptr : (mds::StatPart*)(ws + L.qpart);
+  a.topp = top_p ? (mds::TopP*)(ws + L.topp) : nullptr;
+  a.req = (mds::ReqState*)(ws + L.req);
+  a.rpart = (mds::ResPart*)(ws + L.rpart);
+  a.status = (uint32_t*)ws;
+  hipError_t e;
+  if ((e = mds::launch_target_stats(a, st)) != hipSuccess) return hip_fail(e, "target stats launch");
+  if (!draft_lse && (e = mds::launch_draft_stats(a, st)) != hipSuccess) return hip_fail(e, "draft stats launch");
+  if (top_p && (e = mds::launch_top_p(a, st)) != hipSuccess) return hip_fail(e, "top-p launch");
+  if ((e = mds::launch_residual(a, st)) != hipSuccess) return hip_fail(e, "residual launch");
+  if ((e = mds::launch_verify_finalize(a, st)) != hipSuccess) return hip_fail(e, "verify finalize launch");
+  return ok();
+}
+
+int mds_debug_noise(int n, const int32_t* cols, int64_t seed, int64_t pos_key, uint32_t salt, uint32_t* words,
+                    float* gumbel, void* stream) {
+  if (n < 0) return fail(MDS_ERR_INVALID_ARG, "n must be >= 0");
+  if (n == 0) return ok();
+  if (!cols || !words || !gumbel) return fail(MDS_ERR_INVALID_ARG, "a required pointer is NULL");
+  hipError_t e = mds::launch_debug_noise(n, cols, seed, pos_key, salt, words, gumbel, (hipStream_t)stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "debug noise launch");
+}
+
+int mds_debug_gumbel(int n, const uint32_t* words, float* gumbel, void* stream) {
+  if (n < 0) return fail(MDS_ERR_INVALID_ARG, "n must be >= 0");
+  if (n == 0) return ok();
+  if (!words || !gumbel) return fail(MDS_ERR_INVALID_ARG, "a required pointer is NULL");
+  hipError_t e = mds::launch_debug_gumbel(n, words, gumbel, (hipStream_t)stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "debug gumbel launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,163 @@
+// Device-side building blocks shared by the sampling kernels (gfx950).
+//
+// Noise: Philox4x32-10 (Salmon et al., "Parallel random numbers: as easy as
+// 1, 2, 3", SC'11) keyed by the request seed, counter (column>>2, position
+// key, salt). The pages fix only the keying by (seed, position-1, column) and
+// the draft salt 1<<30 (DSparkSpeculator API page, _sample_logits; PR #65007,
+// Part 1 and its constants review thread); the counter layout is this
+// library's definition and is stated in include/mds.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mds {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr uint32_t kStatusBadAnchor = 1u;
+constexpr uint32_t kStatusBadDraft = 2u;
+constexpr uint32_t kSaltDraft = 1u << 30;
+constexpr uint32_t kSaltAccept = 1u;
+constexpr uint32_t kSaltResample = 2u;
+
+// ---------------------------------------------------------------- Philox --
+struct Philox4 {
+  uint32_t x0, x1, x2, x3;
+};
+
+// Ten rounds; each multiplies words 0 and 2 by the two round constants, keeps
+// both product halves, and folds the high halves into words 1 and 3 with the
+// round key; the key advances by the two Weyl constants between rounds.
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                                 uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return Philox4{c0, c1, c2, c3};
+}
+
+// Uniform (2m+1) * 2^-24 from the top 23 bits m of a word: build 1 + m*2^-23
+// from the bits, then subtract 1 - 2^-24 (both steps exact).
+__device__ __forceinline__ float uniform24(uint32_t w) {
+  const float f = __uint_as_float(0x3F800000u | (w >> 9));
+  return f - 0x1.fffffep-1f;
+}
+
+// Standard Gumbel -log(-log u) with hardware base-2 logs:
+// -ln(-ln u) = -ln(ln 2) - ln 2 * log2(-log2 u).
+__device__ __forceinline__ float gumbel_from_word(uint32_t w) {
+  const float u = uniform24(w);
+  const float e2 = -__builtin_amdgcn_logf(u);  // -log2(u) > 0, u in (0, 1) normal
+  return __builtin_fmaf(-0x1.62e430p-1f, __builtin_amdgcn_logf(e2), 0x1.774f2ap-2f);
+}
+
+// ---------------------------------------------------------- winner keys --
+// Total order of the winner rule: NaN above every value, -0 == +0, and on
+// equal values the lower column wins. key = ord(value) << 32 | ~column, so
+// the largest key is the winner and 0 means "no candidate".
+__device__ __forceinline__ uint32_t ord_f32(float x) {
+  if (x != x) return 0xFFFFFFFFu;
+  const uint32_t b = __float_as_uint(x + 0.0f);  // -0 -> +0
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ uint64_t win_key(float x, uint32_t col) {
+  return ((uint64_t)ord_f32(x) << 32) | (uint32_t)(~col);
+}
+__device__ __forceinline__ uint32_t win_col(uint64_t key) { return ~(uint32_t)key; }
+
+// In-order update of a running winner (columns arrive in increasing order).
+__device__ __forceinline__ void win_update(float& bv, int& bi, float s, int col) {
+  const bool take = (s > bv) || ((s != s) && (bv == bv)) || (bi < 0);
+  bv = take ? s : bv;
+  bi = take ? col : bi;
+}
+
+// ------------------------------------------------------------------ bf16 --
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// round to nearest, ties to even; NaN stays a quiet NaN
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  const uint32_t b = __float_as_uint(f);
+  if (f != f) return (b >> 16) | 0x40u;
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+// ------------------------------------------------------------ arithmetic --
+// z / T from a precomputed reciprocal plus one residual correction.
+__device__ __forceinline__ float div_t(float z, float T, float invT) {
+  const float q = z * invT;
+  const float r = __builtin_fmaf(-q, T, z);
+  return __builtin_fmaf(r, invT, q);
+}
+
+__device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 0x1.715476p+0f); }
+
+// (max, sum of exp(x - max)) pairs; an empty side has max = -inf, sum = 0.
+// A NaN sum marks a row that held NaN and survives every merge.
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  const float M = fmaxf(m, m2);
+  if (M == -INFINITY) {
+    s = s + s2;
+  } else {
+    s = s * __expf(m - M) + s2 * __expf(m2 - M);
+  }
+  m = M;
+}
+
+__device__ __forceinline__ void set_status(uint32_t* status, uint32_t bit) {
+  if (status) atomicOr(status, bit);
+}
+
+// 64-bit max across the lanes l, l^16, l^32, l^48 of a wave
+__device__ __forceinline__ uint64_t max_over_groups16(uint64_t k) {
+  uint64_t o = (uint64_t)__shfl_xor((unsigned long long)k, 16);
+  k = o > k ? o : k;
+  o = (uint64_t)__shfl_xor((unsigned long long)k, 32);
+  return o > k ? o : k;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint64_t o = (uint64_t)__shfl_xor((unsigned long long)k, off);
+    k = o > k ? o : k;
+  }
+  return k;
+}
+
+__device__ __forceinline__ void wave_lse_merge(float& m, float& s) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(s, off);
+    lse_merge(m, s, m2, s2);
+  }
+}
+
+__device__ __forceinline__ float wave_max_f32(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum_f32(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+}  // namespace mds

@@ -1,0 +1,113 @@
+// Host/device interface between the C-ABI layer (abi.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mds {
+
+// ------------------------------------------------------------ draft loop --
+constexpr int kDraftMaxSlabs = 1024;    // column slabs (work-groups) per batch tile and step
+constexpr int kDraftMinTilesPerSlab = 8;  // 16-column tiles per slab, at least
+
+struct DraftStepArgs {
+  int B, K, V, r, k, G, nMT, BT;
+  int base_bf16, cache_bf16, vec_base, vec_cache;
+  const void* base;
+  long long base_rs, base_ss;
+  const uint16_t* w1;
+  const uint16_t* w2;
+  const int32_t* anchor;
+  const long long* anchor_pos;
+  const float* temp;
+  const long long* seeds;
+  void* cache;
+  long long cache_rs, cache_ss;
+  unsigned long long* keys;  // [K][B] winner keys
+  float2* qpart;             // [K][B][G] (max, sum exp) of cache / T per slab
+  uint32_t* status;
+};
+
+struct DraftFinalArgs {
+  int B, K, G;
+  const unsigned long long* keys;
+  const float2* qpart;
+  const float* temp;
+  int32_t* tokens;
+  float* lse;
+};
+
+int draft_nb(int B, int r);
+int draft_slabs(int V);
+hipError_t launch_draft_init(unsigned long long* keys, int n, hipStream_t st);
+hipError_t launch_draft_step(const DraftStepArgs& a, hipStream_t st);
+hipError_t launch_draft_finalize(const DraftFinalArgs& a, hipStream_t st);
+
+// ---------------------------------------------------------- verification --
+constexpr int kStatsChunk = 8192;  // columns per statistics block (the pages' 8192-column blocks)
+
+struct StatPart {  // one (row, chunk) partial of a target or draft row
+  float m;         // max of x = logit / T (T > 0)
+  float s;         // sum of exp(x - m); NaN if the chunk held NaN
+  unsigned long long key;  // winner key of the raw logits (greedy rows)
+};
+
+struct TopP {  // kept set of one target row: ord(t) > tau, or == tau and id <= cut
+  uint32_t tau;
+  int cut;
+  float log_z;  // log of the kept mass sum exp(x - m)
+  int on;
+};
+
+struct ReqState {
+  int n_acc;     // accepted drafts
+  int jstar;     // row of the final draw (n_acc)
+  int mode;      // 0 bonus from p_K, 1 residual of row jstar, 2 greedy (token below), 3 residual empty -> p
+  int token;     // greedy final token
+};
+
+struct ResPart {
+  unsigned long long key_r;  // Gumbel-max winner over log residual
+  unsigned long long key_p;  // Gumbel-max winner over log p (bonus / empty residual)
+  float sum_r;               // residual mass of the chunk
+  float pad;
+};
+
+struct VerifyArgs {
+  int B, K, V, NC;
+  const float* target;
+  long long target_rs;
+  const void* cache;
+  int cache_bf16, vec_cache;
+  long long cache_rs, cache_ss;
+  const float* draft_lse;  // [B*K] or the workspace copy recomputed from the cache
+  const int32_t* draft;
+  const float* temp;
+  const float* top_p;
+  const long long* seeds;
+  const long long* anchor_pos;
+  int32_t* out_tokens;
+  int32_t* num_accepted;
+  StatPart* tpart;  // [B*(K+1)][NC]
+  StatPart* qpart;  // [B*K][NC] when draft_lse must be recomputed
+  float* qlse;      // [B*K] recomputed draft lse
+  TopP* topp;       // [B*(K+1)] or null
+  ReqState* req;    // [B]
+  ResPart* rpart;   // [B][NC]
+  uint32_t* status;
+  int vec_target;
+};
+
+hipError_t launch_target_stats(const VerifyArgs& a, hipStream_t st);
+hipError_t launch_draft_stats(const VerifyArgs& a, hipStream_t st);
+hipError_t launch_top_p(const VerifyArgs& a, hipStream_t st);
+hipError_t launch_residual(const VerifyArgs& a, hipStream_t st);
+hipError_t launch_verify_finalize(const VerifyArgs& a, hipStream_t st);
+
+// ----------------------------------------------------------------- debug --
+hipError_t launch_debug_noise(int n, const int32_t* cols, long long seed, long long pos, uint32_t salt,
+                              uint32_t* words, float* g, hipStream_t st);
+hipError_t launch_debug_gumbel(int n, const uint32_t* words, float* g, hipStream_t st);
+
+}  // namespace mds

@@ -1,0 +1,99 @@
+"""The C-ABI library loads and exports every entry point include/mds.h
+declares, and its host-side validation rejects bad arguments without any
+device work (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mds.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mds_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from markov_draft_sampling_amd import build, library_path
+    if not os.path.exists(library_path()):
+        build.build()
+    return ctypes.CDLL(library_path())
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("mds_markov_draft_loop", "mds_rejection_verify", "mds_draft_workspace_bytes",
+              "mds_verify_workspace_bytes", "mds_abi_version", "mds_status_string", "mds_last_error"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_abi_version(lib):
+    import markov_draft_sampling_amd as mds
+    assert mds.abi_version() == 1
+
+
+def test_workspace_queries_validate_sizes():
+    import markov_draft_sampling_amd as mds
+    assert mds.draft_workspace_bytes(32, 7, 200064, 256) > 0
+    assert mds.verify_workspace_bytes(32, 7, 200064, True, False) > mds.verify_workspace_bytes(32, 7, 200064, False,
+                                                                                               True)
+    with pytest.raises(mds.MdsError, match="invalid argument"):
+        mds.draft_workspace_bytes(0, 7, 1000, 64)
+    with pytest.raises(mds.MdsError, match="invalid argument"):
+        mds.draft_workspace_bytes(1, 33, 1000, 64)
+    with pytest.raises(mds.MdsError, match="invalid argument"):
+        mds.draft_workspace_bytes(1, 3, 1, 64)
+    with pytest.raises(mds.MdsError, match="unsupported"):
+        mds.draft_workspace_bytes(1, 3, 1000, 72)
+    with pytest.raises(mds.MdsError, match="invalid argument"):
+        mds.draft_workspace_bytes(1, 3, 1000, 1024)
+
+
+def test_draft_loop_rejects_bad_arguments_on_the_host(lib):
+    # all pointers NULL: rejected before anything reaches the device
+    f = lib.mds_markov_draft_loop
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    f.argtypes = [ctypes.c_int] * 4 + [vp, ctypes.c_int, i64, i64, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i64, i64,
+                                       vp, vp, vp, ctypes.c_size_t, vp]
+    f.restype = ctypes.c_int
+    args = [4, 3, 1000, 64] + [None, 0, 3000, 1000] + [None] * 7 + [0, 3000, 1000, None, None, None, 0, None]
+    assert f(*args) == -1
+    args[:4] = [4, 3, 1000, 48]
+    assert f(*args) == -2  # rank not a multiple of 32
+    lib.mds_last_error.restype = ctypes.c_char_p
+    assert lib.mds_last_error()
+
+
+def test_verify_rejects_bad_arguments_on_the_host(lib):
+    f = lib.mds_rejection_verify
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    f.argtypes = [ctypes.c_int] * 3 + [vp, i64, vp, ctypes.c_int, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                       ctypes.c_size_t, vp]
+    f.restype = ctypes.c_int
+    fake = 1 << 20  # never dereferenced: validation fails first
+    args = [2, 3, 1000, fake, 999, fake, 0, 3000, 1000, None, fake, fake, None, fake, fake, fake, fake, fake, 1 << 30,
+            None]
+    assert f(*args) == -1  # target row stride < V
+    args[4] = 1000
+    args[18] = 16  # workspace far too small
+    assert f(*args) == -3
+    args[6] = 5  # bad dtype
+    assert f(*args) == -1
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import markov_draft_sampling_amd as mds
+    monkeypatch.setattr(mds, "_LIB", None)
+    monkeypatch.setattr(mds, "library_path", lambda: str(tmp_path / "missing.so"))
+    with pytest.raises(mds.MdsError, match="missing"):
+        mds.abi_version()
