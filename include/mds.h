@@ -57,6 +57,8 @@ extern "C" {
 /* sticky status bits (workspace word 0) */
 #define MDS_STATUS_BAD_ANCHOR 1u      /* an anchor token was outside [0, V); token 0 was used */
 #define MDS_STATUS_BAD_DRAFT 2u       /* a draft token given to verification was outside [0, V); token 0 was used */
+#define MDS_STATUS_BARRIER_TIMEOUT 4u /* the resident draft kernel gave up waiting at a step barrier; the
+                                         draft outputs of that call are invalid */
 
 /* sampling salts: the draft salt is the pages' draft-noise salt (1 << 30) */
 #define MDS_SALT_DRAFT (1u << 30)
@@ -116,6 +118,16 @@ int mds_verify_workspace_bytes(int B, int K, int V, int has_top_p, int has_draft
  *                         unspecified for greedy requests)
  *   workspace             >= mds_draft_workspace_bytes(B, K, V, r) bytes, 256-byte aligned
  *   stream                hipStream_t as void*
+ *
+ * Kernels: when w2 fits in the chip's registers and LDS (V*r*2 bytes within
+ * about 392 KiB per CU, r in {64, 128, 192, 256}) one persistent launch runs
+ * all K steps with w2 read from memory once; it needs every CU of the device
+ * free for the duration of the call (one work-group per CU, grid barriers
+ * between steps with a bounded wait, see MDS_STATUS_BARRIER_TIMEOUT).
+ * Otherwise one launch per step streams w2 each time. The environment
+ * variable MDS_DRAFT_PATH selects: "stream" (the default) the streaming
+ * kernel, "auto" the resident kernel when w2 fits, "resident" requires it
+ * (MDS_ERR_UNSUPPORTED if it does not fit).
  */
 int mds_markov_draft_loop(int B, int K, int V, int r,
                           const void* base, int base_dtype, int64_t base_req_stride, int64_t base_step_stride,
@@ -171,9 +183,12 @@ int mds_rejection_verify(int B, int K, int V,
 
 /*
  * mds_markov_draft_loop_timed - mds_markov_draft_loop that also records
- * events[2*k] before and events[2*k+1] after the step-k kernel (k = 0..K-1)
- * on `stream`, so a caller can measure the fused step kernel alone.
- * events: host array of 2*K hipEvent_t (as void*), created by the caller.
+ * ev_begin just before the first and ev_end just after the last launch of the
+ * Markov step kernel on `stream` (the init and finalize kernels stay outside),
+ * and writes to *n_step_launches how many launches that span held: 1 when
+ * the resident kernel ran all K steps, K for the streaming kernel.
+ * ev_begin, ev_end: hipEvent_t (as void*) created by the caller;
+ * n_step_launches: host pointer, nullable.
  */
 int mds_markov_draft_loop_timed(int B, int K, int V, int r,
                                 const void* base, int base_dtype, int64_t base_req_stride, int64_t base_step_stride,
@@ -182,7 +197,8 @@ int mds_markov_draft_loop_timed(int B, int K, int V, int r,
                                 const float* temperature, const int64_t* seeds,
                                 void* cache, int cache_dtype, int64_t cache_req_stride, int64_t cache_step_stride,
                                 int32_t* draft_tokens, float* draft_lse,
-                                void* workspace, size_t workspace_bytes, void* stream, void* const* events);
+                                void* workspace, size_t workspace_bytes, void* stream,
+                                void* ev_begin, void* ev_end, int* n_step_launches);
 
 /*
  * mds_debug_noise - test hook: writes for n columns cols[i] the Philox word

@@ -18,12 +18,12 @@ import os
 __all__ = [
     "F32", "BF16", "MdsError", "library_path", "abi_version", "draft_workspace_bytes", "verify_workspace_bytes",
     "new_workspace", "workspace_status", "markov_draft_loop", "markov_draft_loop_timed", "rejection_verify",
-    "debug_noise", "debug_gumbel", "STATUS_BAD_ANCHOR", "STATUS_BAD_DRAFT", "SALT_DRAFT", "SALT_ACCEPT",
+    "debug_noise", "debug_gumbel", "STATUS_BAD_ANCHOR", "STATUS_BAD_DRAFT", "STATUS_BARRIER_TIMEOUT", "SALT_DRAFT", "SALT_ACCEPT",
     "SALT_RESAMPLE",
 ]
 
 F32, BF16 = 0, 1
-STATUS_BAD_ANCHOR, STATUS_BAD_DRAFT = 1, 2
+STATUS_BAD_ANCHOR, STATUS_BAD_DRAFT, STATUS_BARRIER_TIMEOUT = 1, 2, 4
 SALT_DRAFT, SALT_ACCEPT, SALT_RESAMPLE = 1 << 30, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -49,7 +49,8 @@ _SIGS = {
     "mds_markov_draft_loop": ([_c_int] * 4 + [_vp, _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int,
                                               _c_i64, _c_i64, _vp, _vp, _vp, _c_sz, _vp], _c_int),
     "mds_markov_draft_loop_timed": ([_c_int] * 4 + [_vp, _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                                    _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _c_sz, _vp, _vp], _c_int),
+                                                    _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _c_sz, _vp, _vp, _vp,
+                                                    ctypes.POINTER(_c_int)], _c_int),
     "mds_rejection_verify": ([_c_int] * 3 + [_vp, _c_i64, _vp, _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp,
                                              _vp, _vp, _vp, _c_sz, _vp], _c_int),
     "mds_debug_noise": ([_c_int, _vp, _c_i64, _c_i64, ctypes.c_uint32, _vp, _vp, _vp], _c_int),
@@ -180,19 +181,21 @@ def markov_draft_loop(base, w1, w2, anchor_tokens, anchor_pos, temperature, seed
 
 
 def markov_draft_loop_timed(base, w1, w2, anchor_tokens, anchor_pos, temperature, seeds, cache, draft_tokens,
-                            draft_lse, workspace, events, stream=None):
-    """markov_draft_loop recording events[2k] / events[2k+1] around step kernel k.
-
-    events: list of 2*K torch.cuda.Event(enable_timing=True), recorded on the
-    stream the kernels run on.
-    """
-    B, K = draft_tokens.shape
-    _need(len(events) == 2 * K, "need 2*K events")
+                            draft_lse, workspace, ev_begin, ev_end, stream=None) -> int:
+    """markov_draft_loop recording ev_begin / ev_end (torch.cuda.Event with
+    timing) around the Markov step kernel launch(es); returns how many
+    launches that span held (1 resident kernel, or K streaming launches)."""
+    import torch
     args = _draft_args(base, w1, w2, anchor_tokens, anchor_pos, temperature, seeds, cache, draft_tokens, draft_lse,
                        workspace)
-    arr = (_vp * (2 * K))(*[_vp(e.cuda_event) for e in events])
-    _check(_lib().mds_markov_draft_loop_timed(*args, _stream(stream, base.device), arr), "markov_draft_loop_timed")
-    return workspace
+    st = stream if stream is not None else torch.cuda.current_stream(base.device)
+    for e in (ev_begin, ev_end):  # torch creates the underlying HIP event on its first record
+        if not e.cuda_event:
+            e.record(st)
+    n = _c_int(0)
+    _check(_lib().mds_markov_draft_loop_timed(*args, _stream(stream, base.device), _vp(ev_begin.cuda_event),
+                                              _vp(ev_end.cuda_event), ctypes.byref(n)), "markov_draft_loop_timed")
+    return n.value
 
 
 def rejection_verify(target, cache, draft_tokens, temperature, seeds, anchor_pos, out_tokens, num_accepted,

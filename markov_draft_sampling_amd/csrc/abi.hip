@@ -1,6 +1,8 @@
 // extern "C" entry points of libmds.so: argument validation on the host,
 // workspace layout, and the kernel sequence on the caller's stream. See
 // include/mds.h for the contract of each call.
+#include <cstdlib>
+#include <cstring>
 #include <string>
 
 #include "../../include/mds.h"
@@ -51,19 +53,33 @@ bool vec_ok(const void* p, int dtype, long long rs, long long ss) {
   return aligned(p, dtype == MDS_BF16 ? 8 : 16) && rs % 4 == 0 && ss % 4 == 0;
 }
 
+// Draft workspace: [status | keys K*B u64 | barrier words K+1 u32 | per-slab
+// (max, sum exp) partials K*B*kDraftMaxSlabs]. Sized without the device so the
+// query needs no GPU.
 struct DraftLayout {
-  int G, nMT;
-  size_t keys, qpart, total;
+  int nMT;
+  size_t keys, bar, qpart, total;
 };
 
 DraftLayout draft_layout(int B, int K, int V) {
   DraftLayout L;
   L.nMT = (V + 15) / 16;
-  L.G = mds::draft_slabs(V);
   L.keys = kAlign;
-  L.qpart = L.keys + up((size_t)K * B * 8);
-  L.total = L.qpart + up((size_t)K * B * L.G * sizeof(float2));
+  L.bar = L.keys + up((size_t)K * B * 8);
+  L.qpart = L.bar + up((size_t)(K + 1) * 4);
+  L.total = L.qpart + up((size_t)K * B * mds::kDraftMaxSlabs * sizeof(float2));
   return L;
+}
+
+// Which draft kernel runs: MDS_DRAFT_PATH = "stream" (default) streams w2 at
+// every step; "resident" requires the persistent kernel that keeps w2 on chip;
+// "auto" uses the resident kernel when w2 fits.
+int draft_path_choice() {
+  const char* e = getenv("MDS_DRAFT_PATH");
+  if (!e || !*e || !strcmp(e, "stream")) return 1;
+  if (!strcmp(e, "auto")) return 0;
+  if (!strcmp(e, "resident")) return 2;
+  return -1;
 }
 
 struct VerifyLayout {
@@ -98,7 +114,7 @@ int draft_impl(int B, int K, int V, int r, const void* base, int base_dtype, int
                const void* w1, const void* w2, const int32_t* anchor, const int64_t* anchor_pos,
                const float* temperature, const int64_t* seeds, void* cache, int cache_dtype, int64_t cache_rs,
                int64_t cache_ss, int32_t* draft_tokens, float* draft_lse, void* workspace, size_t ws_bytes,
-               void* stream, void* const* events) {
+               void* stream, void* ev_begin, void* ev_end, int* n_launches) {
   int rc;
   if ((rc = check_sizes(B, K, V)) || (rc = check_rank(r))) return rc;
   if (!base || !w1 || !w2 || !anchor || !anchor_pos || !temperature || !seeds || !cache || !draft_tokens ||
@@ -120,7 +136,6 @@ int draft_impl(int B, int K, int V, int r, const void* base, int base_dtype, int
   a.K = K;
   a.V = V;
   a.r = r;
-  a.G = L.G;
   a.nMT = L.nMT;
   a.base_bf16 = base_dtype == MDS_BF16;
   a.cache_bf16 = cache_dtype == MDS_BF16;
@@ -141,17 +156,35 @@ int draft_impl(int B, int K, int V, int r, const void* base, int base_dtype, int
   a.keys = (unsigned long long*)(ws + L.keys);
   a.qpart = (float2*)(ws + L.qpart);
   a.status = (uint32_t*)ws;
-  hipError_t e = mds::launch_draft_init(a.keys, K * B, st);
-  if (e != hipSuccess) return hip_fail(e, "draft init launch");
-  for (int k = 0; k < K; ++k) {
-    a.k = k;
-    if (events && (e = hipEventRecord((hipEvent_t)events[2 * k], st)) != hipSuccess)
-      return hip_fail(e, "event record");
-    if ((e = mds::launch_draft_step(a, st)) != hipSuccess) return hip_fail(e, "draft step launch");
-    if (events && (e = hipEventRecord((hipEvent_t)events[2 * k + 1], st)) != hipSuccess)
-      return hip_fail(e, "event record");
+  a.bar = (unsigned*)(ws + L.bar);
+  a.abort_flag = a.bar + K;
+  const int choice = draft_path_choice();
+  if (choice < 0) return fail(MDS_ERR_INVALID_ARG, "MDS_DRAFT_PATH must be auto, stream or resident");
+  int dev = 0, cus = 0, lds_max = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+  if (e != hipSuccess) return hip_fail(e, "device query");
+  int n_lds = 0;
+  size_t res_lds = 0;
+  const bool resident = choice != 1 && cus <= mds::kDraftMaxSlabs &&
+                        mds::draft_resident_plan(V, r, cus, (size_t)lds_max, &n_lds, &res_lds) == hipSuccess;
+  if (choice == 2 && !resident) return fail(MDS_ERR_UNSUPPORTED, "w2 does not fit on chip for the resident kernel");
+  a.G = resident ? cus : mds::draft_slabs(V, cus);
+  a.n_lds_tiles = n_lds;
+  if ((e = mds::launch_draft_init(a.keys, K * B, a.bar, K + 1, st)) != hipSuccess) return hip_fail(e, "draft init launch");
+  if (ev_begin && (e = hipEventRecord((hipEvent_t)ev_begin, st)) != hipSuccess) return hip_fail(e, "event record");
+  if (resident) {
+    if ((e = mds::launch_draft_resident(a, res_lds, st)) != hipSuccess) return hip_fail(e, "resident draft launch");
+  } else {
+    for (int k = 0; k < K; ++k) {
+      a.k = k;
+      if ((e = mds::launch_draft_step(a, st)) != hipSuccess) return hip_fail(e, "draft step launch");
+    }
   }
-  mds::DraftFinalArgs f{B, K, L.G, a.keys, a.qpart, temperature, draft_tokens, draft_lse};
+  if (ev_end && (e = hipEventRecord((hipEvent_t)ev_end, st)) != hipSuccess) return hip_fail(e, "event record");
+  if (n_launches) *n_launches = resident ? 1 : K;
+  mds::DraftFinalArgs f{B, K, a.G, a.keys, a.qpart, temperature, draft_tokens, draft_lse};
   if ((e = mds::launch_draft_finalize(f, st)) != hipSuccess) return hip_fail(e, "draft finalize launch");
   return ok();
 }
@@ -159,11 +192,15 @@ int draft_impl(int B, int K, int V, int r, const void* base, int base_dtype, int
 }  // namespace
 
 namespace mds {
-int draft_slabs(int V) {
+// Streaming kernel: two work-groups per CU (what its LDS and registers allow),
+// fewer for small vocabularies, a multiple of the 8 XCDs when large.
+int draft_slabs(int V, int cus) {
   const int nMT = (V + 15) / 16;
   int G = (nMT + kDraftMinTilesPerSlab - 1) / kDraftMinTilesPerSlab;
+  const int cap = cus > 0 ? 2 * cus : kDraftMaxSlabs;
+  if (G > cap) G = cap;
   if (G > kDraftMaxSlabs) G = kDraftMaxSlabs;
-  if (G > 64) G &= ~7;  // a multiple of the 8 XCDs
+  if (G > 64) G &= ~7;
   return G < 1 ? 1 : G;
 }
 }  // namespace mds
@@ -209,7 +246,7 @@ int mds_markov_draft_loop(int B, int K, int V, int r, const void* base, int base
                           void* stream) {
   return draft_impl(B, K, V, r, base, base_dtype, base_req_stride, base_step_stride, w1, w2, anchor_tokens,
                     anchor_pos, temperature, seeds, cache, cache_dtype, cache_req_stride, cache_step_stride,
-                    draft_tokens, draft_lse, workspace, workspace_bytes, stream, nullptr);
+                    draft_tokens, draft_lse, workspace, workspace_bytes, stream, nullptr, nullptr, nullptr);
 }
 
 int mds_markov_draft_loop_timed(int B, int K, int V, int r, const void* base, int base_dtype,
@@ -217,11 +254,12 @@ int mds_markov_draft_loop_timed(int B, int K, int V, int r, const void* base, in
                                 const int32_t* anchor_tokens, const int64_t* anchor_pos, const float* temperature,
                                 const int64_t* seeds, void* cache, int cache_dtype, int64_t cache_req_stride,
                                 int64_t cache_step_stride, int32_t* draft_tokens, float* draft_lse, void* workspace,
-                                size_t workspace_bytes, void* stream, void* const* events) {
-  if (!events) return fail(MDS_ERR_INVALID_ARG, "events is NULL");
+                                size_t workspace_bytes, void* stream, void* ev_begin, void* ev_end,
+                                int* n_step_launches) {
+  if (!ev_begin || !ev_end) return fail(MDS_ERR_INVALID_ARG, "events must not be NULL");
   return draft_impl(B, K, V, r, base, base_dtype, base_req_stride, base_step_stride, w1, w2, anchor_tokens,
                     anchor_pos, temperature, seeds, cache, cache_dtype, cache_req_stride, cache_step_stride,
-                    draft_tokens, draft_lse, workspace, workspace_bytes, stream, events);
+                    draft_tokens, draft_lse, workspace, workspace_bytes, stream, ev_begin, ev_end, n_step_launches);
 }
 
 int mds_rejection_verify(int B, int K, int V, const float* target, int64_t target_row_stride, const void* cache,

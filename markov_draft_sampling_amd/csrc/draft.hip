@@ -25,40 +25,15 @@
 
 namespace mds {
 
+size_t draft_step_lds(int NB, int r) {
+  return (size_t)64 * r * 2 + (size_t)NB * (r + 8) * 2 + (size_t)NB * (64 + 4) * 4 + NB * 4 + 4 * NB * 8 + 8 * NB * 4;
+}
+
 namespace {
 
 // LDS row stride of the embedding tile in bf16 elements: r plus 8 (16 bytes)
 // so that the 16 rows a ds_read_b128 touches start on different banks.
 __device__ __forceinline__ int emb_stride(int r) { return r + 8; }
-
-template <bool BF16>
-__device__ __forceinline__ void load4(const void* p, long long off, int n, bool vec, float (&v)[4]) {
-  if (BF16) {
-    const uint16_t* q = (const uint16_t*)p + off;
-    if (vec && n == 4) {
-      const u32x2 w = __builtin_nontemporal_load((const u32x2*)q);
-      v[0] = bf16_bits_to_f32(w.x & 0xFFFFu);
-      v[1] = bf16_bits_to_f32(w.x >> 16);
-      v[2] = bf16_bits_to_f32(w.y & 0xFFFFu);
-      v[3] = bf16_bits_to_f32(w.y >> 16);
-    } else {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) v[t] = t < n ? bf16_bits_to_f32(q[t]) : 0.0f;
-    }
-  } else {
-    const float* q = (const float*)p + off;
-    if (vec && n == 4) {
-      const f32x4 w = __builtin_nontemporal_load((const f32x4*)q);
-      v[0] = w.x;
-      v[1] = w.y;
-      v[2] = w.z;
-      v[3] = w.w;
-    } else {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) v[t] = t < n ? q[t] : 0.0f;
-    }
-  }
-}
 
 template <bool BF16>
 __device__ __forceinline__ void store4(void* p, long long off, int n, bool vec, const float (&z)[4], float (&stored)[4]) {
@@ -74,7 +49,7 @@ __device__ __forceinline__ void store4(void* p, long long off, int n, bool vec, 
       u32x2 w;
       w.x = h[0] | (h[1] << 16);
       w.y = h[2] | (h[3] << 16);
-      __builtin_nontemporal_store(w, (u32x2*)q);
+      *(u32x2*)q = w;
     } else {
 #pragma unroll
       for (int t = 0; t < 4; ++t)
@@ -86,7 +61,7 @@ __device__ __forceinline__ void store4(void* p, long long off, int n, bool vec, 
     float* q = (float*)p + off;
     if (vec && n == 4) {
       const f32x4 w = {z[0], z[1], z[2], z[3]};
-      __builtin_nontemporal_store(w, (f32x4*)q);
+      *(f32x4*)q = w;
     } else {
 #pragma unroll
       for (int t = 0; t < 4; ++t)
@@ -95,24 +70,68 @@ __device__ __forceinline__ void store4(void* p, long long off, int n, bool vec, 
   }
 }
 
-// RKT: r / 32 when known at compile time, 0 for a runtime rank (<= 512).
+// Geometry of one step kernel work-group: NB requests x CW = 64 columns per
+// chunk; each of the 4 waves owns one 16-column MFMA tile of the chunk.
+constexpr int kCW = 64;
+
+template <bool BF16>
+__device__ __forceinline__ void load_row4(const void* p, long long off, int n, bool vec, float (&v)[4]) {
+  if (BF16) {
+    const uint16_t* q = (const uint16_t*)p + off;
+    if (vec && n == 4) {
+      const u32x2 w = *(const u32x2*)q;
+      v[0] = bf16_bits_to_f32(w.x & 0xFFFFu);
+      v[1] = bf16_bits_to_f32(w.x >> 16);
+      v[2] = bf16_bits_to_f32(w.y & 0xFFFFu);
+      v[3] = bf16_bits_to_f32(w.y >> 16);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) v[t] = t < n ? bf16_bits_to_f32(q[t]) : 0.0f;
+    }
+  } else {
+    const float* q = (const float*)p + off;
+    if (vec && n == 4) {
+      const f32x4 w = *(const f32x4*)q;
+      v[0] = w.x;
+      v[1] = w.y;
+      v[2] = w.z;
+      v[3] = w.w;
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) v[t] = t < n ? q[t] : 0.0f;
+    }
+  }
+}
+
+// The chunk's w2 rows [c0, c0 + 64) x r are loaded with coalesced 16-byte
+// loads and stored in LDS row-major with the 16-byte column chunks of row rho
+// XOR-permuted by (rho & 7): the MFMA operand reads (16 rows, same chunk)
+// then hit 8 distinct bank groups.
 template <int NB, int RKT>
 __global__ __launch_bounds__(256) void draft_step_kernel(DraftStepArgs a) {
-  constexpr int NT = NB / 16;
+  constexpr int NT = NB / 16;     // 16-request MFMA tiles
+  constexpr int EPT = NB * kCW / 4 / 256;  // float4 groups of the epilogue per thread
   constexpr int RKMAX = RKT > 0 ? RKT : 16;
+  constexpr int WLMAX = RKMAX;    // 16-byte w2 loads per thread per chunk = 64 * r / 8 / 256 = r / 32
   const int RK = RKT > 0 ? RKT : (a.r >> 5);
+  const int r = a.r, V = a.V, k = a.k;
+  const int cpr = r >> 3;                 // 16-byte chunks per w2 row
+  const int xmask = (cpr & 7) ? 3 : 7;  // keeps the permuted chunk inside its row
   extern __shared__ __align__(16) unsigned char smem[];
-  const int rs = emb_stride(a.r);
-  uint16_t* s_e = (uint16_t*)smem;                             // [NB][rs]
-  int* s_prev = (int*)(smem + (size_t)NB * rs * 2);           // [NB]
-  unsigned long long* s_key = (unsigned long long*)(s_prev + NB);  // [4][NB]
-  float* s_qm = (float*)(s_key + 4 * NB);                      // [4][NB]
-  float* s_qs = s_qm + 4 * NB;                                 // [4][NB]
+  const int rs = emb_stride(r);
+  uint16_t* s_w = (uint16_t*)smem;                                   // [64][r] swizzled w2 stage
+  uint16_t* s_e = s_w + kCW * r;                                     // [NB][rs] embeddings
+  float* s_bias = (float*)(s_e + NB * rs);                           // [NB][kCW + 4]
+  int* s_prev = (int*)(s_bias + NB * (kCW + 4));                     // [NB]
+  unsigned long long* s_key = (unsigned long long*)(s_prev + NB);    // [4][NB]
+  float* s_qm = (float*)(s_key + 4 * NB);                            // [4][NB]
+  float* s_qs = s_qm + 4 * NB;                                       // [4][NB]
+  constexpr int BST = kCW + 4;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // Work-groups are dealt round-robin to the 8 XCDs by linear id. When the
-  // slab count is a multiple of 8, the batch tiles of one column slab are
-  // given ids on the same XCD so its w2 rows are re-read from that XCD's L2.
+  // slab count is a multiple of 8, the batch tiles of one column slab get ids
+  // on the same XCD so its w2 rows are re-read from that XCD's L2.
   int g, bt;
   {
     const int id = blockIdx.x;
@@ -126,7 +145,6 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftStepArgs a) {
     }
   }
   const int b0 = bt * NB;
-  const int k = a.k;
 
   // previous token of every request of the tile
   for (int i = tid; i < NB; i += 256) {
@@ -134,7 +152,7 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftStepArgs a) {
     int prev = 0;
     if (b < a.B) {
       long long t = (k == 0) ? (long long)a.anchor[b] : (long long)win_col(a.keys[(size_t)(k - 1) * a.B + b]);
-      if (t < 0 || t >= a.V) {
+      if (t < 0 || t >= V) {
         set_status(a.status, kStatusBadAnchor);
         t = 0;
       }
@@ -144,179 +162,224 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftStepArgs a) {
   }
   __syncthreads();
   // Markov embeddings w1[prev] -> LDS (zero rows past the batch)
-  {
-    const int cpr = a.r >> 3;  // 16-byte chunks per row
-    for (int i = tid; i < NB * cpr; i += 256) {
-      const int row = i / cpr, ch = i - row * cpr;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (b0 + row < a.B) v = *(const uint4*)(a.w1 + (size_t)s_prev[row] * a.r + ch * 8);
-      *(uint4*)(s_e + row * rs + ch * 8) = v;
+  for (int i = tid; i < NB * cpr; i += 256) {
+    const int row = i / cpr, ch = i - row * cpr;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (b0 + row < a.B) v = *(const u32x4*)(a.w1 + (size_t)s_prev[row] * r + ch * 8);
+    *(u32x4*)(s_e + row * rs + ch * 8) = v;
+  }
+
+  // this work-group's columns: 16-column tiles [mt_begin, mt_end)
+  const int mt_begin = (int)(((long long)g * a.nMT) / a.G);
+  const int mt_end = (int)(((long long)(g + 1) * a.nMT) / a.G);
+  const int c_begin = mt_begin * 16, c_end = min(mt_end * 16, V);
+  const int nchunks = (mt_end - mt_begin + 3) >> 2;
+
+  // epilogue ownership: float4 group j = tid + 256*e -> request row j / 16, columns 4*(j % 16)
+  int erow[EPT], ecol[EPT];
+  bool ev[EPT];
+  float Tv[EPT], invT[EPT];
+  uint32_t sk0[EPT], sk1[EPT], pk0[EPT], pk1[EPT];
+  long long rbase[EPT], rcache[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int j = tid + 256 * e;
+    erow[e] = j / (kCW / 4);
+    ecol[e] = (j % (kCW / 4)) * 4;
+    const int b = b0 + erow[e];
+    ev[e] = b < a.B;
+    const int bb = ev[e] ? b : 0;
+    Tv[e] = a.temp[bb];
+    invT[e] = Tv[e] > 0.0f ? 1.0f / Tv[e] : 0.0f;
+    const unsigned long long sd = (unsigned long long)a.seeds[bb];
+    const unsigned long long pk = (unsigned long long)(a.anchor_pos[bb] + k);
+    sk0[e] = (uint32_t)sd;
+    sk1[e] = (uint32_t)(sd >> 32);
+    pk0[e] = (uint32_t)pk;
+    pk1[e] = (uint32_t)(pk >> 32);
+    rbase[e] = (long long)bb * a.base_rs + (long long)k * a.base_ss;
+    rcache[e] = (long long)bb * a.cache_rs + (long long)k * a.cache_ss;
+  }
+  float bv[EPT], qm[EPT], qs[EPT];
+  int bi[EPT];
+  bool qnan[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    bv[e] = -INFINITY;
+    bi[e] = -1;
+    qm[e] = -INFINITY;
+    qs[e] = 0.0f;
+    qnan[e] = false;
+  }
+
+  // chunk loaders (w2 rows into registers, base into registers)
+  u32x4 wreg[WLMAX];
+  float bz[EPT][4], bzn[EPT][4];
+  auto load_w2 = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < WLMAX; ++i) {
+      if (i < RK) {
+        const int q = tid + 256 * i;  // 16-byte chunk of the 64-row block
+        const int row = q / cpr;
+        const int v = c0 + row;
+        const uint16_t* p = a.w2 + (size_t)(v < V ? v : 0) * r + (q - row * cpr) * 8;
+        u32x4 t = *(const u32x4*)p;
+        if (v >= V) t = u32x4{0u, 0u, 0u, 0u};
+        wreg[i] = t;
+      }
     }
+  };
+  auto store_w2 = [&]() {
+#pragma unroll
+    for (int i = 0; i < WLMAX; ++i) {
+      if (i < RK) {
+        const int q = tid + 256 * i;
+        const int row = q / cpr, ch = q - row * cpr;
+        *(u32x4*)(s_w + row * r + ((ch ^ (row & xmask)) * 8)) = wreg[i];
+      }
+    }
+  };
+  auto load_base = [&](int c0, float (&dst)[EPT][4]) {
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int c = c0 + ecol[e];
+      const int n = c_end - c >= 4 ? 4 : (c_end - c > 0 ? c_end - c : 0);
+      if (ev[e] && n > 0) {
+        if (a.base_bf16)
+          load_row4<true>(a.base, rbase[e] + c, n, a.vec_base, dst[e]);
+        else
+          load_row4<false>(a.base, rbase[e] + c, n, a.vec_base, dst[e]);
+      }
+    }
+  };
+
+  if (nchunks > 0) {
+    load_w2(c_begin);
+    load_base(c_begin, bz);
+    store_w2();
   }
   __syncthreads();
 
-  // per-lane request parameters for each 16-request sub-tile
   const int lrow = lane & 15, lgrp = lane >> 4;
-  bool rv[NT];
-  float Tv[NT], invT[NT];
-  uint32_t sk0[NT], sk1[NT], pk0[NT], pk1[NT];
-  long long rbase[NT], rcache[NT];
+  for (int ci = 0; ci < nchunks; ++ci) {
+    const int c0 = c_begin + ci * kCW;
+    const bool more = ci + 1 < nchunks;
+    if (more) {
+      load_w2(c0 + kCW);
+      load_base(c0 + kCW, bzn);
+    }
+    // projection of this wave's 16 columns for all NB requests
+    if (c0 + wave * 16 < c_end) {
+      floatx4 acc[NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int b = b0 + nt * 16 + lrow;
-    rv[nt] = b < a.B;
-    const int bb = rv[nt] ? b : 0;
-    Tv[nt] = a.temp[bb];
-    invT[nt] = Tv[nt] > 0.0f ? 1.0f / Tv[nt] : 0.0f;
-    const unsigned long long sd = (unsigned long long)a.seeds[bb];
-    const unsigned long long pk = (unsigned long long)(a.anchor_pos[bb] + k);
-    sk0[nt] = (uint32_t)sd;
-    sk1[nt] = (uint32_t)(sd >> 32);
-    pk0[nt] = (uint32_t)pk;
-    pk1[nt] = (uint32_t)(pk >> 32);
-    rbase[nt] = (long long)bb * a.base_rs + (long long)k * a.base_ss;
-    rcache[nt] = (long long)bb * a.cache_rs + (long long)k * a.cache_ss;
-  }
-
-  float bv[NT], qm[NT], qs[NT];
-  int bi[NT];
-  bool qnan[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    bv[nt] = -INFINITY;
-    bi[nt] = -1;
-    qm[nt] = -INFINITY;
-    qs[nt] = 0.0f;
-    qnan[nt] = false;
-  }
-
-  const int mt_begin = (int)(((long long)g * a.nMT) / a.G);
-  const int mt_end = (int)(((long long)(g + 1) * a.nMT) / a.G);
-  const int V = a.V, r = a.r;
-
-  for (int mt = mt_begin + wave; mt < mt_end; mt += 4) {
-    const int c0 = mt * 16;
-    // A operand: 16 rows of w2 (vocabulary columns c0..c0+15), 32 ranks per step
-    bf16x8 afr[RKMAX];
-    {
-      const int v = c0 + lrow;
-      const uint16_t* wp = a.w2 + (size_t)(v < V ? v : 0) * r + lgrp * 8;
+      for (int nt = 0; nt < NT; ++nt) acc[nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+      const int arow = wave * 16 + lrow;
 #pragma unroll
       for (int s = 0; s < RKMAX; ++s) {
         if (s < RK) {
-          bf16x8 t = *(const bf16x8*)(wp + s * 32);
-          if (v >= V) t = bf16x8{};
-          afr[s] = t;
+          const int ch = s * 4 + lgrp;
+          const bf16x8 afr = *(const bf16x8*)(s_w + arow * r + ((ch ^ (arow & xmask)) * 8));
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            const bf16x8 bfr = *(const bf16x8*)(s_e + (nt * 16 + lrow) * rs + s * 32 + lgrp * 8);
+            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr, acc[nt], 0, 0, 0);
+          }
         }
       }
-    }
-    // epilogue inputs: four consecutive columns of request (nt*16 + lrow)
-    const int c = c0 + lgrp * 4;
-    const int n = V - c >= 4 ? 4 : (V - c > 0 ? V - c : 0);
-    float bz[NT][4];
+      // lane holds bias of columns wave*16 + 4*lgrp + t for request nt*16 + lrow
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      if (rv[nt] && n > 0) {
-        if (a.base_bf16)
-          load4<true>(a.base, rbase[nt] + c, n, a.vec_base, bz[nt]);
-        else
-          load4<false>(a.base, rbase[nt] + c, n, a.vec_base, bz[nt]);
+      for (int nt = 0; nt < NT; ++nt) {
+        const f32x4 v = {acc[nt][0], acc[nt][1], acc[nt][2], acc[nt][3]};
+        *(f32x4*)(s_bias + (nt * 16 + lrow) * BST + wave * 16 + lgrp * 4) = v;
       }
     }
-    // projection: bias[c0 + i][request j] for the tile
-    floatx4 acc[NT];
+    __syncthreads();
+    // epilogue: bias + base -> cache, temperature, Gumbel noise, winner, q statistics
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int s = 0; s < RKMAX; ++s) {
-      if (s < RK) {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const bf16x8 bfr = *(const bf16x8*)(s_e + (nt * 16 + lrow) * rs + s * 32 + lgrp * 8);
-          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[s], bfr, acc[nt], 0, 0, 0);
-        }
-      }
-    }
-    if (n == 0) continue;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      if (!rv[nt]) continue;
+    for (int e = 0; e < EPT; ++e) {
+      const int c = c0 + ecol[e];
+      const int n = c_end - c >= 4 ? 4 : (c_end - c > 0 ? c_end - c : 0);
+      if (!ev[e] || n == 0) continue;
+      const f32x4 bias = *(const f32x4*)(s_bias + erow[e] * BST + ecol[e]);
       float z[4], cv[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) z[t] = bz[nt][t] + acc[nt][t];
+      z[0] = bz[e][0] + bias.x;
+      z[1] = bz[e][1] + bias.y;
+      z[2] = bz[e][2] + bias.z;
+      z[3] = bz[e][3] + bias.w;
       if (a.cache_bf16)
-        store4<true>(a.cache, rcache[nt] + c, n, a.vec_cache, z, cv);
+        store4<true>(a.cache, rcache[e] + c, n, a.vec_cache, z, cv);
       else
-        store4<false>(a.cache, rcache[nt] + c, n, a.vec_cache, z, cv);
-      if (Tv[nt] > 0.0f) {
-        const Philox4 w = philox4x32_10((uint32_t)(c >> 2), pk0[nt], pk1[nt], kSaltDraft, sk0[nt], sk1[nt]);
+        store4<false>(a.cache, rcache[e] + c, n, a.vec_cache, z, cv);
+      if (Tv[e] > 0.0f) {
+        const Philox4 w = philox4x32_10((uint32_t)(c >> 2), pk0[e], pk1[e], kSaltDraft, sk0[e], sk1[e]);
         const uint32_t wd[4] = {w.x0, w.x1, w.x2, w.x3};
         float x[4];
         float xm = -INFINITY;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const float sv = div_t(z[t], Tv[nt], invT[nt]) + gumbel_from_word(wd[t]);
-          if (t < n) win_update(bv[nt], bi[nt], sv, c + t);
-          const float xv = div_t(cv[t], Tv[nt], invT[nt]);
-          qnan[nt] |= (t < n) && (xv != xv);
+          const float sv = div_t(z[t], Tv[e], invT[e]) + gumbel_from_word(wd[t]);
+          if (t < n) win_update(bv[e], bi[e], sv, c + t);
+          const float xv = div_t(cv[t], Tv[e], invT[e]);
+          qnan[e] |= (t < n) && (xv != xv);
           x[t] = (t < n && xv == xv) ? xv : -INFINITY;
           xm = fmaxf(xm, x[t]);
         }
-        const float mn = fmaxf(qm[nt], xm);
+        const float mn = fmaxf(qm[e], xm);
         if (mn != -INFINITY) {
-          float acc_s = qs[nt] * fast_exp(qm[nt] - mn);
+          float acc_s = qs[e] * fast_exp(qm[e] - mn);
 #pragma unroll
           for (int t = 0; t < 4; ++t) acc_s += fast_exp(x[t] - mn);
-          qs[nt] = acc_s;
-          qm[nt] = mn;
+          qs[e] = acc_s;
+          qm[e] = mn;
         }
       } else {
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-          if (t < n) win_update(bv[nt], bi[nt], z[t], c + t);
+          if (t < n) win_update(bv[e], bi[e], z[t], c + t);
       }
     }
+    if (more) {
+      store_w2();
+#pragma unroll
+      for (int e = 0; e < EPT; ++e)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) bz[e][t] = bzn[e][t];
+    }
+    __syncthreads();
   }
 
-  // merge the four lanes of each request, then the four waves, then publish
+  // merge: the 16 threads of one request row are 16 consecutive lanes
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    uint64_t key = bi[nt] >= 0 ? win_key(bv[nt], (uint32_t)bi[nt]) : 0ull;
-    key = max_over_groups16(key);
-    float m = qm[nt], s = qnan[nt] ? NAN : qs[nt];
-    {
-      float m2 = __shfl_xor(m, 16), s2 = __shfl_xor(s, 16);
-      lse_merge(m, s, m2, s2);
-      m2 = __shfl_xor(m, 32);
-      s2 = __shfl_xor(s, 32);
+  for (int e = 0; e < EPT; ++e) {
+    unsigned long long key = bi[e] >= 0 ? win_key(bv[e], (uint32_t)bi[e]) : 0ull;
+    float m = qm[e], s = qnan[e] ? NAN : qs[e];
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const unsigned long long k2 = __shfl_xor(key, off);
+      key = k2 > key ? k2 : key;
+      const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(s, off);
       lse_merge(m, s, m2, s2);
     }
-    if (lgrp == 0) {
-      s_key[wave * NB + nt * 16 + lrow] = key;
-      s_qm[wave * NB + nt * 16 + lrow] = m;
-      s_qs[wave * NB + nt * 16 + lrow] = s;
+    if ((lane & 15) == 0) {
+      s_key[erow[e]] = key;
+      s_qm[erow[e]] = m;
+      s_qs[erow[e]] = s;
     }
   }
   __syncthreads();
   for (int i = tid; i < NB; i += 256) {
     const int b = b0 + i;
     if (b >= a.B) continue;
-    unsigned long long key = s_key[i];
-    float m = s_qm[i], s = s_qs[i];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) {
-      const unsigned long long k2 = s_key[w * NB + i];
-      key = k2 > key ? k2 : key;
-      lse_merge(m, s, s_qm[w * NB + i], s_qs[w * NB + i]);
-    }
+    const unsigned long long key = s_key[i];
     if (key) atomicMax(&a.keys[(size_t)k * a.B + b], key);
-    a.qpart[((size_t)k * a.B + b) * a.G + g] = make_float2(m, s);
+    a.qpart[((size_t)k * a.B + b) * a.G + g] = make_float2(s_qm[i], s_qs[i]);
   }
 }
 
-__global__ __launch_bounds__(256) void draft_init_kernel(unsigned long long* keys, int n) {
+__global__ __launch_bounds__(256) void draft_init_kernel(unsigned long long* keys, int n, unsigned* bar, int nbar) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < n) keys[i] = 0ull;
+  if (i < nbar) bar[i] = 0u;
 }
 
 // Draft tokens from the winner keys, and log-sum-exp of cache / T per row
@@ -347,7 +410,12 @@ __global__ __launch_bounds__(256) void draft_finalize_kernel(DraftFinalArgs a) {
 
 template <int NB, int RKT>
 hipError_t launch_step(const DraftStepArgs& a, int bt, hipStream_t st) {
-  const size_t lds = (size_t)NB * (a.r + 8) * 2 + NB * 4 + 4 * NB * 8 + 8 * NB * 4;
+  const size_t lds = draft_step_lds(NB, a.r);
+  if (lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute((const void*)draft_step_kernel<NB, RKT>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
   DraftStepArgs b = a;
   b.BT = bt;
   hipLaunchKernelGGL((draft_step_kernel<NB, RKT>), dim3(a.G * bt), dim3(256), lds, st, b);
@@ -374,8 +442,9 @@ int draft_nb(int B, int r) {
   return B <= 16 ? 16 : 32;
 }
 
-hipError_t launch_draft_init(unsigned long long* keys, int n, hipStream_t st) {
-  hipLaunchKernelGGL(draft_init_kernel, dim3((n + 255) / 256), dim3(256), 0, st, keys, n);
+hipError_t launch_draft_init(unsigned long long* keys, int n, unsigned* bar, int nbar, hipStream_t st) {
+  const int m = n > nbar ? n : nbar;
+  hipLaunchKernelGGL(draft_init_kernel, dim3((m + 255) / 256), dim3(256), 0, st, keys, n, bar, nbar);
   return hipGetLastError();
 }
 

@@ -27,6 +27,10 @@ struct DraftStepArgs {
   unsigned long long* keys;  // [K][B] winner keys
   float2* qpart;             // [K][B][G] (max, sum exp) of cache / T per slab
   uint32_t* status;
+  unsigned* bar;             // [K] grid-barrier arrival counters (resident kernel)
+  unsigned* abort_flag;      // set when a barrier wait times out (resident kernel)
+  int n_lds_tiles;           // resident kernel: LDS tiles per work-group (max)
+  int zero;                  // always 0 (an offset the compiler cannot fold)
 };
 
 struct DraftFinalArgs {
@@ -39,9 +43,14 @@ struct DraftFinalArgs {
 };
 
 int draft_nb(int B, int r);
-int draft_slabs(int V);
-hipError_t launch_draft_init(unsigned long long* keys, int n, hipStream_t st);
+int draft_slabs(int V, int cus);
+hipError_t launch_draft_init(unsigned long long* keys, int n, unsigned* bar, int nbar, hipStream_t st);
 hipError_t launch_draft_step(const DraftStepArgs& a, hipStream_t st);
+// Resident path: one launch runs all K steps with w2 held on chip. Returns
+// hipErrorNotSupported (and launches nothing) when w2 does not fit.
+hipError_t draft_resident_plan(int V, int r, int G, size_t lds_limit, int* n_lds_tiles, size_t* lds_bytes);
+hipError_t launch_draft_resident(const DraftStepArgs& a, size_t lds_bytes, hipStream_t st);
+constexpr uint32_t kStatusBarrierTimeout = 4u;
 hipError_t launch_draft_finalize(const DraftFinalArgs& a, hipStream_t st);
 
 // ---------------------------------------------------------- verification --

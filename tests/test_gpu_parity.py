@@ -10,6 +10,14 @@ from parity import Report, compare_draft, compare_verify, full_parity, run_gpu, 
 pytestmark = pytest.mark.gpu
 
 
+@pytest.fixture(params=["auto", "stream"], autouse=True)
+def draft_path(request, monkeypatch):
+    """Every parity case runs with the resident draft kernel ("auto" uses it
+    wherever w2 fits on chip) and with the streaming kernel."""
+    monkeypatch.setenv("MDS_DRAFT_PATH", request.param)
+    return request.param
+
+
 def _assert(rep: Report, label: str):
     print(f"{label}: tokens {rep.tokens_total} (excused {rep.tokens_excused}, bad {rep.tokens_bad}); "
           f"cache max err {rep.cache_max_err:.2e} (excused {rep.cache_excused}, bad {rep.cache_bad}); "
