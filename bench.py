@@ -77,6 +77,8 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=8, help="requests the CPU oracle baseline runs on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="do not flush caches between timed steps")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (reference dispatch for counter scaling)")
     a = ap.parse_args()
     if a.gpus != 1:
         print("bench.py runs on one GPU only: the path is measured on a single MI355X "
@@ -194,6 +196,14 @@ def main():
         "status_word": status,
         "timed_wall_s": wall,
     }
+    if a.copy_calibration:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            flush.sum()
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = {"read": src.numel() * 4, "write": dst.numel() * 4}
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, min(a.cpu_sample, B))
     print(json.dumps(res), flush=True)

@@ -211,6 +211,19 @@ int mds_debug_noise(int n, const int32_t* cols, int64_t seed, int64_t pos_key, u
                     uint32_t* words, float* gumbel, void* stream);
 
 /*
+ * mds_debug_top_p - test hook: the exact top-p kept set of `rows` independent
+ * rows (row i at target + i*row_stride, temperature[i] > 0, top_p[i]) as
+ * verification computes it: column v is kept iff ord(t_v) > tau[i], or
+ * ord(t_v) == tau[i] and v <= cut[i], where ord maps a float to an unsigned key
+ * in the same order (NaN above all, -0 == +0); log_z[i] is the log of the kept
+ * mass sum exp(x - max x), x = t / T. on[i] = 0 means nothing was filtered
+ * (top_p >= 1). workspace >= mds_verify_workspace_bytes(rows, 1, V, 1, 1).
+ */
+int mds_debug_top_p(int rows, int V, const float* target, int64_t row_stride, const float* temperature,
+                    const float* top_p, uint32_t* tau, int32_t* cut, float* log_z, int32_t* on,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * mds_debug_gumbel - test hook: the float32 Gumbel variate the kernels derive
  * from each given 32-bit word (device arrays of n elements). Only the top 23
  * bits of a word matter, so 2^23 words cover every possible variate.

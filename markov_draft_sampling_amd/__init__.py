@@ -18,7 +18,7 @@ import os
 __all__ = [
     "F32", "BF16", "MdsError", "library_path", "abi_version", "draft_workspace_bytes", "verify_workspace_bytes",
     "new_workspace", "workspace_status", "markov_draft_loop", "markov_draft_loop_timed", "rejection_verify",
-    "debug_noise", "debug_gumbel", "STATUS_BAD_ANCHOR", "STATUS_BAD_DRAFT", "STATUS_BARRIER_TIMEOUT", "SALT_DRAFT", "SALT_ACCEPT",
+    "debug_noise", "debug_gumbel", "debug_top_p", "STATUS_BAD_ANCHOR", "STATUS_BAD_DRAFT", "STATUS_BARRIER_TIMEOUT", "SALT_DRAFT", "SALT_ACCEPT",
     "SALT_RESAMPLE",
 ]
 
@@ -55,6 +55,7 @@ _SIGS = {
                                              _vp, _vp, _vp, _c_sz, _vp], _c_int),
     "mds_debug_noise": ([_c_int, _vp, _c_i64, _c_i64, ctypes.c_uint32, _vp, _vp, _vp], _c_int),
     "mds_debug_gumbel": ([_c_int, _vp, _vp, _vp], _c_int),
+    "mds_debug_top_p": ([_c_int, _c_int, _vp, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp], _c_int),
 }
 
 
@@ -250,3 +251,23 @@ def debug_gumbel(words):
     g = torch.empty(words.numel(), dtype=torch.float32, device=words.device)
     _check(_lib().mds_debug_gumbel(words.numel(), _ptr(words), _ptr(g), _stream(None, words.device)), "debug_gumbel")
     return g
+
+
+def debug_top_p(target, temperature, top_p):
+    """Exact top-p kept set per row as verification computes it.
+
+    target: float32 [rows, V] on the GPU; temperature, top_p: float32 [rows].
+    Returns (tau uint32-as-int64, cut, log_z, on) tensors of [rows].
+    """
+    import torch
+    rows, V = target.shape
+    _need(target.is_cuda and target.dtype == torch.float32 and target.stride(1) == 1, "target: float32 [rows, V]")
+    ws = new_workspace(verify_workspace_bytes(rows, 1, V, True, True), target.device)
+    tau = torch.empty(rows, dtype=torch.int32, device=target.device)
+    cut = torch.empty(rows, dtype=torch.int32, device=target.device)
+    log_z = torch.empty(rows, dtype=torch.float32, device=target.device)
+    on = torch.empty(rows, dtype=torch.int32, device=target.device)
+    _check(_lib().mds_debug_top_p(rows, V, _ptr(target), target.stride(0), _ptr(temperature), _ptr(top_p), _ptr(tau),
+                                  _ptr(cut), _ptr(log_z), _ptr(on), _ptr(ws), ws.numel(), _stream(None, target.device)),
+           "debug_top_p")
+    return tau.to(torch.int64) & 0xFFFFFFFF, cut, log_z, on

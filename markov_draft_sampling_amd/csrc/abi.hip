@@ -326,6 +326,41 @@ int mds_debug_noise(int n, const int32_t* cols, int64_t seed, int64_t pos_key, u
   return e == hipSuccess ? ok() : hip_fail(e, "debug noise launch");
 }
 
+int mds_debug_top_p(int rows, int V, const float* target, int64_t row_stride, const float* temperature,
+                    const float* top_p, uint32_t* tau, int32_t* cut, float* log_z, int32_t* on, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  int rc;
+  if ((rc = check_sizes(rows, 1, V))) return rc;
+  if (!target || !temperature || !top_p || !tau || !cut || !log_z || !on || !workspace)
+    return fail(MDS_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (row_stride < V) return fail(MDS_ERR_INVALID_ARG, "row_stride must be >= V");
+  if (!aligned(workspace, kAlign)) return fail(MDS_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const VerifyLayout L = verify_layout(rows, 1, V, true, true);
+  if (workspace_bytes < L.total) return fail(MDS_ERR_WORKSPACE, "workspace too small");
+  unsigned char* ws = (unsigned char*)workspace;
+  hipStream_t st = (hipStream_t)stream;
+  // every row is its own request with K = 0: row b*(K+1)+j is just b
+  mds::VerifyArgs a{};
+  a.B = rows;
+  a.K = 0;
+  a.V = V;
+  a.NC = L.NC;
+  a.target = target;
+  a.target_rs = row_stride;
+  a.vec_target = aligned(target, 16) && row_stride % 4 == 0;
+  a.temp = temperature;
+  a.top_p = top_p;
+  a.tpart = (mds::StatPart*)(ws + L.tpart);
+  a.topp = (mds::TopP*)(ws + L.topp);
+  a.status = (uint32_t*)ws;
+  hipError_t e;
+  if ((e = mds::launch_target_stats(a, st)) != hipSuccess) return hip_fail(e, "target stats launch");
+  if ((e = mds::launch_top_p(a, st)) != hipSuccess) return hip_fail(e, "top-p launch");
+  if ((e = mds::launch_debug_top_p_out(rows, a.topp, tau, cut, log_z, on, st)) != hipSuccess)
+    return hip_fail(e, "top-p output launch");
+  return ok();
+}
+
 int mds_debug_gumbel(int n, const uint32_t* words, float* gumbel, void* stream) {
   if (n < 0) return fail(MDS_ERR_INVALID_ARG, "n must be >= 0");
   if (n == 0) return ok();

@@ -98,11 +98,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 }
 
 // ------------------------------------------------------------ arithmetic --
-// z / T from a precomputed reciprocal plus one residual correction.
+// z / T from a precomputed reciprocal plus one residual correction; an
+// infinite z keeps its sign (the correction would turn it into NaN).
 __device__ __forceinline__ float div_t(float z, float T, float invT) {
   const float q = z * invT;
   const float r = __builtin_fmaf(-q, T, z);
-  return __builtin_fmaf(r, invT, q);
+  const float y = __builtin_fmaf(r, invT, q);
+  return __builtin_isinf(q) ? q : y;
 }
 
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 0x1.715476p+0f); }

@@ -118,5 +118,7 @@ hipError_t launch_verify_finalize(const VerifyArgs& a, hipStream_t st);
 hipError_t launch_debug_noise(int n, const int32_t* cols, long long seed, long long pos, uint32_t salt,
                               uint32_t* words, float* g, hipStream_t st);
 hipError_t launch_debug_gumbel(int n, const uint32_t* words, float* g, hipStream_t st);
+hipError_t launch_debug_top_p_out(int rows, const TopP* tp, uint32_t* tau, int32_t* cut, float* log_z, int32_t* on,
+                                  hipStream_t st);
 
 }  // namespace mds

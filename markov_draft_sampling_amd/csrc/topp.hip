@@ -116,6 +116,10 @@ __global__ __launch_bounds__(kTp) void top_p_kernel(VerifyArgs a) {
     if (tid == 0) s_M = m;
   }
   __syncthreads();
+  if (s_M == -INFINITY) {  // no finite logit: only the first column (the row maximum by rule) is kept
+    if (tid == 0) *out = TopP{ord_f32(-INFINITY), 0, -INFINITY, 1};
+    return;
+  }
   RowCtx rc{a.target + (long long)row * a.target_rs, a.V, a.vec_target != 0, T, 1.0f / T, s_M};
 
   // narrowing levels: (shift, width) of the digit below the fixed prefix
@@ -314,9 +318,27 @@ __global__ __launch_bounds__(kTp) void top_p_kernel(VerifyArgs a) {
   }
 }
 
+__global__ void debug_top_p_out_kernel(int rows, const TopP* tp, uint32_t* tau, int32_t* cut, float* log_z,
+                                       int32_t* on) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows) return;
+  tau[i] = tp[i].tau;
+  cut[i] = tp[i].cut;
+  log_z[i] = tp[i].log_z;
+  on[i] = tp[i].on;
+}
+
 }  // namespace
 
+hipError_t launch_debug_top_p_out(int rows, const TopP* tp, uint32_t* tau, int32_t* cut, float* log_z, int32_t* on,
+                                  hipStream_t st) {
+  hipLaunchKernelGGL(debug_top_p_out_kernel, dim3((rows + 255) / 256), dim3(256), 0, st, rows, tp, tau, cut, log_z,
+                     on);
+  return hipGetLastError();
+}
+
 hipError_t launch_top_p(const VerifyArgs& a, hipStream_t st) {
+  if (a.B * (a.K + 1) == 0) return hipSuccess;
   hipLaunchKernelGGL(top_p_kernel, dim3(a.B * (a.K + 1)), dim3(kTp), 0, st, a);
   return hipGetLastError();
 }
