@@ -43,7 +43,29 @@ def algorithmic_bytes(B, K, V, r, s_base=4, s_cache=4, s_tgt=4):
     return draft_step, draft, verify
 
 
-def cpu_baseline(wl, n_req: int):
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "markov_draft_sampling_amd", "csrc")
+
+
+def recorded_traffic(profile: str, sources) -> float | None:
+    """HBM bytes per launch from a committed counter summary, or None when the
+    kernel sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(PROFILES, profile)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "kernel_source_sha256"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    h = hashlib.sha256(b"".join(open(os.path.join(CSRC, n), "rb").read() for n in sources)).hexdigest()
+    if fields.get("kernel_source_sha256") != h or "traffic_bytes_per_launch" not in fields:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
+
+
+def cpu_baseline(wl, n_req: int, repeats: int = 2):
     """The oracle, as it stands, on the first n_req requests of the workload."""
     import numpy as np
     import oracle
@@ -54,18 +76,19 @@ def cpu_baseline(wl, n_req: int):
         ctx = None
     rows = np.arange(n_req)
     K = wl.K
-    t0 = time.perf_counter()
-    d = oracle.draft_loop(wl.draft_base[rows], wl.base_dtype, wl.w1, wl.w2, wl.anchor_tokens[rows],
-                          wl.anchor_pos[rows], wl.seeds[rows], wl.temperature[rows], wl.cache_dtype)
     tgt = wl.target.reshape(wl.B, K + 1, wl.V)[rows].reshape(n_req * (K + 1), wl.V)
-    oracle.verify(tgt, d["cache"], wl.cache_dtype, d["tokens"], wl.temperature[rows],
-                  None if wl.top_p is None else wl.top_p[rows], wl.seeds[rows], wl.anchor_pos[rows])
-    dt = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for _ in range(repeats):
+        d = oracle.draft_loop(wl.draft_base[rows], wl.base_dtype, wl.w1, wl.w2, wl.anchor_tokens[rows],
+                              wl.anchor_pos[rows], wl.seeds[rows], wl.temperature[rows], wl.cache_dtype)
+        oracle.verify(tgt, d["cache"], wl.cache_dtype, d["tokens"], wl.temperature[rows],
+                      None if wl.top_p is None else wl.top_p[rows], wl.seeds[rows], wl.anchor_pos[rows])
+    dt = (time.perf_counter() - t0) / repeats
     if ctx is not None:
         ctx.unregister() if hasattr(ctx, "unregister") else None
     return {"value": n_req * K / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_req} of the {wl.B} requests (all {K} draft steps + verification), "
-                      f"float64 NumPy, BLAS limited to 1 thread; {dt:.1f} s"}
+            "sample": f"{n_req} of the {wl.B} requests (all {K} draft steps + verification), run {repeats} times, "
+                      f"float64 NumPy, BLAS limited to 1 thread; {dt:.1f} s per run"}
 
 
 def main():
@@ -74,7 +97,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--batch", type=int, default=32)
-    ap.add_argument("--cpu-sample", type=int, default=8, help="requests the CPU oracle baseline runs on")
+    ap.add_argument("--cpu-sample", type=int, default=32, help="requests the CPU oracle baseline runs on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="do not flush caches between timed steps")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -163,6 +186,14 @@ def main():
     achieved = bytes_per_launch / (kern_avg_ms * 1e-3) / 1e9
     step_gbps = (draft_b + verify_b) / (ms * 1e-3) / 1e9
     acc_len = float((nacc.float() + 1).mean().item())
+    if n_launch == 1:
+        traffic = recorded_traffic("draft_resident_kernel_hbm_traffic_V200064_B32.md",
+                                   ("draft_resident.hip", "mds_device.h", "mds_internal.h"))
+    else:
+        traffic = recorded_traffic("draft_step_kernel_hbm_traffic_V200064_B32.md",
+                                   ("draft.hip", "mds_device.h", "mds_internal.h"))
+    if B != 32:
+        traffic = None
     status = mds.workspace_status(ws_d) | mds.workspace_status(ws_v)
 
     res = {
@@ -186,7 +217,7 @@ def main():
         "roofline": {"kernel": ("draft_resident_kernel (all K Markov steps, w2 held on chip)" if n_launch == 1 else
                                 "draft_step_kernel (one Markov step, w2 streamed)"),
                      "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "bytes_per_launch": bytes_per_launch, "avg_launch_us": kern_avg_ms * 1e3,
                      "launches": int(n_launch * a.steps)},
         "warm": {"ms_per_step": warm_ms, "value": tokens / (warm_ms * 1e-3)},
