@@ -31,23 +31,28 @@ namespace {
 constexpr int kNB = 32;        // requests per batch tile
 constexpr int kThreads = 256;  // 4 waves, one per SIMD
 constexpr unsigned kSpinLimit = 1u << 21;
+constexpr int kDepth = 4;      // base-row tiles in flight per wave (register ring)
 
 __device__ __forceinline__ size_t fixed_lds(int r) {
   return (size_t)kNB * (r + 8) * 2 + kNB * 4 + 4 * kNB * 8 + 8 * kNB * 4 + 64;
 }
 
 // Wait until `target` work-groups have arrived at `counter`. Returns false
-// when the wait was abandoned (timeout here or elsewhere).
+// when the wait was abandoned (timeout here or elsewhere). The only data the
+// next step reads across work-groups are the winner keys, written by
+// device-scope atomics that have returned (so are performed) before this
+// barrier and read back with device-scope atomic loads; no cache maintenance
+// is needed (a release fence here would write back the L2, full of cache rows).
 __device__ bool grid_barrier(unsigned* counter, unsigned target, unsigned* abort_flag, uint32_t* status,
                              int* s_flag) {
-  __threadfence();  // every thread's winner atomics are complete at device scope
   __syncthreads();
   if (threadIdx.x == 0) {
-    __threadfence();  // publish this work-group's winner atomics and partials
     atomicAdd(counter, 1u);
     int ok = 1;
     unsigned spins = 0;
-    while (__hip_atomic_load(counter, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    // poll with relaxed device-scope loads (served past the non-coherent L2,
+    // no cache maintenance per poll), then one acquire fence after the wait
+    while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
       if (__hip_atomic_load(abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
         ok = 0;
         break;
@@ -58,7 +63,7 @@ __device__ bool grid_barrier(unsigned* counter, unsigned target, unsigned* abort
         ok = 0;
         break;
       }
-      __builtin_amdgcn_s_sleep(8);
+      __builtin_amdgcn_s_sleep(2);
     }
     *s_flag = ok;
   }
@@ -265,7 +270,9 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         qnan[nt] = false;
       }
 
-      float cur[NT][4], nxt[NT][4];
+      // base rows of the next kDepth-1 tiles stay in flight in a register ring
+      // (the tile loop is unrolled by kDepth so every slot has a static index)
+      float ring[kDepth][NT][4];
       auto load_base = [&](int t, float (&dst)[NT][4]) {
         const int c = tile_col(t) + lgrp * 4;
         const int n = V - c >= 4 ? 4 : (V - c > 0 ? V - c : 0);
@@ -279,7 +286,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
           }
         }
       };
-      auto epilogue = [&](int t, const floatx4 (&acc)[NT]) {
+      auto epilogue = [&](int t, const floatx4 (&acc)[NT], const float (&bz)[NT][4]) {
         const int c = tile_col(t) + lgrp * 4;
         const int n = V - c >= 4 ? 4 : (V - c > 0 ? V - c : 0);
         if (n == 0) return;
@@ -288,7 +295,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
           if (!rv[nt]) continue;
           float z[4], cv[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) z[i] = cur[nt][i] + acc[nt][i];
+          for (int i = 0; i < 4; ++i) z[i] = bz[nt][i] + acc[nt][i];
           if (a.cache_bf16)
             store_col4<true>(a.cache, rcache[nt] + c, n, a.vec_cache, z, cv);
           else
@@ -322,11 +329,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
           }
         }
       };
-
-      if (T_w > 0) load_base(0, cur);
-      for (int t = 0; t < T_w; ++t) {
-        if (t + 1 < T_w) load_base(t + 1, nxt);
-        floatx4 acc[NT];
+      auto project = [&](int t, floatx4 (&acc)[NT]) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
         if (t < R_w) {
@@ -362,11 +365,22 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
               acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfrag(s, nt, t), acc[nt], 0, 0, 0);
           }
         }
-        epilogue(t, acc);
+      };
+
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+      for (int u = 0; u < kDepth - 1; ++u)
+        if (u < T_w) load_base(u, ring[u]);
+      for (int t0 = 0; t0 < T_w; t0 += kDepth) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) cur[nt][i] = nxt[nt][i];
+        for (int u = 0; u < kDepth; ++u) {
+          const int t = t0 + u;
+          if (t < T_w) {
+            if (t + kDepth - 1 < T_w) load_base(t + kDepth - 1, ring[(u + kDepth - 1) % kDepth]);
+            floatx4 acc[NT];
+            project(t, acc);
+            epilogue(t, acc, ring[u]);
+          }
+        }
       }
 
       // merge the four lanes of each request, then the four waves, then publish
@@ -398,7 +412,9 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
             key = k2 > key ? k2 : key;
             lse_merge(m, s, s_qm[w * kNB + tid], s_qs[w * kNB + tid]);
           }
-          if (key) atomicMax(&a.keys[(size_t)k * B + b], key);
+          // the returned value makes the wave wait until the atomic is performed
+          const unsigned long long prev = key ? atomicMax(&a.keys[(size_t)k * B + b], key) : 0ull;
+          s_flag[1] = (int)(prev >> 63);
           a.qpart[((size_t)k * B + b) * G + g] = make_float2(m, s);
         }
       }
