@@ -170,7 +170,10 @@ int mds_markov_draft_loop(int B, int K, int V, int r,
  *   temperature, seeds, anchor_pos   as for the draft loop
  *   top_p                 float [B] or NULL (off); a value >= 1 turns it off for that request
  *   workspace             >= mds_verify_workspace_bytes(B, K, V, top_p != NULL,
- *                         draft_lse != NULL) bytes, 256-byte aligned
+ *                         draft_lse != NULL) bytes, 256-byte aligned, zero-filled
+ *                         before its first use. Bytes [256, 256 + 512 KiB) hold one
+ *                         arrival counter per request that every call leaves at
+ *                         zero; the caller must not write the workspace between calls.
  */
 int mds_rejection_verify(int B, int K, int V,
                          const float* target, int64_t target_row_stride,

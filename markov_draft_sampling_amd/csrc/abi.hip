@@ -84,26 +84,44 @@ int draft_path_choice() {
 
 struct VerifyLayout {
   int NC;
-  size_t tpart, qpart, qlse, topp, req, rpart, total;
+  size_t tpart, qpart, rowstat, qlse, topp, req, rkey, total;
 };
 
+// [status block][per-request counters, fixed size][partials and per-row state]
 VerifyLayout verify_layout(int B, int K, int V, bool top_p, bool has_lse) {
   VerifyLayout L;
   L.NC = (V + mds::kStatsChunk - 1) / mds::kStatsChunk;
-  size_t o = kAlign;
+  size_t o = mds::kVerifyCounterOffset + mds::kVerifyCounterBytes;
   L.tpart = o;
-  o += up((size_t)B * (K + 1) * L.NC * sizeof(mds::StatPart));
+  o += up((size_t)B * (K + 1) * L.NC * 8);
   L.qpart = has_lse ? 0 : o;
-  if (!has_lse) o += up((size_t)B * K * L.NC * sizeof(mds::StatPart));
-  L.qlse = 0;
+  if (!has_lse) o += up((size_t)B * K * L.NC * 8);
+  L.rowstat = o;
+  o += up((size_t)B * (K + 1) * sizeof(mds::RowStat));
+  L.qlse = o;
+  o += up((size_t)B * K * sizeof(float));
   L.topp = top_p ? o : 0;
   if (top_p) o += up((size_t)B * (K + 1) * sizeof(mds::TopP));
   L.req = o;
   o += up((size_t)B * sizeof(mds::ReqState));
-  L.rpart = o;
-  o += up((size_t)B * L.NC * sizeof(mds::ResPart));
+  L.rkey = o;
+  o += up((size_t)B * 16);
   L.total = o;
   return L;
+}
+
+void verify_workspace_args(mds::VerifyArgs& a, unsigned char* ws, const VerifyLayout& L, bool top_p, bool has_lse) {
+  a.NC = L.NC;
+  a.status = (uint32_t*)ws;
+  a.cnt = (unsigned*)(ws + mds::kVerifyCounterOffset);
+  a.tpart = (unsigned long long*)(ws + L.tpart);
+  a.qpart = has_lse ? nullptr : (unsigned long long*)(ws + L.qpart);
+  a.rowstat = (mds::RowStat*)(ws + L.rowstat);
+  a.qlse = (float*)(ws + L.qlse);
+  a.topp = top_p ? (mds::TopP*)(ws + L.topp) : nullptr;
+  a.req = (mds::ReqState*)(ws + L.req);
+  a.rkey = (unsigned long long*)(ws + L.rkey);
+  a.decide = !top_p;
 }
 
 int hip_fail(hipError_t e, const char* where) {
@@ -285,7 +303,6 @@ int mds_rejection_verify(int B, int K, int V, const float* target, int64_t targe
   a.B = B;
   a.K = K;
   a.V = V;
-  a.NC = L.NC;
   a.target = target;
   a.target_rs = target_row_stride;
   a.vec_target = aligned(target, 16) && target_row_stride % 4 == 0;
@@ -302,18 +319,14 @@ int mds_rejection_verify(int B, int K, int V, const float* target, int64_t targe
   a.anchor_pos = (const long long*)anchor_pos;
   a.out_tokens = out_tokens;
   a.num_accepted = num_accepted;
-  a.tpart = (mds::StatPart*)(ws + L.tpart);
-  a.qpart = draft_lse ? nullptr : (mds::StatPart*)(ws + L.qpart);
-  a.topp = top_p ? (mds::TopP*)(ws + L.topp) : nullptr;
-  a.req = (mds::ReqState*)(ws + L.req);
-  a.rpart = (mds::ResPart*)(ws + L.rpart);
-  a.status = (uint32_t*)ws;
+  verify_workspace_args(a, ws, L, top_p != nullptr, draft_lse != nullptr);
   hipError_t e;
-  if ((e = mds::launch_target_stats(a, st)) != hipSuccess) return hip_fail(e, "target stats launch");
-  if (!draft_lse && (e = mds::launch_draft_stats(a, st)) != hipSuccess) return hip_fail(e, "draft stats launch");
-  if (top_p && (e = mds::launch_top_p(a, st)) != hipSuccess) return hip_fail(e, "top-p launch");
+  if ((e = mds::launch_verify_stats(a, st)) != hipSuccess) return hip_fail(e, "verify stats launch");
+  if (top_p) {
+    if ((e = mds::launch_top_p(a, st)) != hipSuccess) return hip_fail(e, "top-p launch");
+    if ((e = mds::launch_decide(a, st)) != hipSuccess) return hip_fail(e, "decide launch");
+  }
   if ((e = mds::launch_residual(a, st)) != hipSuccess) return hip_fail(e, "residual launch");
-  if ((e = mds::launch_verify_finalize(a, st)) != hipSuccess) return hip_fail(e, "verify finalize launch");
   return ok();
 }
 
@@ -344,17 +357,14 @@ int mds_debug_top_p(int rows, int V, const float* target, int64_t row_stride, co
   a.B = rows;
   a.K = 0;
   a.V = V;
-  a.NC = L.NC;
   a.target = target;
   a.target_rs = row_stride;
   a.vec_target = aligned(target, 16) && row_stride % 4 == 0;
   a.temp = temperature;
   a.top_p = top_p;
-  a.tpart = (mds::StatPart*)(ws + L.tpart);
-  a.topp = (mds::TopP*)(ws + L.topp);
-  a.status = (uint32_t*)ws;
+  verify_workspace_args(a, ws, L, true, true);
   hipError_t e;
-  if ((e = mds::launch_target_stats(a, st)) != hipSuccess) return hip_fail(e, "target stats launch");
+  if ((e = mds::launch_verify_stats(a, st)) != hipSuccess) return hip_fail(e, "verify stats launch");
   if ((e = mds::launch_top_p(a, st)) != hipSuccess) return hip_fail(e, "top-p launch");
   if ((e = mds::launch_debug_top_p_out(rows, a.topp, tau, cut, log_z, on, st)) != hipSuccess)
     return hip_fail(e, "top-p output launch");

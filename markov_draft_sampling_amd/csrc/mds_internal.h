@@ -56,9 +56,12 @@ hipError_t launch_draft_finalize(const DraftFinalArgs& a, hipStream_t st);
 // ---------------------------------------------------------- verification --
 constexpr int kStatsChunk = 8192;  // columns per statistics block (the pages' 8192-column blocks)
 
-struct StatPart {  // one (row, chunk) partial of a target or draft row
-  float m;         // max of x = logit / T (T > 0)
-  float s;         // sum of exp(x - m); NaN if the chunk held NaN
+// Partials of one (row, block) are published as one 64-bit word: for a
+// sampled row (max, sum exp) of x = logit / T as two floats (max in the low
+// half), for a greedy row the winner key of the raw logits.
+struct RowStat {  // combined statistics of one target row
+  float m;        // max of x = logit / T (sampled rows)
+  float lz;       // log of sum exp(x - m); NaN if the row held NaN
   unsigned long long key;  // winner key of the raw logits (greedy rows)
 };
 
@@ -69,19 +72,23 @@ struct TopP {  // kept set of one target row: ord(t) > tau, or == tau and id <= 
   int on;
 };
 
-struct ReqState {
-  int n_acc;     // accepted drafts
-  int jstar;     // row of the final draw (n_acc)
-  int mode;      // 0 bonus from p_K, 1 residual of row jstar, 2 greedy (token below), 3 residual empty -> p
-  int token;     // greedy final token
+struct ReqState {  // the accept decision of one request, read by the residual draw
+  int n_acc;   // accepted drafts; the final token is drawn from row n_acc
+  int mode;    // 0 bonus from p_K, 1 residual of row n_acc, 2 greedy (done), 3 residual empty -> p
+  float M, LZ; // row n_acc: max of logit / T and log of its (kept) mass
+  float LQ;    // draft row n_acc: log sum exp of cache / T (mode 1)
+  int pad;
+  TopP tp;     // kept set of row n_acc (tp.on == 0 when no top-p)
 };
 
-struct ResPart {
-  unsigned long long key_r;  // Gumbel-max winner over log residual
-  unsigned long long key_p;  // Gumbel-max winner over log p (bonus / empty residual)
-  float sum_r;               // residual mass of the chunk
-  float pad;
-};
+// The kVerifyCounterBytes after the verify workspace's 256-byte status block
+// hold one arrival counter per request. Every call leaves them at zero, so
+// they sit at a fixed offset whatever (B, K, V) a call uses. Requests
+// b and b + 2048k share a 256-byte line; any other two counters do not (many
+// work-groups bumping counters of one line serialise on it).
+constexpr size_t kVerifyCounterOffset = 256;
+constexpr size_t kVerifyCounterBytes = (size_t)2048 * 256;
+__host__ __device__ constexpr int verify_counter_index(int b) { return (b & 2047) * 64 + (b >> 11); }
 
 struct VerifyArgs {
   int B, K, V, NC;
@@ -90,7 +97,7 @@ struct VerifyArgs {
   const void* cache;
   int cache_bf16, vec_cache;
   long long cache_rs, cache_ss;
-  const float* draft_lse;  // [B*K] or the workspace copy recomputed from the cache
+  const float* draft_lse;  // [B*K], or null: then the statistics pass also reads the cache rows
   const int32_t* draft;
   const float* temp;
   const float* top_p;
@@ -98,21 +105,23 @@ struct VerifyArgs {
   const long long* anchor_pos;
   int32_t* out_tokens;
   int32_t* num_accepted;
-  StatPart* tpart;  // [B*(K+1)][NC]
-  StatPart* qpart;  // [B*K][NC] when draft_lse must be recomputed
-  float* qlse;      // [B*K] recomputed draft lse
-  TopP* topp;       // [B*(K+1)] or null
-  ReqState* req;    // [B]
-  ResPart* rpart;   // [B][NC]
+  unsigned long long* tpart;  // [B*(K+1)][NC] packed partials of the target rows
+  unsigned long long* qpart;  // [B*K][NC] packed partials of the cache rows (draft_lse null)
+  RowStat* rowstat;           // [B*(K+1)]
+  float* qlse;                // [B*K] draft log-normalisers (copied or combined)
+  TopP* topp;                 // [B*(K+1)] or null
+  ReqState* req;              // [B]
+  unsigned long long* rkey;   // [B][2] residual / p winner keys of the final draw
+  unsigned* cnt;              // [B] arrival counters (zero between calls)
   uint32_t* status;
   int vec_target;
+  int decide;                 // the statistics pass also takes the accept decision (no top-p)
 };
 
-hipError_t launch_target_stats(const VerifyArgs& a, hipStream_t st);
-hipError_t launch_draft_stats(const VerifyArgs& a, hipStream_t st);
+hipError_t launch_verify_stats(const VerifyArgs& a, hipStream_t st);
 hipError_t launch_top_p(const VerifyArgs& a, hipStream_t st);
+hipError_t launch_decide(const VerifyArgs& a, hipStream_t st);
 hipError_t launch_residual(const VerifyArgs& a, hipStream_t st);
-hipError_t launch_verify_finalize(const VerifyArgs& a, hipStream_t st);
 
 // ----------------------------------------------------------------- debug --
 hipError_t launch_debug_noise(int n, const int32_t* cols, long long seed, long long pos, uint32_t salt,

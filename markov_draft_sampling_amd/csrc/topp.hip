@@ -106,15 +106,7 @@ __global__ __launch_bounds__(kTp) void top_p_kernel(VerifyArgs a) {
     return;
   }
   const int tid = threadIdx.x;
-  if (tid < 64) {
-    float m = -INFINITY, s = 0.0f;
-    for (int i = tid; i < a.NC; i += 64) {
-      const StatPart q = a.tpart[(size_t)row * a.NC + i];
-      lse_merge(m, s, q.m, q.s);
-    }
-    wave_lse_merge(m, s);
-    if (tid == 0) s_M = m;
-  }
+  if (tid == 0) s_M = a.rowstat[row].m;
   __syncthreads();
   if (s_M == -INFINITY) {  // no finite logit: only the first column (the row maximum by rule) is kept
     if (tid == 0) *out = TopP{ord_f32(-INFINITY), 0, -INFINITY, 1};

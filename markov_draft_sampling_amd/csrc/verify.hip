@@ -2,21 +2,30 @@
 //
 // PR #65007 (Part 2) describes the stock rejection sampler as per-block
 // kernels over 8192-column statistics blocks whose partials per-request
-// kernels combine, plus residual-mass and resample kernels. Here:
-//   target_stats_kernel  one work-group per (target row, 8192-column block):
-//                        (max, sum exp) of logit / T for sampled requests,
-//                        the winner key of the raw logits for greedy ones
-//                        (PR #63554, Notes: greedy verification compares with
-//                        the target argmax and never reads the draft cache);
-//   draft_stats_kernel   the same (max, sum exp) over the draft cache rows,
-//                        only when the draft loop did not provide them;
-//   residual_kernel      one work-group per (request, block): every group
-//                        first combines its request's partials and runs the
-//                        K accept tests p(x) >= u * q(x) itself (a few scalar
-//                        loads), then draws over its block with Gumbel-max
-//                        from the normalised residual max(0, p - q) of the
-//                        first rejected row, or from p for the bonus token;
-//   verify_finalize_kernel  combines the per-block draws and writes tokens.
+// kernels combine, plus residual-mass and resample kernels. Here two
+// launches do the whole pass when there is no top-p:
+//   stats_kernel     one work-group per (row, 8192-column block) streams the
+//                    target rows (and the draft cache rows when the draft
+//                    loop gave no log-normalisers): (max, sum exp) of
+//                    logit / T for sampled requests, the winner key of the
+//                    raw logits for greedy ones (PR #63554, Notes: greedy
+//                    verification compares with the target argmax and never
+//                    reads the draft cache). The last work-group of a request
+//                    to finish combines its partials and runs the K accept
+//                    tests p(x) >= u * q(x);
+//   residual_kernel  one work-group per (request, block) draws over its block
+//                    with Gumbel-max from the normalised residual
+//                    max(0, p - q) of the first rejected row, or from p for
+//                    the bonus token; the last one of a request writes the
+//                    output tokens.
+// With top-p the statistics pass only combines rows; the top-p kernel and a
+// small decide_kernel (one work-group per request) sit in between.
+//
+// Cross-work-group hand-off inside a launch: partials and winner keys are
+// published with device-scope atomic read-modify-writes whose completion the
+// publishing thread waits for before it bumps the request's arrival counter;
+// the last arrival reads them back with read-modify-writes as well. Every
+// counter returns to zero before the call ends.
 #include "mds_device.h"
 #include "mds_internal.h"
 
@@ -25,145 +34,143 @@ namespace mds {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPerThread = kStatsChunk / kThreads;  // 32 columns
+constexpr int kPerThread = kStatsChunk / kThreads;  // 32 columns: c0 + 1024 i + 4 tid + e
+constexpr int kMaxK = 32;
 
 __device__ __forceinline__ float load_f32_or_bf16(const void* p, long long off, int bf16) {
   return bf16 ? bf16_bits_to_f32(((const uint16_t*)p)[off]) : ((const float*)p)[off];
 }
 
-// block-wide merge of (m, s) and of a winner key over 4 waves
-__device__ __forceinline__ void block_merge(float& m, float& s, unsigned long long& key, float* sm, float* ss,
-                                            unsigned long long* sk) {
+// Wait until every vector memory operation of this thread has completed
+// (returning atomics included); the "memory" clobber keeps the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ unsigned long long pack_ms(float m, float s) {
+  return ((unsigned long long)__float_as_uint(s) << 32) | __float_as_uint(m);
+}
+__device__ __forceinline__ float unpack_m(unsigned long long p) { return __uint_as_float((uint32_t)p); }
+__device__ __forceinline__ float unpack_s(unsigned long long p) { return __uint_as_float((uint32_t)(p >> 32)); }
+__device__ __forceinline__ unsigned long long rmw_read(unsigned long long* p) { return atomicAdd(p, 0ull); }
+
+// The 32 values of one 8192-column block that this thread owns. When the
+// whole block exists and vector access is allowed (a block-uniform test) all
+// eight loads are issued before any value is used.
+template <bool BF16>
+__device__ __forceinline__ void load_block(const void* rowp, int V, int c0, bool vec, float pad,
+                                           float (&v)[kPerThread]) {
+  const int tc = c0 + (int)threadIdx.x * 4;
+  if (vec && c0 + kStatsChunk <= V) {
+#pragma unroll
+    for (int i = 0; i < kPerThread / 4; ++i) {
+      if (BF16) {
+        const u32x2 w = __builtin_nontemporal_load((const u32x2*)((const uint16_t*)rowp + tc + i * 1024));
+        v[4 * i + 0] = bf16_bits_to_f32(w.x & 0xFFFFu);
+        v[4 * i + 1] = bf16_bits_to_f32(w.x >> 16);
+        v[4 * i + 2] = bf16_bits_to_f32(w.y & 0xFFFFu);
+        v[4 * i + 3] = bf16_bits_to_f32(w.y >> 16);
+      } else {
+        const f32x4 w = __builtin_nontemporal_load((const f32x4*)((const float*)rowp + tc + i * 1024));
+        v[4 * i + 0] = w.x;
+        v[4 * i + 1] = w.y;
+        v[4 * i + 2] = w.z;
+        v[4 * i + 3] = w.w;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kPerThread / 4; ++i) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = tc + i * 1024 + e;
+        v[4 * i + e] = c < V ? load_f32_or_bf16(rowp, c, BF16) : pad;
+      }
+    }
+  }
+}
+
+// (max, sum exp) of x = v / T over the thread's columns, NaN sum if one is NaN
+__device__ __forceinline__ void thread_stats(float (&v)[kPerThread], int c0, int V, float T, float invT, float& m,
+                                             float& s) {
+  const int tc = c0 + (int)threadIdx.x * 4;
+  m = -INFINITY;
+  s = 0.0f;
+  bool has_nan = false;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    const bool valid = tc + (j >> 2) * 1024 + (j & 3) < V;
+    const float x = valid ? div_t(v[j], T, invT) : -INFINITY;
+    has_nan |= x != x;
+    v[j] = (x == x) ? x : -INFINITY;
+    m = fmaxf(m, v[j]);
+  }
+  if (m != -INFINITY) {
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) s += fast_exp(v[j] - m);
+  }
+  if (has_nan) s = NAN;
+}
+
+// winner key of the raw values over the thread's columns
+__device__ __forceinline__ unsigned long long thread_key(const float (&v)[kPerThread], int c0, int V) {
+  const int tc = c0 + (int)threadIdx.x * 4;
+  float bv = -INFINITY;
+  int bi = -1;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    const int c = tc + (j >> 2) * 1024 + (j & 3);
+    if (c < V) win_update(bv, bi, v[j], c);
+  }
+  return bi >= 0 ? win_key(bv, (uint32_t)bi) : 0ull;
+}
+
+// block-wide merge over the 4 waves; the result is valid in thread 0
+__device__ __forceinline__ void block_merge_ms(float& m, float& s) {
+  __shared__ float sm[4], ss[4];
   wave_lse_merge(m, s);
-  key = wave_max_u64(key);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) {
     sm[wave] = m;
     ss[wave] = s;
-    sk[wave] = key;
   }
   __syncthreads();
-  m = sm[0];
-  s = ss[0];
-  key = sk[0];
-#pragma unroll
-  for (int w = 1; w < kThreads / 64; ++w) {
-    lse_merge(m, s, sm[w], ss[w]);
-    key = sk[w] > key ? sk[w] : key;
-  }
-}
-
-// (max, sum exp) of x = v / T and the raw winner key over one 8192-column block
-template <bool BF16>
-__device__ void row_block_stats(const void* rowp, int V, int c_begin, bool vec, float T, float invT, bool want_stats,
-                                bool want_key, StatPart* out) {
-  __shared__ float sm[4], ss[4];
-  __shared__ unsigned long long sk[4];
-  float vals[kPerThread];
-  int cols[kPerThread / 4];
-#pragma unroll
-  for (int i = 0; i < kPerThread / 4; ++i) {
-    const int c = c_begin + (i * kThreads + threadIdx.x) * 4;
-    cols[i] = c;
-    const int n = V - c >= 4 ? 4 : (V - c > 0 ? V - c : 0);
-    if (vec && n == 4) {
-      if (BF16) {
-        const u32x2 w = __builtin_nontemporal_load((const u32x2*)((const uint16_t*)rowp + c));
-        vals[4 * i + 0] = bf16_bits_to_f32(w.x & 0xFFFFu);
-        vals[4 * i + 1] = bf16_bits_to_f32(w.x >> 16);
-        vals[4 * i + 2] = bf16_bits_to_f32(w.y & 0xFFFFu);
-        vals[4 * i + 3] = bf16_bits_to_f32(w.y >> 16);
-      } else {
-        const f32x4 w = __builtin_nontemporal_load((const f32x4*)((const float*)rowp + c));
-        vals[4 * i + 0] = w.x;
-        vals[4 * i + 1] = w.y;
-        vals[4 * i + 2] = w.z;
-        vals[4 * i + 3] = w.w;
-      }
-    } else {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) vals[4 * i + t] = t < n ? load_f32_or_bf16(rowp, c + t, BF16) : -INFINITY;
-    }
-  }
-  float m = -INFINITY, s = 0.0f;
-  bool has_nan = false;
-  unsigned long long key = 0ull;
-  if (want_stats) {
-#pragma unroll
-    for (int j = 0; j < kPerThread; ++j) {
-      const bool valid = cols[j >> 2] + (j & 3) < V;
-      const float x = valid ? div_t(vals[j], T, invT) : -INFINITY;
-      has_nan |= valid && (x != x);
-      vals[j] = (x == x) ? x : -INFINITY;
-      m = fmaxf(m, vals[j]);
-    }
-    if (m != -INFINITY) {
-#pragma unroll
-      for (int j = 0; j < kPerThread; ++j) s += fast_exp(vals[j] - m);
-    }
-    if (has_nan) s = NAN;
-  }
-  if (want_key) {
-    float bv = -INFINITY;
-    int bi = -1;
-#pragma unroll
-    for (int i = 0; i < kPerThread / 4; ++i) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        if (cols[i] + t < V) win_update(bv, bi, vals[4 * i + t], cols[i] + t);
-    }
-    key = bi >= 0 ? win_key(bv, (uint32_t)bi) : 0ull;
-  }
-  block_merge(m, s, key, sm, ss, sk);
   if (threadIdx.x == 0) {
-    out->m = m;
-    out->s = s;
-    out->key = key;
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) lse_merge(m, s, sm[w], ss[w]);
   }
 }
 
-__global__ __launch_bounds__(kThreads) void target_stats_kernel(VerifyArgs a) {
-  const int chunk = blockIdx.x, row = blockIdx.y;
-  const int b = row / (a.K + 1);
-  const float T = a.temp[b];
-  const bool greedy = !(T > 0.0f);
-  const float* rowp = a.target + (long long)row * a.target_rs;
-  row_block_stats<false>(rowp, a.V, chunk * kStatsChunk, a.vec_target, greedy ? 1.0f : T, greedy ? 1.0f : 1.0f / T,
-                         !greedy, greedy, a.tpart + (size_t)row * a.NC + chunk);
-}
-
-__global__ __launch_bounds__(kThreads) void draft_stats_kernel(VerifyArgs a) {
-  const int chunk = blockIdx.x, row = blockIdx.y;  // row = b*K + k
-  const int b = row / a.K, k = row - b * a.K;
-  const float T = a.temp[b];
-  StatPart* out = a.qpart + (size_t)row * a.NC + chunk;
-  if (!(T > 0.0f)) {
-    if (threadIdx.x == 0) *out = StatPart{-INFINITY, 0.0f, 0ull};
-    return;
-  }
-  const long long off = (long long)b * a.cache_rs + (long long)k * a.cache_ss;
-  if (a.cache_bf16)
-    row_block_stats<true>((const uint16_t*)a.cache + off, a.V, chunk * kStatsChunk, a.vec_cache, T, 1.0f / T, true,
-                          false, out);
-  else
-    row_block_stats<false>((const float*)a.cache + off, a.V, chunk * kStatsChunk, a.vec_cache, T, 1.0f / T, true,
-                           false, out);
-}
-
-// combine NC partials of `parts` with one wave; returns (m, s) and key in lane 0..63
-__device__ __forceinline__ void combine_parts(const StatPart* parts, int NC, float& m, float& s,
-                                              unsigned long long& key) {
-  const int lane = threadIdx.x & 63;
-  m = -INFINITY;
-  s = 0.0f;
-  key = 0ull;
-  for (int i = lane; i < NC; i += 64) {
-    const StatPart p = parts[i];
-    lse_merge(m, s, p.m, p.s);
-    key = p.key > key ? p.key : key;
-  }
-  wave_lse_merge(m, s);
+__device__ __forceinline__ unsigned long long block_max_key(unsigned long long key) {
+  __shared__ unsigned long long sk[4];
   key = wave_max_u64(key);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) sk[wave] = key;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) key = sk[w] > key ? sk[w] : key;
+  }
+  return key;
+}
+
+// two keys at once (one LDS round); results valid in thread 0
+__device__ __forceinline__ void block_max_key2(unsigned long long& k0, unsigned long long& k1) {
+  __shared__ unsigned long long sk[2][4];
+  k0 = wave_max_u64(k0);
+  k1 = wave_max_u64(k1);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    sk[0][wave] = k0;
+    sk[1][wave] = k1;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) {
+      k0 = sk[0][w] > k0 ? sk[0][w] : k0;
+      k1 = sk[1][w] > k1 ? sk[1][w] : k1;
+    }
+  }
 }
 
 __device__ __forceinline__ bool kept(const TopP& tp, float t, int v) {
@@ -172,65 +179,105 @@ __device__ __forceinline__ bool kept(const TopP& tp, float t, int v) {
   return o > tp.tau || (o == tp.tau && v <= tp.cut);
 }
 
-constexpr int kMaxK = 32;
+// Per-request statistics staged in LDS for the decision.
+struct ReqLds {
+  float m[kMaxK + 1], lz[kMaxK + 1], lq[kMaxK], qm[kMaxK];
+  unsigned long long key[kMaxK + 1], qkey[kMaxK];
+  int acc[kMaxK];
+};
 
-__global__ __launch_bounds__(kThreads) void residual_kernel(VerifyArgs a) {
-  __shared__ float s_m[kMaxK + 1], s_lz[kMaxK + 1], s_lq[kMaxK];
-  __shared__ unsigned long long s_key[kMaxK + 1];
-  __shared__ int s_n, s_mode, s_acc[kMaxK];
-  __shared__ float sm[4], ss[4];
-  __shared__ unsigned long long sk[4];
-  const int chunk = blockIdx.x, b = blockIdx.y;
+constexpr int kStage = 1024;  // partials a combining wave stages in LDS at a time
+
+// Orders the LDS accesses of one wave around it (a wave's LDS operations
+// execute in issue order; this keeps the compiler from moving them).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// One wave combines nrows consecutive rows of NC packed partials starting at
+// p: the max of the words (keys) or their (max, sum exp) merge, in chunk
+// order. Partials are read with device-scope atomic loads, staged in LDS a
+// page at a time (all loads of a page in flight together), then lane j merges
+// row j of the page. Results go to om / os / okey [row].
+__device__ void wave_combine(const unsigned long long* p, int nrows, int NC, bool keys, unsigned long long* stage,
+                             float* om, float* os, unsigned long long* okey) {
+  const int lane = threadIdx.x & 63;
+  const int cpp = NC < kStage ? NC : kStage;  // chunks per page
+  const int rpp = kStage / cpp;               // rows per page, >= 1
+  for (int r0 = 0; r0 < nrows; r0 += rpp) {
+    const int nr = nrows - r0 < rpp ? nrows - r0 : rpp;
+    float m = -INFINITY, s = 0.0f;
+    unsigned long long key = 0ull;
+    for (int c0 = 0; c0 < NC; c0 += cpp) {
+      const int nc = NC - c0 < cpp ? NC - c0 : cpp;
+      const int n = nr * nc;
+      for (int t0 = 0; t0 < n; t0 += 64 * 16) {
+        unsigned long long w[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          int t = t0 + u * 64 + lane;
+          t = t < n ? t : n - 1;
+          const int rr = t / nc, cc = t - rr * nc;
+          w[u] = __hip_atomic_load(p + (size_t)(r0 + rr) * NC + c0 + cc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int t = t0 + u * 64 + lane;
+          if (t < n) stage[t] = w[u];
+        }
+      }
+      wave_lds_sync();
+      if (lane < nr) {
+        for (int cc = 0; cc < nc; ++cc) {
+          const unsigned long long x = stage[lane * nc + cc];
+          if (keys)
+            key = x > key ? x : key;
+          else
+            lse_merge(m, s, unpack_m(x), unpack_s(x));
+        }
+      }
+      wave_lds_sync();
+    }
+    if (lane < nr) {
+      om[r0 + lane] = m;
+      os[r0 + lane] = s;
+      okey[r0 + lane] = key;
+    }
+  }
+  wave_lds_sync();
+}
+
+// The K accept tests of request b (independent; the first failure ends the
+// run), then ReqState for the residual draw. Greedy requests are finished
+// here: the final token is the argmax of row n_acc. Run by one wave with L
+// filled.
+__device__ void decide(const VerifyArgs& a, int b, ReqLds& L) {
   const int K = a.K, V = a.V;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const float T = a.temp[b];
   const bool greedy = !(T > 0.0f);
   const float invT = greedy ? 1.0f : 1.0f / T;
-
-  // per-row statistics of this request
-  for (int j = wave; j <= K; j += 4) {
-    float m, s;
-    unsigned long long key;
-    combine_parts(a.tpart + (size_t)(b * (K + 1) + j) * a.NC, a.NC, m, s, key);
-    if (lane == 0) {
-      s_m[j] = m;
-      s_lz[j] = (a.topp && a.topp[b * (K + 1) + j].on) ? a.topp[b * (K + 1) + j].log_z : __logf(s);
-      s_key[j] = key;
-    }
-  }
-  if (!greedy) {
-    if (a.qpart) {
-      for (int k = wave; k < K; k += 4) {
-        float m, s;
-        unsigned long long key;
-        combine_parts(a.qpart + (size_t)(b * K + k) * a.NC, a.NC, m, s, key);
-        if (lane == 0) s_lq[k] = (s != s) ? NAN : m + __logf(s);
-      }
-    } else {
-      for (int k = threadIdx.x; k < K; k += kThreads) s_lq[k] = a.draft_lse[b * K + k];
-    }
-  }
-  __syncthreads();
-
-  // the K accept tests are independent; the first failing one ends the run
-  for (int k = threadIdx.x; k < K; k += kThreads) {
+  if (lane < K) {
+    const int k = lane;
     int x = a.draft[b * K + k];
     bool ok;
     if (greedy) {
-      ok = x == (int32_t)win_col(s_key[k]);
+      ok = x == (int32_t)win_col(L.key[k]);
     } else {
       if (x < 0 || x >= V) {
         set_status(a.status, kStatusBadDraft);
         x = 0;
       }
-      const long long rowoff = (long long)(b * (K + 1) + k) * a.target_rs;
-      const float tx = a.target[rowoff + x];
+      const int row = b * (K + 1) + k;
+      const float tx = a.target[(long long)row * a.target_rs + x];
       float logp = -INFINITY;
-      if (!a.topp || kept(a.topp[b * (K + 1) + k], tx, x)) logp = div_t(tx, T, invT) - s_m[k] - s_lz[k];
+      if (!a.topp || kept(a.topp[row], tx, x)) logp = div_t(tx, T, invT) - L.m[k] - L.lz[k];
       const float p = expf(logp);
       const long long coff = (long long)b * a.cache_rs + (long long)k * a.cache_ss + x;
       const float cx = load_f32_or_bf16(a.cache, coff, a.cache_bf16);
-      const float q = expf(div_t(cx, T, invT) - s_lq[k]);
+      const float q = expf(div_t(cx, T, invT) - L.lq[k]);
       const unsigned long long sd = (unsigned long long)a.seeds[b];
       const unsigned long long pk = (unsigned long long)(a.anchor_pos[b] + k);
       const Philox4 w = philox4x32_10(0u, (uint32_t)pk, (uint32_t)(pk >> 32), kSaltAccept, (uint32_t)sd,
@@ -238,143 +285,229 @@ __global__ __launch_bounds__(kThreads) void residual_kernel(VerifyArgs a) {
       const float u = uniform24(w.x0);
       ok = p >= u * q;  // a NaN q rejects
     }
-    s_acc[k] = ok;
+    L.acc[k] = ok;
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int n = 0;
-    while (n < K && s_acc[n]) ++n;
-    const int mode = greedy ? 2 : (n < K ? ((s_lq[n] != s_lq[n]) ? 3 : 1) : 0);
-    s_n = n;
-    s_mode = mode;
-    if (chunk == 0) a.req[b] = ReqState{n, n, mode, greedy ? (int)win_col(s_key[n]) : -1};
+  wave_lds_sync();
+  int n = 0;
+  while (n < K && L.acc[n]) ++n;
+  if (greedy && lane <= K) {
+    const int i = lane;
+    int v = -1;
+    if (i < n) {
+      v = a.draft[b * K + i];
+      if (v < 0 || v >= V) v = 0;
+    } else if (i == n) {
+      v = (int)win_col(L.key[n]);
+    }
+    a.out_tokens[(size_t)b * (K + 1) + i] = v;
   }
-  __syncthreads();
-  const int n = s_n, mode = s_mode;
-  if (mode == 2) return;
+  if (lane == 0) {
+    ReqState r;
+    r.n_acc = n;
+    r.mode = greedy ? 2 : (n < K ? ((L.lq[n] != L.lq[n]) ? 3 : 1) : 0);
+    r.M = L.m[n];
+    r.LZ = L.lz[n];
+    r.LQ = r.mode == 1 ? L.lq[n] : 0.0f;
+    r.pad = 0;
+    r.tp = a.topp ? a.topp[b * (K + 1) + n] : TopP{0u, 0, 0.0f, 0};
+    if (r.tp.on) r.LZ = r.tp.log_z;
+    a.req[b] = r;
+    a.rkey[2 * b] = 0ull;
+    a.rkey[2 * b + 1] = 0ull;
+    if (greedy) a.num_accepted[b] = n;
+  }
+}
 
-  // Gumbel-max over this block of row n: log residual, and log p as fallback / bonus
-  const int j = n;
-  const float M = s_m[j], LZ = s_lz[j];
-  const float LQ = mode == 1 ? s_lq[j] : 0.0f;
-  const TopP tp = a.topp ? a.topp[b * (K + 1) + j] : TopP{0u, 0, 0.0f, 0};
-  const float* trow = a.target + (long long)(b * (K + 1) + j) * a.target_rs;
-  const long long crow = (long long)b * a.cache_rs + (long long)j * a.cache_ss;
+// Run by wave 0 of the last work-group of request b: combine every partial of
+// the request, write the row statistics and, without top-p, decide. Resets
+// the request's counter.
+__device__ void combine_request(const VerifyArgs& a, int b, ReqLds& L, unsigned long long* stage) {
+  const int K = a.K, NC = a.NC;
+  const int lane = threadIdx.x & 63;
+  const bool greedy = !(a.temp[b] > 0.0f);
+  wave_combine(a.tpart + (size_t)b * (K + 1) * NC, K + 1, NC, greedy, stage, L.m, L.lz, L.key);
+  if (lane <= K) {
+    const float s = L.lz[lane];
+    const float lz = (s != s) ? NAN : __logf(s);
+    L.lz[lane] = lz;
+    a.rowstat[b * (K + 1) + lane] = RowStat{L.m[lane], lz, L.key[lane]};
+  }
+  if (a.qpart && !greedy) {
+    wave_combine(a.qpart + (size_t)b * K * NC, K, NC, false, stage, L.qm, L.lq, L.qkey);
+    if (lane < K) {
+      const float s = L.lq[lane];
+      const float lq = (s != s) ? NAN : L.qm[lane] + __logf(s);
+      L.lq[lane] = lq;
+      a.qlse[b * K + lane] = lq;
+    }
+  } else if (lane < K) {
+    const float lq = greedy ? 0.0f : a.draft_lse[b * K + lane];
+    L.lq[lane] = lq;
+    a.qlse[b * K + lane] = lq;
+  }
+  if (lane == 0) atomicExch(a.cnt + verify_counter_index(b), 0u);
+  wave_lds_sync();
+  if (a.decide) decide(a, b, L);
+}
+
+// Grid (NC, rows) with rows = B(K+1) target rows, then B*K cache rows when
+// draft_lse is null; rows are split over y and z (y at most 32768).
+__global__ __launch_bounds__(kThreads) void stats_kernel(VerifyArgs a) {
+  __shared__ ReqLds L;
+  __shared__ unsigned long long stage[kStage];
+  const int chunk = blockIdx.x;
+  const int row = (int)blockIdx.z * (int)gridDim.y + (int)blockIdx.y;
+  const int K = a.K, V = a.V, NC = a.NC;
+  const int n_t = a.B * (K + 1);
+  const int n_rows = n_t + (a.qpart ? a.B * K : 0);
+  if (row >= n_rows) return;
+  const bool is_target = row < n_t;
+  const int b = is_target ? row / (K + 1) : (row - n_t) / K;
+  const float T = a.temp[b];
+  const bool greedy = !(T > 0.0f);
+  const int c0 = chunk * kStatsChunk;
+  unsigned long long* slot = nullptr;
+  unsigned long long word = 0ull;
+  if (is_target) {
+    float v[kPerThread];
+    load_block<false>(a.target + (long long)row * a.target_rs, V, c0, a.vec_target != 0, 0.0f, v);
+    if (greedy) {
+      word = block_max_key(thread_key(v, c0, V));
+    } else {
+      float m, s;
+      thread_stats(v, c0, V, T, 1.0f / T, m, s);
+      block_merge_ms(m, s);
+      word = pack_ms(m, s);
+    }
+    slot = a.tpart + (size_t)row * NC + chunk;
+  } else if (!greedy) {
+    const int q = row - n_t, k = q - b * K;
+    const long long off = (long long)b * a.cache_rs + (long long)k * a.cache_ss;
+    float v[kPerThread];
+    if (a.cache_bf16)
+      load_block<true>((const uint16_t*)a.cache + off, V, c0, a.vec_cache != 0, 0.0f, v);
+    else
+      load_block<false>((const float*)a.cache + off, V, c0, a.vec_cache != 0, 0.0f, v);
+    float m, s;
+    thread_stats(v, c0, V, T, 1.0f / T, m, s);
+    block_merge_ms(m, s);
+    word = pack_ms(m, s);
+    slot = a.qpart + (size_t)q * NC + chunk;
+  }
+  // waves 1..3 are done; wave 0 publishes and, if it is the request's last
+  // arrival, combines
+  if (threadIdx.x >= 64) return;
+  int last = 0;
+  if (threadIdx.x == 0) {
+    if (slot) {
+      const unsigned long long prev = atomicExch(slot, word);
+      asm volatile("" ::"v"(prev));  // keep the returning form
+    }
+    wait_vmem();
+    const unsigned n_wg = (unsigned)NC * (unsigned)(K + 1 + (a.qpart ? K : 0));
+    last = atomicAdd(a.cnt + verify_counter_index(b), 1u) == n_wg - 1;
+  }
+  last = __shfl(last, 0);
+  if (!last) return;
+  combine_request(a, b, L, stage);
+}
+
+// With top-p: one wave per request after the top-p kernel.
+__global__ __launch_bounds__(64) void decide_kernel(VerifyArgs a) {
+  __shared__ ReqLds L;
+  const int b = blockIdx.x, K = a.K;
+  const int j = threadIdx.x;
+  if (j <= K) {
+    const RowStat rs = a.rowstat[b * (K + 1) + j];
+    const TopP tp = a.topp ? a.topp[b * (K + 1) + j] : TopP{0u, 0, 0.0f, 0};
+    L.m[j] = rs.m;
+    L.lz[j] = tp.on ? tp.log_z : rs.lz;
+    L.key[j] = rs.key;
+    if (j < K) L.lq[j] = a.qlse[b * K + j];
+  }
+  wave_lds_sync();
+  decide(a, b, L);
+}
+
+__global__ __launch_bounds__(kThreads) void residual_kernel(VerifyArgs a) {
+  const int chunk = blockIdx.x, b = blockIdx.y;
+  const ReqState rq = a.req[b];
+  if (rq.mode == 2) return;
+  const int K = a.K, V = a.V;
+  const float T = a.temp[b];
+  const float invT = 1.0f / T;
+  const int j = rq.n_acc, mode = rq.mode;
+  const float M = rq.M, LZ = rq.LZ, LQ = rq.LQ;
+  const TopP tp = rq.tp;
+  const int c0 = chunk * kStatsChunk;
+  const int tc = c0 + (int)threadIdx.x * 4;
+  float tv[kPerThread], cv[kPerThread];
+  load_block<false>(a.target + (long long)(b * (K + 1) + j) * a.target_rs, V, c0, a.vec_target != 0, 0.0f, tv);
+  if (mode == 1) {
+    const long long off = (long long)b * a.cache_rs + (long long)j * a.cache_ss;
+    if (a.cache_bf16)
+      load_block<true>((const uint16_t*)a.cache + off, V, c0, a.vec_cache != 0, 0.0f, cv);
+    else
+      load_block<false>((const float*)a.cache + off, V, c0, a.vec_cache != 0, 0.0f, cv);
+  }
   const unsigned long long sd = (unsigned long long)a.seeds[b];
   const unsigned long long pk = (unsigned long long)(a.anchor_pos[b] + j);
-  float bvr = -INFINITY, bvp = -INFINITY, sum_r = 0.0f;
+  float bvr = -INFINITY, bvp = -INFINITY;
   int bir = -1, bip = -1;
-  const int c_begin = chunk * kStatsChunk;
-#pragma unroll 2
+#pragma unroll
   for (int i = 0; i < kPerThread / 4; ++i) {
-    const int c = c_begin + (i * kThreads + threadIdx.x) * 4;
-    const int nv = V - c >= 4 ? 4 : (V - c > 0 ? V - c : 0);
-    if (nv == 0) continue;
-    float tv[4], cv[4];
-    if (a.vec_target && nv == 4) {
-      const f32x4 w = __builtin_nontemporal_load((const f32x4*)(trow + c));
-      tv[0] = w.x;
-      tv[1] = w.y;
-      tv[2] = w.z;
-      tv[3] = w.w;
-    } else {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) tv[t] = t < nv ? trow[c + t] : 0.0f;
-    }
-    if (mode == 1) {
-      if (a.vec_cache && nv == 4) {
-        if (a.cache_bf16) {
-          const u32x2 w = __builtin_nontemporal_load((const u32x2*)((const uint16_t*)a.cache + crow + c));
-          cv[0] = bf16_bits_to_f32(w.x & 0xFFFFu);
-          cv[1] = bf16_bits_to_f32(w.x >> 16);
-          cv[2] = bf16_bits_to_f32(w.y & 0xFFFFu);
-          cv[3] = bf16_bits_to_f32(w.y >> 16);
-        } else {
-          const f32x4 w = __builtin_nontemporal_load((const f32x4*)((const float*)a.cache + crow + c));
-          cv[0] = w.x;
-          cv[1] = w.y;
-          cv[2] = w.z;
-          cv[3] = w.w;
-        }
-      } else {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) cv[t] = t < nv ? load_f32_or_bf16(a.cache, crow + c + t, a.cache_bf16) : 0.0f;
-      }
-    }
+    const int c = tc + i * 1024;
+    if (c >= V) break;
     const Philox4 w = philox4x32_10((uint32_t)(c >> 2), (uint32_t)pk, (uint32_t)(pk >> 32), kSaltResample,
                                     (uint32_t)sd, (uint32_t)(sd >> 32));
     const uint32_t wd[4] = {w.x0, w.x1, w.x2, w.x3};
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      if (t >= nv) break;
-      const float g = gumbel_from_word(wd[t]);
-      const float logp = kept(tp, tv[t], c + t) ? div_t(tv[t], T, invT) - M - LZ : -INFINITY;
-      win_update(bvp, bip, logp + g, c + t);
-      if (mode == 1) {
-        const float pv = __expf(logp);
-        const float qv = __expf(div_t(cv[t], T, invT) - LQ);
-        const float rv = pv - qv;
-        const float sr = rv > 0.0f ? __logf(rv) + g : -INFINITY;
-        sum_r += rv > 0.0f ? rv : 0.0f;
-        win_update(bvr, bir, sr, c + t);
+    for (int e = 0; e < 4; ++e) {
+      if (c + e < V) {
+        const float g = gumbel_from_word(wd[e]);
+        const float t = tv[4 * i + e];
+        const float logp = kept(tp, t, c + e) ? div_t(t, T, invT) - M - LZ : -INFINITY;
+        win_update(bvp, bip, logp + g, c + e);
+        if (mode == 1) {
+          const float rv = __expf(logp) - __expf(div_t(cv[4 * i + e], T, invT) - LQ);
+          // only a positive residual is a candidate; its score is finite
+          const float sr = fmaxf(__logf(rv), -0x1.fffffep+127f) + g;
+          const bool take = rv > 0.0f && (sr > bvr || bir < 0);
+          bvr = take ? sr : bvr;
+          bir = take ? c + e : bir;
+        }
       }
     }
   }
   unsigned long long kr = bir >= 0 ? win_key(bvr, (uint32_t)bir) : 0ull;
   unsigned long long kp = bip >= 0 ? win_key(bvp, (uint32_t)bip) : 0ull;
-  kr = wave_max_u64(kr);
-  kp = wave_max_u64(kp);
-  sum_r = wave_sum_f32(sum_r);
-  if (lane == 0) {
-    sk[wave] = kr;
-    sm[wave] = sum_r;
-  }
-  __shared__ unsigned long long skp[4];
-  if (lane == 0) skp[wave] = kp;
-  __syncthreads();
+  block_max_key2(kr, kp);
   if (threadIdx.x == 0) {
-    ResPart out{0ull, 0ull, 0.0f, 0.0f};
-    for (int wv = 0; wv < 4; ++wv) {
-      out.key_r = sk[wv] > out.key_r ? sk[wv] : out.key_r;
-      out.key_p = skp[wv] > out.key_p ? skp[wv] : out.key_p;
-      out.sum_r += sm[wv];
+    unsigned long long* rk = a.rkey + 2 * b;
+    const unsigned long long p0 = atomicMax(rk, kr);
+    const unsigned long long p1 = atomicMax(rk + 1, kp);
+    asm volatile("" ::"v"(p0), "v"(p1));  // keep the returning forms
+    wait_vmem();
+    unsigned* cnt = a.cnt + verify_counter_index(b);
+    if (atomicAdd(cnt, 1u) == (unsigned)a.NC - 1u) {
+      // every block of the request has published: read and clear the keys
+      const unsigned long long KR = atomicExch(rk, 0ull);
+      const unsigned long long KP = atomicExch(rk + 1, 0ull);
+      atomicExch(cnt, 0u);
+      const int token = (int)win_col((mode == 1 && KR != 0ull) ? KR : KP);
+      for (int i = 0; i <= K; ++i) {
+        int v = -1;
+        if (i < j) {
+          v = a.draft[b * K + i];
+          if (v < 0 || v >= V) v = 0;
+        } else if (i == j) {
+          v = token;
+        }
+        a.out_tokens[(size_t)b * (K + 1) + i] = v;
+      }
+      a.num_accepted[b] = j;
     }
-    a.rpart[(size_t)b * a.NC + chunk] = out;
   }
-}
-
-__global__ __launch_bounds__(kThreads) void verify_finalize_kernel(VerifyArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (b >= a.B) return;
-  const ReqState rq = a.req[b];
-  int token = rq.token;
-  if (rq.mode != 2) {
-    unsigned long long kr = 0ull, kp = 0ull;
-    float sr = 0.0f;
-    for (int i = lane; i < a.NC; i += 64) {
-      const ResPart p = a.rpart[(size_t)b * a.NC + i];
-      kr = p.key_r > kr ? p.key_r : kr;
-      kp = p.key_p > kp ? p.key_p : kp;
-      sr += p.sum_r;
-    }
-    kr = wave_max_u64(kr);
-    kp = wave_max_u64(kp);
-    sr = wave_sum_f32(sr);
-    token = (int)win_col((rq.mode == 1 && sr > 0.0f) ? kr : kp);
-  }
-  const int K = a.K;
-  for (int i = lane; i <= K; i += 64) {
-    int v = -1;
-    if (i < rq.n_acc) {
-      v = a.draft[b * K + i];
-      if (v < 0 || v >= a.V) v = 0;
-    } else if (i == rq.n_acc) {
-      v = token;
-    }
-    a.out_tokens[(size_t)b * (K + 1) + i] = v;
-  }
-  if (lane == 0) a.num_accepted[b] = rq.n_acc;
 }
 
 __global__ void debug_noise_kernel(int n, const int32_t* cols, long long seed, long long pos, uint32_t salt,
@@ -398,23 +531,21 @@ __global__ void debug_gumbel_kernel(int n, const uint32_t* words, float* g) {
 
 }  // namespace
 
-hipError_t launch_target_stats(const VerifyArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(target_stats_kernel, dim3(a.NC, a.B * (a.K + 1)), dim3(kThreads), 0, st, a);
+hipError_t launch_verify_stats(const VerifyArgs& a, hipStream_t st) {
+  const int rows = a.B * (a.K + 1) + (a.qpart ? a.B * a.K : 0);
+  const int gy = rows < 32768 ? rows : 32768;
+  const int gz = (rows + gy - 1) / gy;
+  hipLaunchKernelGGL(stats_kernel, dim3(a.NC, gy, gz), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_draft_stats(const VerifyArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(draft_stats_kernel, dim3(a.NC, a.B * a.K), dim3(kThreads), 0, st, a);
+hipError_t launch_decide(const VerifyArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(decide_kernel, dim3(a.B), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_residual(const VerifyArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(residual_kernel, dim3(a.NC, a.B), dim3(kThreads), 0, st, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_verify_finalize(const VerifyArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(verify_finalize_kernel, dim3((a.B + 3) / 4), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
