@@ -190,8 +190,8 @@ def main():
         traffic = recorded_traffic("draft_resident_kernel_hbm_traffic_V200064_B32.md",
                                    ("draft_resident.hip", "mds_device.h", "mds_internal.h"))
     else:
-        traffic = recorded_traffic("draft_step_kernel_hbm_traffic_V200064_B32.md",
-                                   ("draft.hip", "mds_device.h", "mds_internal.h"))
+        traffic = recorded_traffic("draft_wave_kernel_hbm_traffic_V200064_B32.md",
+                                   ("draft_wave.hip", "mds_device.h", "mds_internal.h"))
     if B != 32:
         traffic = None
     status = mds.workspace_status(ws_d) | mds.workspace_status(ws_v)
@@ -215,7 +215,7 @@ def main():
         "hbm": {"algorithmic_bytes_per_step": draft_b + verify_b, "achieved_GBps": step_gbps,
                 "peak_GBps": HBM_PEAK_GBPS, "frac": step_gbps / HBM_PEAK_GBPS},
         "roofline": {"kernel": ("draft_resident_kernel (all K Markov steps, w2 held on chip)" if n_launch == 1 else
-                                "draft_step_kernel (one Markov step, w2 streamed)"),
+                                "draft_wave_kernel (one Markov step, w2 streamed)"),
                      "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "bytes_per_launch": bytes_per_launch, "avg_launch_us": kern_avg_ms * 1e3,

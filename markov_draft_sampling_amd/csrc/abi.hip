@@ -188,7 +188,8 @@ int draft_impl(int B, int K, int V, int r, const void* base, int base_dtype, int
   const bool resident = choice != 1 && cus <= mds::kDraftMaxSlabs &&
                         mds::draft_resident_plan(V, r, cus, (size_t)lds_max, &n_lds, &res_lds) == hipSuccess;
   if (choice == 2 && !resident) return fail(MDS_ERR_UNSUPPORTED, "w2 does not fit on chip for the resident kernel");
-  a.G = resident ? cus : mds::draft_slabs(V, cus);
+  const bool wave_kernel = !resident && r <= 256;
+  a.G = resident ? cus : (wave_kernel ? mds::draft_wave_slabs(V, cus) : mds::draft_slabs(V, cus));
   a.n_lds_tiles = n_lds;
   if ((e = mds::launch_draft_init(a.keys, K * B, a.bar, K + 1, st)) != hipSuccess) return hip_fail(e, "draft init launch");
   if (ev_begin && (e = hipEventRecord((hipEvent_t)ev_begin, st)) != hipSuccess) return hip_fail(e, "event record");
@@ -197,7 +198,8 @@ int draft_impl(int B, int K, int V, int r, const void* base, int base_dtype, int
   } else {
     for (int k = 0; k < K; ++k) {
       a.k = k;
-      if ((e = mds::launch_draft_step(a, st)) != hipSuccess) return hip_fail(e, "draft step launch");
+      e = wave_kernel ? mds::launch_draft_wave(a, st) : mds::launch_draft_step(a, st);
+      if (e != hipSuccess) return hip_fail(e, "draft step launch");
     }
   }
   if (ev_end && (e = hipEventRecord((hipEvent_t)ev_end, st)) != hipSuccess) return hip_fail(e, "event record");
@@ -216,6 +218,18 @@ int draft_slabs(int V, int cus) {
   const int nMT = (V + 15) / 16;
   int G = (nMT + kDraftMinTilesPerSlab - 1) / kDraftMinTilesPerSlab;
   const int cap = cus > 0 ? 2 * cus : kDraftMaxSlabs;
+  if (G > cap) G = cap;
+  if (G > kDraftMaxSlabs) G = kDraftMaxSlabs;
+  if (G > 64) G &= ~7;
+  return G < 1 ? 1 : G;
+}
+
+// Wave-independent kernel: one work-group per CU (measured best against two
+// per CU for the V = 200064, B = 32 step), at least 8 tiles per slab.
+int draft_wave_slabs(int V, int cus) {
+  const int nMT = (V + 15) / 16;
+  int G = (nMT + kDraftMinTilesPerSlab - 1) / kDraftMinTilesPerSlab;
+  const int cap = cus > 0 ? cus : kDraftMaxSlabs;
   if (G > cap) G = cap;
   if (G > kDraftMaxSlabs) G = kDraftMaxSlabs;
   if (G > 64) G &= ~7;

@@ -146,29 +146,6 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftStepArgs a) {
   }
   const int b0 = bt * NB;
 
-  // previous token of every request of the tile
-  for (int i = tid; i < NB; i += 256) {
-    const int b = b0 + i;
-    int prev = 0;
-    if (b < a.B) {
-      long long t = (k == 0) ? (long long)a.anchor[b] : (long long)win_col(a.keys[(size_t)(k - 1) * a.B + b]);
-      if (t < 0 || t >= V) {
-        set_status(a.status, kStatusBadAnchor);
-        t = 0;
-      }
-      prev = (int)t;
-    }
-    s_prev[i] = prev;
-  }
-  __syncthreads();
-  // Markov embeddings w1[prev] -> LDS (zero rows past the batch)
-  for (int i = tid; i < NB * cpr; i += 256) {
-    const int row = i / cpr, ch = i - row * cpr;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (b0 + row < a.B) v = *(const u32x4*)(a.w1 + (size_t)s_prev[row] * r + ch * 8);
-    *(u32x4*)(s_e + row * rs + ch * 8) = v;
-  }
-
   // this work-group's columns: 16-column tiles [mt_begin, mt_end)
   const int mt_begin = (int)(((long long)g * a.nMT) / a.G);
   const int mt_end = (int)(((long long)(g + 1) * a.nMT) / a.G);
@@ -215,6 +192,10 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftStepArgs a) {
   // chunk loaders (w2 rows into registers, base into registers)
   u32x4 wreg[WLMAX];
   float bz[EPT][4], bzn[EPT][4];
+  // Rows past V are read from row 0 instead: they only feed bias columns
+  // past V (row m of the product depends on w2 row m alone), which the
+  // epilogue never uses. No select on the loaded data, so the loads of the
+  // next chunk stay in flight while this one is computed.
   auto load_w2 = [&](int c0) {
 #pragma unroll
     for (int i = 0; i < WLMAX; ++i) {
@@ -223,9 +204,7 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftStepArgs a) {
         const int row = q / cpr;
         const int v = c0 + row;
         const uint16_t* p = a.w2 + (size_t)(v < V ? v : 0) * r + (q - row * cpr) * 8;
-        u32x4 t = *(const u32x4*)p;
-        if (v >= V) t = u32x4{0u, 0u, 0u, 0u};
-        wreg[i] = t;
+        wreg[i] = *(const u32x4*)p;
       }
     }
   };
@@ -240,6 +219,19 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftStepArgs a) {
     }
   };
   auto load_base = [&](int c0, float (&dst)[EPT][4]) {
+    if (!a.base_bf16 && a.vec_base && c0 + kCW <= c_end) {
+      // whole chunk inside the slab (a block-uniform test): unconditional
+      // vector loads (rows past the batch read request 0 and are never used)
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        const f32x4 w = *(const f32x4*)((const float*)a.base + rbase[e] + c0 + ecol[e]);
+        dst[e][0] = w.x;
+        dst[e][1] = w.y;
+        dst[e][2] = w.z;
+        dst[e][3] = w.w;
+      }
+      return;
+    }
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
       const int c = c0 + ecol[e];
@@ -253,11 +245,36 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftStepArgs a) {
     }
   };
 
+  // the first chunk's loads go out before the previous tokens and the
+  // embedding gather, whose latency they then overlap
   if (nchunks > 0) {
     load_w2(c_begin);
     load_base(c_begin, bz);
-    store_w2();
   }
+  // previous token of every request of the tile
+  for (int i = tid; i < NB; i += 256) {
+    const int b = b0 + i;
+    int prev = 0;
+    if (b < a.B) {
+      long long t = (k == 0) ? (long long)a.anchor[b] : (long long)win_col(a.keys[(size_t)(k - 1) * a.B + b]);
+      if (t < 0 || t >= V) {
+        set_status(a.status, kStatusBadAnchor);
+        t = 0;
+      }
+      prev = (int)t;
+    }
+    s_prev[i] = prev;
+  }
+  __syncthreads();
+  // Markov embeddings w1[prev] -> LDS (zero rows past the batch)
+  for (int i = tid; i < NB * cpr; i += 256) {
+    const int row = i / cpr, ch = i - row * cpr;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (b0 + row < a.B) v = *(const u32x4*)(a.w1 + (size_t)s_prev[row] * r + ch * 8);
+    *(u32x4*)(s_e + row * rs + ch * 8) = v;
+  }
+
+  if (nchunks > 0) store_w2();
   __syncthreads();
 
   const int lrow = lane & 15, lgrp = lane >> 4;

@@ -1,0 +1,409 @@
+// Markov draft step, wave-independent streaming variant (gfx950, rank <= 256).
+//
+// The same fused step as draft_step_kernel (one step of the sequential loop of
+// the DSparkSpeculator API page: Markov embedding of the previous token ->
+// Markov bias -> biased logits -> Gumbel-max sample, plus the draft-logits
+// cache and its (max, sum exp) for q), laid out so that the four waves of a
+// work-group never wait for each other inside the column loop:
+//   * wave w of slab g walks the 16-column tiles mt_begin + w, + 4, + 8, ...;
+//   * the 16 w2 rows of a tile are loaded straight into the MFMA A operand
+//     (v_mfma_f32_16x16x32_bf16, lane l: row l % 16, rank elements
+//     8 (l / 16) + 32 s of slice s), and the next tile's rows and base logits
+//     are in flight while the current tile is computed;
+//   * the embeddings of the batch tile (the B operand) sit in LDS for the
+//     whole launch;
+//   * the epilogue runs in the accumulator layout: lane l owns request
+//     16 nt + l % 16 and the 4 consecutive columns 4 (l / 16) .. + 3 of the
+//     tile, so base loads and cache stores are 16-byte vector accesses.
+// Winners and q statistics are merged across the 4 lanes of a request row,
+// then across the waves in LDS, then across work-groups with one 64-bit
+// atomic max per request (PR #65007, Part 1, step 4: the first-max rule
+// composes over any column partition).
+#include "mds_device.h"
+#include "mds_internal.h"
+
+#include <type_traits>
+
+namespace mds {
+
+namespace {
+
+constexpr int kRKMax = 8;  // rank slices of 32 (r <= 256)
+
+template <int NB, bool BBF16, bool CBF16>
+__global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
+  constexpr int NT = NB / 16;
+  const int r = a.r, V = a.V, k = a.k;
+  const int RK = r >> 5;
+  const int rs = r + 8;  // LDS row stride of the embeddings (bf16 elements)
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint16_t* s_e = (uint16_t*)smem;                                   // [NB][rs]
+  int* s_prev = (int*)(s_e + NB * rs);                               // [NB]
+  unsigned long long* s_key = (unsigned long long*)(s_prev + NB);    // [4][NB]
+  float* s_qm = (float*)(s_key + 4 * NB);                            // [4][NB]
+  float* s_qs = s_qm + 4 * NB;                                       // [4][NB]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  // Work-groups are dealt round-robin to the 8 XCDs by linear id; when the
+  // slab count is a multiple of 8 the batch tiles of one slab share an XCD.
+  int g, bt;
+  {
+    const int id = blockIdx.x;
+    if ((a.G & 7) == 0) {
+      const int xcd = id & 7, local = id >> 3;
+      g = (local / a.BT) * 8 + xcd;
+      bt = local - (local / a.BT) * a.BT;
+    } else {
+      g = id % a.G;
+      bt = id / a.G;
+    }
+  }
+  const int b0 = bt * NB;
+  const int mt_begin = (int)(((long long)g * a.nMT) / a.G);
+  const int mt_end = (int)(((long long)(g + 1) * a.nMT) / a.G);
+
+  // the requests this lane serves: 16 nt + lr of the batch tile
+  bool valid[NT];
+  float Tv[NT], invT[NT];
+  uint32_t sk0[NT], sk1[NT], pk0[NT], pk1[NT];
+  long long rbase[NT], rcache[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int b = b0 + nt * 16 + lr;
+    valid[nt] = b < a.B;
+    const int bb = valid[nt] ? b : a.B - 1;
+    Tv[nt] = a.temp[bb];
+    invT[nt] = Tv[nt] > 0.0f ? 1.0f / Tv[nt] : 0.0f;
+    const unsigned long long sd = (unsigned long long)a.seeds[bb];
+    const unsigned long long pk = (unsigned long long)(a.anchor_pos[bb] + k);
+    sk0[nt] = (uint32_t)sd;
+    sk1[nt] = (uint32_t)(sd >> 32);
+    pk0[nt] = (uint32_t)pk;
+    pk1[nt] = (uint32_t)(pk >> 32);
+    rbase[nt] = (long long)bb * a.base_rs + (long long)k * a.base_ss;
+    rcache[nt] = (long long)bb * a.cache_rs + (long long)k * a.cache_ss;
+  }
+
+  // Tile loaders. w2 rows past V are read from row V - 1: they only feed
+  // bias columns past V, which the epilogue never uses. No select touches
+  // the loaded data, so the next tile's loads stay in flight.
+  auto load_a = [&](int t, u32x4 (&A)[kRKMax]) {
+    const int v = t * 16 + lr;
+    const uint16_t* p = a.w2 + (size_t)(v < V ? v : V - 1) * r + lg * 8;
+#pragma unroll
+    for (int s = 0; s < kRKMax; ++s)
+      if (s < RK) A[s] = *(const u32x4*)(p + s * 32);
+  };
+  auto load_base = [&](int t, float (&bz)[NT][4]) {
+    const int c = t * 16 + lg * 4;
+    if (a.vec_base && t * 16 + 16 <= V) {  // whole tile inside V: a wave-uniform test
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        if (BBF16) {
+          const u32x2 w = *(const u32x2*)((const uint16_t*)a.base + rbase[nt] + c);
+          bz[nt][0] = bf16_bits_to_f32(w.x & 0xFFFFu);
+          bz[nt][1] = bf16_bits_to_f32(w.x >> 16);
+          bz[nt][2] = bf16_bits_to_f32(w.y & 0xFFFFu);
+          bz[nt][3] = bf16_bits_to_f32(w.y >> 16);
+        } else {
+          const f32x4 w = *(const f32x4*)((const float*)a.base + rbase[nt] + c);
+          bz[nt][0] = w.x;
+          bz[nt][1] = w.y;
+          bz[nt][2] = w.z;
+          bz[nt][3] = w.w;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const long long off = rbase[nt] + c + i;
+          bz[nt][i] = c + i < V ? (BBF16 ? bf16_bits_to_f32(((const uint16_t*)a.base)[off])
+                                         : ((const float*)a.base)[off])
+                                : 0.0f;
+        }
+    }
+  };
+
+  // the first tile's loads go out before the previous tokens and the
+  // embedding gather, whose latency they then overlap
+  const int t_first = mt_begin + wave;
+  u32x4 A[kRKMax], An[kRKMax];
+  float bz[NT][4], bzn[NT][4];
+  if (t_first < mt_end) {
+    load_a(t_first, A);
+    load_base(t_first, bz);
+  }
+
+  // previous token of every request of the tile
+  const int cpr = r >> 3;  // 16-byte chunks per embedding row
+  for (int i = tid; i < NB; i += 256) {
+    const int b = b0 + i;
+    int prev = 0;
+    if (b < a.B) {
+      long long tk = (k == 0) ? (long long)a.anchor[b] : (long long)win_col(a.keys[(size_t)(k - 1) * a.B + b]);
+      if (tk < 0 || tk >= V) {
+        set_status(a.status, kStatusBadAnchor);
+        tk = 0;
+      }
+      prev = (int)tk;
+    }
+    s_prev[i] = prev;
+  }
+  __syncthreads();
+  // Markov embeddings w1[prev] -> LDS (zero rows past the batch)
+  for (int i = tid; i < NB * cpr; i += 256) {
+    const int row = i / cpr, ch = i - row * cpr;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (b0 + row < a.B) v = *(const u32x4*)(a.w1 + (size_t)s_prev[row] * r + ch * 8);
+    *(u32x4*)(s_e + row * rs + ch * 8) = v;
+  }
+  __syncthreads();
+
+  // Running winner and q statistics per served request. The winner starts
+  // at the lane's first column (value -inf), so a later column replaces it
+  // only when strictly larger or the first NaN: the first-max rule.
+  const int c_first = t_first * 16 + lg * 4;
+  float bv[NT], qm[NT], qs[NT];
+  int bi[NT];
+  bool qnan[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    bv[nt] = -INFINITY;
+    bi[nt] = (t_first < mt_end && c_first < V) ? c_first : -1;
+    qm[nt] = -INFINITY;
+    qs[nt] = 0.0f;
+    qnan[nt] = false;
+  }
+  // Fast epilogue for full tiles when every request of the batch tile exists
+  // and samples (T > 0), with vector cache stores; T == 1 skips the division.
+  bool all_sampled = true, all_t1 = true;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    all_sampled &= Tv[nt] > 0.0f;
+    all_t1 &= Tv[nt] == 1.0f;
+  }
+  const bool fast_req = b0 + NB <= a.B && a.vec_cache && __all(all_sampled);
+  const bool t1 = __all(all_t1);
+
+  for (int t = t_first; t < mt_end; t += 4) {
+    const bool more = t + 4 < mt_end;
+    if (more) {
+      load_a(t + 4, An);
+      load_base(t + 4, bzn);
+    }
+    // bias of this tile: D[column][request] for the NT request tiles
+    floatx4 acc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < kRKMax; ++s) {
+      if (s < RK) {
+        const bf16x8 afr = __builtin_bit_cast(bf16x8, A[s]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const bf16x8 bfr = *(const bf16x8*)(s_e + (nt * 16 + lr) * rs + s * 32 + lg * 8);
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr, acc[nt], 0, 0, 0);
+        }
+      }
+    }
+    // epilogue: lane holds columns c .. c+3 of request 16 nt + lr
+    const int c = t * 16 + lg * 4;
+    // Straight-line form: no per-element branches. A NaN among the q values
+    // is carried by the sum itself (NaN stays NaN through every later merge).
+    auto epi_fast = [&](auto t1_tag) {
+      constexpr bool T1 = decltype(t1_tag)::value;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        float z[4], cv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[i] = bz[nt][i] + acc[nt][i];
+        if (CBF16) {
+          uint32_t h[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            h[i] = f32_to_bf16_bits(z[i]);
+            cv[i] = bf16_bits_to_f32(h[i]);
+          }
+          u32x2 w;
+          w.x = h[0] | (h[1] << 16);
+          w.y = h[2] | (h[3] << 16);
+          *(u32x2*)((uint16_t*)a.cache + rcache[nt] + c) = w;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) cv[i] = z[i];
+          *(f32x4*)((float*)a.cache + rcache[nt] + c) = f32x4{z[0], z[1], z[2], z[3]};
+        }
+        const Philox4 w = philox4x32_10((uint32_t)(c >> 2), pk0[nt], pk1[nt], kSaltDraft, sk0[nt], sk1[nt]);
+        const uint32_t wd[4] = {w.x0, w.x1, w.x2, w.x3};
+        float y[4], x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          y[i] = T1 ? z[i] : div_t(z[i], Tv[nt], invT[nt]);
+          x[i] = CBF16 ? (T1 ? cv[i] : div_t(cv[i], Tv[nt], invT[nt])) : y[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float sv = y[i] + gumbel_from_word(wd[i]);
+          const bool take = (sv > bv[nt]) || ((sv != sv) && (bv[nt] == bv[nt]));
+          bv[nt] = take ? sv : bv[nt];
+          bi[nt] = take ? c + i : bi[nt];
+        }
+        const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));  // NaN-ignoring max
+        const float mn = fmaxf(qm[nt], mx);
+        const float sub = mn == -INFINITY ? 0.0f : mn;
+        float s_acc = qs[nt] * fast_exp(qm[nt] - sub);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s_acc += fast_exp(x[i] - sub);
+        qs[nt] = s_acc;
+        qm[nt] = mn;
+      }
+    };
+    if (fast_req && t * 16 + 16 <= V) {
+      if (t1)
+        epi_fast(std::integral_constant<bool, true>());
+      else
+        epi_fast(std::integral_constant<bool, false>());
+    } else {
+    const int n = V - c >= 4 ? 4 : (V - c > 0 ? V - c : 0);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      if (!valid[nt] || n == 0) continue;
+      float z[4], cv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[i] = bz[nt][i] + acc[nt][i];
+      if (CBF16) {
+        uint32_t h[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          h[i] = f32_to_bf16_bits(z[i]);
+          cv[i] = bf16_bits_to_f32(h[i]);
+        }
+        uint16_t* q = (uint16_t*)a.cache + rcache[nt] + c;
+        if (a.vec_cache && n == 4) {
+          u32x2 w;
+          w.x = h[0] | (h[1] << 16);
+          w.y = h[2] | (h[3] << 16);
+          *(u32x2*)q = w;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (i < n) q[i] = (uint16_t)h[i];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cv[i] = z[i];
+        float* q = (float*)a.cache + rcache[nt] + c;
+        if (a.vec_cache && n == 4) {
+          *(f32x4*)q = f32x4{z[0], z[1], z[2], z[3]};
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (i < n) q[i] = z[i];
+        }
+      }
+      if (Tv[nt] > 0.0f) {
+        const Philox4 w = philox4x32_10((uint32_t)(c >> 2), pk0[nt], pk1[nt], kSaltDraft, sk0[nt], sk1[nt]);
+        const uint32_t wd[4] = {w.x0, w.x1, w.x2, w.x3};
+        float x[4];
+        float xm = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float sv = div_t(z[i], Tv[nt], invT[nt]) + gumbel_from_word(wd[i]);
+          if (i < n) win_update(bv[nt], bi[nt], sv, c + i);
+          const float xv = div_t(cv[i], Tv[nt], invT[nt]);
+          qnan[nt] |= (i < n) && (xv != xv);
+          x[i] = (i < n && xv == xv) ? xv : -INFINITY;
+          xm = fmaxf(xm, x[i]);
+        }
+        const float mn = fmaxf(qm[nt], xm);
+        if (mn != -INFINITY) {
+          float s_acc = qs[nt] * fast_exp(qm[nt] - mn);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s_acc += fast_exp(x[i] - mn);
+          qs[nt] = s_acc;
+          qm[nt] = mn;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (i < n) win_update(bv[nt], bi[nt], z[i], c + i);
+      }
+    }
+    }
+    if (more) {
+#pragma unroll
+      for (int s = 0; s < kRKMax; ++s) A[s] = An[s];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bz[nt][i] = bzn[nt][i];
+    }
+  }
+
+  // merge the 4 lanes of each request row (lanes lr, lr + 16, lr + 32, lr + 48)
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    unsigned long long key = bi[nt] >= 0 ? win_key(bv[nt], (uint32_t)bi[nt]) : 0ull;
+    float m = qm[nt], s = qnan[nt] ? NAN : qs[nt];
+#pragma unroll
+    for (int off = 16; off < 64; off <<= 1) {
+      const unsigned long long k2 = __shfl_xor(key, off);
+      key = k2 > key ? k2 : key;
+      const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(s, off);
+      lse_merge(m, s, m2, s2);
+    }
+    if (lg == 0) {
+      s_key[wave * NB + nt * 16 + lr] = key;
+      s_qm[wave * NB + nt * 16 + lr] = m;
+      s_qs[wave * NB + nt * 16 + lr] = s;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < NB; i += 256) {
+    const int b = b0 + i;
+    if (b >= a.B) continue;
+    unsigned long long key = s_key[i];
+    float m = s_qm[i], s = s_qs[i];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      const unsigned long long k2 = s_key[w * NB + i];
+      key = k2 > key ? k2 : key;
+      lse_merge(m, s, s_qm[w * NB + i], s_qs[w * NB + i]);
+    }
+    if (key) atomicMax(&a.keys[(size_t)k * a.B + b], key);
+    a.qpart[((size_t)k * a.B + b) * a.G + g] = make_float2(m, s);
+  }
+}
+
+template <int NB, bool BBF16, bool CBF16>
+hipError_t launch_wave(const DraftStepArgs& a, int bt, hipStream_t st) {
+  DraftStepArgs b = a;
+  b.BT = bt;
+  hipLaunchKernelGGL((draft_wave_kernel<NB, BBF16, CBF16>), dim3(a.G * bt), dim3(256), draft_wave_lds(NB, a.r), st,
+                     b);
+  return hipGetLastError();
+}
+
+template <int NB>
+hipError_t launch_wave_nb(const DraftStepArgs& a, int bt, hipStream_t st) {
+  if (a.base_bf16) return a.cache_bf16 ? launch_wave<NB, true, true>(a, bt, st) : launch_wave<NB, true, false>(a, bt, st);
+  return a.cache_bf16 ? launch_wave<NB, false, true>(a, bt, st) : launch_wave<NB, false, false>(a, bt, st);
+}
+
+}  // namespace
+
+size_t draft_wave_lds(int NB, int r) {
+  return (size_t)NB * (r + 8) * 2 + (size_t)NB * 4 + (size_t)4 * NB * 8 + (size_t)8 * NB * 4;
+}
+
+hipError_t launch_draft_wave(const DraftStepArgs& a, hipStream_t st) {
+  if (a.r > 32 * kRKMax) return hipErrorNotSupported;
+  const int nb = draft_nb(a.B, a.r);
+  const int bt = (a.B + nb - 1) / nb;
+  return nb == 16 ? launch_wave_nb<16>(a, bt, st) : launch_wave_nb<32>(a, bt, st);
+}
+
+}  // namespace mds

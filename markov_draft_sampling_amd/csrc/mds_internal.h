@@ -44,8 +44,13 @@ struct DraftFinalArgs {
 
 int draft_nb(int B, int r);
 int draft_slabs(int V, int cus);
+int draft_wave_slabs(int V, int cus);
 hipError_t launch_draft_init(unsigned long long* keys, int n, unsigned* bar, int nbar, hipStream_t st);
 hipError_t launch_draft_step(const DraftStepArgs& a, hipStream_t st);
+// Wave-independent streaming step (rank <= 256); hipErrorNotSupported
+// (nothing launched) for a larger rank.
+size_t draft_wave_lds(int NB, int r);
+hipError_t launch_draft_wave(const DraftStepArgs& a, hipStream_t st);
 // Resident path: one launch runs all K steps with w2 held on chip. Returns
 // hipErrorNotSupported (and launches nothing) when w2 does not fit.
 hipError_t draft_resident_plan(int V, int r, int G, size_t lds_limit, int* n_lds_tiles, size_t* lds_bytes);
