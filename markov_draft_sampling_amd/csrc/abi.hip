@@ -84,7 +84,7 @@ int draft_path_choice() {
 
 struct VerifyLayout {
   int NC;
-  size_t tpart, qpart, rowstat, qlse, topp, req, rkey, total;
+  size_t tpart, qpart, rowstat, qlse, topp, req, total;
 };
 
 // [status block][per-request counters, fixed size][partials and per-row state]
@@ -104,8 +104,6 @@ VerifyLayout verify_layout(int B, int K, int V, bool top_p, bool has_lse) {
   if (top_p) o += up((size_t)B * (K + 1) * sizeof(mds::TopP));
   L.req = o;
   o += up((size_t)B * sizeof(mds::ReqState));
-  L.rkey = o;
-  o += up((size_t)B * 16);
   L.total = o;
   return L;
 }
@@ -120,8 +118,9 @@ void verify_workspace_args(mds::VerifyArgs& a, unsigned char* ws, const VerifyLa
   a.qlse = (float*)(ws + L.qlse);
   a.topp = top_p ? (mds::TopP*)(ws + L.topp) : nullptr;
   a.req = (mds::ReqState*)(ws + L.req);
-  a.rkey = (unsigned long long*)(ws + L.rkey);
+  a.rkey = (unsigned long long*)(ws + mds::kVerifyCounterOffset);
   a.decide = !top_p;
+  a.NR = (a.V + mds::kResCols - 1) / mds::kResCols;
 }
 
 int hip_fail(hipError_t e, const char* where) {

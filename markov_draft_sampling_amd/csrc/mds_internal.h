@@ -94,6 +94,10 @@ struct ReqState {  // the accept decision of one request, read by the residual d
 constexpr size_t kVerifyCounterOffset = 256;
 constexpr size_t kVerifyCounterBytes = (size_t)2048 * 256;
 __host__ __device__ constexpr int verify_counter_index(int b) { return (b & 2047) * 64 + (b >> 11); }
+// The winner key of request b's final draw (64-bit) sits in the upper half of
+// the same 256-byte line as its counter: index in 64-bit words from the start
+// of the counter block.
+__host__ __device__ constexpr int verify_key_index(int b) { return (b & 2047) * 32 + 16 + (b >> 11); }
 
 struct VerifyArgs {
   int B, K, V, NC;
@@ -110,18 +114,21 @@ struct VerifyArgs {
   const long long* anchor_pos;
   int32_t* out_tokens;
   int32_t* num_accepted;
-  unsigned long long* tpart;  // [B*(K+1)][NC] packed partials of the target rows
-  unsigned long long* qpart;  // [B*K][NC] packed partials of the cache rows (draft_lse null)
+  unsigned long long* tpart;  // [NC][B*(K+1)] packed partials of the target rows
+  unsigned long long* qpart;  // [NC][B*K] packed partials of the cache rows (draft_lse null)
   RowStat* rowstat;           // [B*(K+1)]
   float* qlse;                // [B*K] draft log-normalisers (copied or combined)
   TopP* topp;                 // [B*(K+1)] or null
   ReqState* req;              // [B]
-  unsigned long long* rkey;   // [B][2] residual / p winner keys of the final draw
+  unsigned long long* rkey;   // winner keys of the final draws, at verify_key_index(b)
   unsigned* cnt;              // [B] arrival counters (zero between calls)
   uint32_t* status;
   int vec_target;
   int decide;                 // the statistics pass also takes the accept decision (no top-p)
+  int NR;                     // residual blocks per request (kResCols columns each)
 };
+
+constexpr int kResCols = 2048;  // columns per residual work-group
 
 hipError_t launch_verify_stats(const VerifyArgs& a, hipStream_t st);
 hipError_t launch_top_p(const VerifyArgs& a, hipStream_t st);

@@ -13,11 +13,11 @@
 //                    reads the draft cache). The last work-group of a request
 //                    to finish combines its partials and runs the K accept
 //                    tests p(x) >= u * q(x);
-//   residual_kernel  one work-group per (request, block) draws over its block
-//                    with Gumbel-max from the normalised residual
-//                    max(0, p - q) of the first rejected row, or from p for
-//                    the bonus token; the last one of a request writes the
-//                    output tokens.
+//   residual_kernel  one work-group per (request, 2048-column block) draws
+//                    over its block with Gumbel-max from the normalised
+//                    residual max(0, p - q) of the first rejected row, or
+//                    from p for the bonus token; the last one of a request
+//                    writes the output tokens.
 // With top-p the statistics pass only combines rows; the top-p kernel and a
 // small decide_kernel (one work-group per request) sit in between.
 //
@@ -153,26 +153,6 @@ __device__ __forceinline__ unsigned long long block_max_key(unsigned long long k
   return key;
 }
 
-// two keys at once (one LDS round); results valid in thread 0
-__device__ __forceinline__ void block_max_key2(unsigned long long& k0, unsigned long long& k1) {
-  __shared__ unsigned long long sk[2][4];
-  k0 = wave_max_u64(k0);
-  k1 = wave_max_u64(k1);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) {
-    sk[0][wave] = k0;
-    sk[1][wave] = k1;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-#pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w) {
-      k0 = sk[0][w] > k0 ? sk[0][w] : k0;
-      k1 = sk[1][w] > k1 ? sk[1][w] : k1;
-    }
-  }
-}
-
 __device__ __forceinline__ bool kept(const TopP& tp, float t, int v) {
   if (!tp.on) return true;
   const uint32_t o = ord_f32(t);
@@ -196,13 +176,14 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// One wave combines nrows consecutive rows of NC packed partials starting at
-// p: the max of the words (keys) or their (max, sum exp) merge, in chunk
-// order. Partials are read with device-scope atomic loads, staged in LDS a
-// page at a time (all loads of a page in flight together), then lane j merges
-// row j of the page. Results go to om / os / okey [row].
-__device__ void wave_combine(const unsigned long long* p, int nrows, int NC, bool keys, unsigned long long* stage,
-                             float* om, float* os, unsigned long long* okey) {
+// One wave combines nrows consecutive rows of NC packed partials, partial
+// (row, chunk) at p[chunk * cstride + row]: the max of the words (keys) or
+// their (max, sum exp) merge, in chunk order. Partials are read with
+// device-scope atomic loads, staged in LDS a page at a time (all loads of a
+// page in flight together), then lane j merges row j of the page. Results go
+// to om / os / okey [row].
+__device__ void wave_combine(const unsigned long long* p, size_t cstride, int nrows, int NC, bool keys,
+                             unsigned long long* stage, float* om, float* os, unsigned long long* okey) {
   const int lane = threadIdx.x & 63;
   const int cpp = NC < kStage ? NC : kStage;  // chunks per page
   const int rpp = kStage / cpp;               // rows per page, >= 1
@@ -220,7 +201,8 @@ __device__ void wave_combine(const unsigned long long* p, int nrows, int NC, boo
           int t = t0 + u * 64 + lane;
           t = t < n ? t : n - 1;
           const int rr = t / nc, cc = t - rr * nc;
-          w[u] = __hip_atomic_load(p + (size_t)(r0 + rr) * NC + c0 + cc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          w[u] = __hip_atomic_load(p + (size_t)(c0 + cc) * cstride + (r0 + rr), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
         }
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
@@ -312,8 +294,7 @@ __device__ void decide(const VerifyArgs& a, int b, ReqLds& L) {
     r.tp = a.topp ? a.topp[b * (K + 1) + n] : TopP{0u, 0, 0.0f, 0};
     if (r.tp.on) r.LZ = r.tp.log_z;
     a.req[b] = r;
-    a.rkey[2 * b] = 0ull;
-    a.rkey[2 * b + 1] = 0ull;
+    a.rkey[verify_key_index(b)] = 0ull;
     if (greedy) a.num_accepted[b] = n;
   }
 }
@@ -325,7 +306,7 @@ __device__ void combine_request(const VerifyArgs& a, int b, ReqLds& L, unsigned 
   const int K = a.K, NC = a.NC;
   const int lane = threadIdx.x & 63;
   const bool greedy = !(a.temp[b] > 0.0f);
-  wave_combine(a.tpart + (size_t)b * (K + 1) * NC, K + 1, NC, greedy, stage, L.m, L.lz, L.key);
+  wave_combine(a.tpart + (size_t)b * (K + 1), (size_t)a.B * (K + 1), K + 1, NC, greedy, stage, L.m, L.lz, L.key);
   if (lane <= K) {
     const float s = L.lz[lane];
     const float lz = (s != s) ? NAN : __logf(s);
@@ -333,7 +314,7 @@ __device__ void combine_request(const VerifyArgs& a, int b, ReqLds& L, unsigned 
     a.rowstat[b * (K + 1) + lane] = RowStat{L.m[lane], lz, L.key[lane]};
   }
   if (a.qpart && !greedy) {
-    wave_combine(a.qpart + (size_t)b * K * NC, K, NC, false, stage, L.qm, L.lq, L.qkey);
+    wave_combine(a.qpart + (size_t)b * K, (size_t)a.B * K, K, NC, false, stage, L.qm, L.lq, L.qkey);
     if (lane < K) {
       const float s = L.lq[lane];
       const float lq = (s != s) ? NAN : L.qm[lane] + __logf(s);
@@ -379,7 +360,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(VerifyArgs a) {
       block_merge_ms(m, s);
       word = pack_ms(m, s);
     }
-    slot = a.tpart + (size_t)row * NC + chunk;
+    slot = a.tpart + (size_t)chunk * n_t + row;
   } else if (!greedy) {
     const int q = row - n_t, k = q - b * K;
     const long long off = (long long)b * a.cache_rs + (long long)k * a.cache_ss;
@@ -392,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(VerifyArgs a) {
     thread_stats(v, c0, V, T, 1.0f / T, m, s);
     block_merge_ms(m, s);
     word = pack_ms(m, s);
-    slot = a.qpart + (size_t)q * NC + chunk;
+    slot = a.qpart + (size_t)chunk * ((size_t)a.B * K) + q;
   }
   // waves 1..3 are done; wave 0 publishes and, if it is the request's last
   // arrival, combines
@@ -429,85 +410,176 @@ __global__ __launch_bounds__(64) void decide_kernel(VerifyArgs a) {
   decide(a, b, L);
 }
 
+// Score of column c for the final draw: log residual + g (mode 1; only a
+// positive residual is a candidate, with a finite score), else log p + g.
+struct DrawCtx {
+  float T, invT, M, LZ, LQ;
+  TopP tp;
+  uint32_t pk0, pk1, sk0, sk1;
+};
+
+__device__ __forceinline__ float draw_logp(const DrawCtx& d, float t, int c) {
+  return kept(d.tp, t, c) ? div_t(t, d.T, d.invT) - d.M - d.LZ : -INFINITY;
+}
+
+// Gumbel-max over log p of a whole target row by one wave (lanes 0..63): the
+// draw when the residual of the rejected row is empty everywhere.
+__device__ unsigned long long wave_draw_p(const VerifyArgs& a, const float* trow, const DrawCtx& d) {
+  const int lane = threadIdx.x & 63, V = a.V;
+  float bv = -INFINITY;
+  int bi = -1;
+  for (int c = lane * 4; c < V; c += 256) {
+    const Philox4 w = philox4x32_10((uint32_t)(c >> 2), d.pk0, d.pk1, kSaltResample, d.sk0, d.sk1);
+    const uint32_t wd[4] = {w.x0, w.x1, w.x2, w.x3};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (c + e < V) win_update(bv, bi, draw_logp(d, trow[c + e], c + e) + gumbel_from_word(wd[e]), c + e);
+  }
+  return wave_max_u64(bi >= 0 ? win_key(bv, (uint32_t)bi) : 0ull);
+}
+
+// One work-group per (request, kResCols-column block): the block's winner of
+// the final draw is merged into the request's key with one atomic max; the
+// last block of the request writes the output tokens. In mode 1 only the
+// residual is scored; if it turns out empty everywhere (key 0) the last block
+// draws from p over the whole row instead.
+template <bool CBF16>
 __global__ __launch_bounds__(kThreads) void residual_kernel(VerifyArgs a) {
+  constexpr int kPer = kResCols / kThreads;  // 8 columns: c0 + 1024 i + 4 tid + e
   const int chunk = blockIdx.x, b = blockIdx.y;
   const ReqState rq = a.req[b];
   if (rq.mode == 2) return;
   const int K = a.K, V = a.V;
-  const float T = a.temp[b];
-  const float invT = 1.0f / T;
   const int j = rq.n_acc, mode = rq.mode;
-  const float M = rq.M, LZ = rq.LZ, LQ = rq.LQ;
-  const TopP tp = rq.tp;
-  const int c0 = chunk * kStatsChunk;
-  const int tc = c0 + (int)threadIdx.x * 4;
-  float tv[kPerThread], cv[kPerThread];
-  load_block<false>(a.target + (long long)(b * (K + 1) + j) * a.target_rs, V, c0, a.vec_target != 0, 0.0f, tv);
-  if (mode == 1) {
-    const long long off = (long long)b * a.cache_rs + (long long)j * a.cache_ss;
-    if (a.cache_bf16)
-      load_block<true>((const uint16_t*)a.cache + off, V, c0, a.vec_cache != 0, 0.0f, cv);
-    else
-      load_block<false>((const float*)a.cache + off, V, c0, a.vec_cache != 0, 0.0f, cv);
-  }
+  DrawCtx d;
+  d.T = a.temp[b];
+  d.invT = 1.0f / d.T;
+  d.M = rq.M;
+  d.LZ = rq.LZ;
+  d.LQ = rq.LQ;
+  d.tp = rq.tp;
   const unsigned long long sd = (unsigned long long)a.seeds[b];
   const unsigned long long pk = (unsigned long long)(a.anchor_pos[b] + j);
-  float bvr = -INFINITY, bvp = -INFINITY;
-  int bir = -1, bip = -1;
+  d.pk0 = (uint32_t)pk;
+  d.pk1 = (uint32_t)(pk >> 32);
+  d.sk0 = (uint32_t)sd;
+  d.sk1 = (uint32_t)(sd >> 32);
+  const bool resid = mode == 1;
+  const float* trow = a.target + (long long)(b * (K + 1) + j) * a.target_rs;
+  const long long crow = (long long)b * a.cache_rs + (long long)j * a.cache_ss;
+  const int c0 = chunk * kResCols;
+  const int tc = c0 + (int)threadIdx.x * 4;
+  float tv[kPer], cv[kPer];
+  if (a.vec_target && c0 + kResCols <= V) {  // block-uniform: all loads issued before any use
 #pragma unroll
-  for (int i = 0; i < kPerThread / 4; ++i) {
+    for (int i = 0; i < kPer / 4; ++i) {
+      const f32x4 w = __builtin_nontemporal_load((const f32x4*)(trow + tc + i * 1024));
+      tv[4 * i + 0] = w.x;
+      tv[4 * i + 1] = w.y;
+      tv[4 * i + 2] = w.z;
+      tv[4 * i + 3] = w.w;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int c = tc + (q >> 2) * 1024 + (q & 3);
+      tv[q] = c < V ? trow[c] : 0.0f;
+    }
+  }
+  // bf16 cache words stay packed until they are used, so no unpacking
+  // waits on a load before the next one is issued
+  uint32_t cw[kPer / 2];
+  if (resid) {
+    if (a.vec_cache && c0 + kResCols <= V) {
+#pragma unroll
+      for (int i = 0; i < kPer / 4; ++i) {
+        if (CBF16) {
+          const u32x2 w = __builtin_nontemporal_load((const u32x2*)((const uint16_t*)a.cache + crow + tc + i * 1024));
+          cw[2 * i + 0] = w.x;
+          cw[2 * i + 1] = w.y;
+        } else {
+          const f32x4 w = __builtin_nontemporal_load((const f32x4*)((const float*)a.cache + crow + tc + i * 1024));
+          cv[4 * i + 0] = w.x;
+          cv[4 * i + 1] = w.y;
+          cv[4 * i + 2] = w.z;
+          cv[4 * i + 3] = w.w;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        const int c = tc + (q >> 2) * 1024 + (q & 3);
+        if (CBF16) {
+          const uint32_t h = c < V ? ((const uint16_t*)a.cache)[crow + c] : 0u;
+          cw[q >> 1] = (q & 1) ? (cw[q >> 1] | (h << 16)) : h;
+        } else {
+          cv[q] = c < V ? ((const float*)a.cache)[crow + c] : 0.0f;
+        }
+      }
+    }
+  }
+  float bv = -INFINITY;
+  int bi = -1;
+#pragma unroll
+  for (int i = 0; i < kPer / 4; ++i) {
     const int c = tc + i * 1024;
     if (c >= V) break;
-    const Philox4 w = philox4x32_10((uint32_t)(c >> 2), (uint32_t)pk, (uint32_t)(pk >> 32), kSaltResample,
-                                    (uint32_t)sd, (uint32_t)(sd >> 32));
+    const Philox4 w = philox4x32_10((uint32_t)(c >> 2), d.pk0, d.pk1, kSaltResample, d.sk0, d.sk1);
     const uint32_t wd[4] = {w.x0, w.x1, w.x2, w.x3};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if (c + e < V) {
         const float g = gumbel_from_word(wd[e]);
-        const float t = tv[4 * i + e];
-        const float logp = kept(tp, t, c + e) ? div_t(t, T, invT) - M - LZ : -INFINITY;
-        win_update(bvp, bip, logp + g, c + e);
-        if (mode == 1) {
-          const float rv = __expf(logp) - __expf(div_t(cv[4 * i + e], T, invT) - LQ);
-          // only a positive residual is a candidate; its score is finite
+        const float logp = draw_logp(d, tv[4 * i + e], c + e);
+        if (resid) {
+          const int q = 4 * i + e;
+          const float cq = CBF16 ? bf16_bits_to_f32((q & 1) ? (cw[q >> 1] >> 16) : (cw[q >> 1] & 0xFFFFu)) : cv[q];
+          const float rv = __expf(logp) - __expf(div_t(cq, d.T, d.invT) - d.LQ);
           const float sr = fmaxf(__logf(rv), -0x1.fffffep+127f) + g;
-          const bool take = rv > 0.0f && (sr > bvr || bir < 0);
-          bvr = take ? sr : bvr;
-          bir = take ? c + e : bir;
+          const bool take = rv > 0.0f && (sr > bv || bi < 0);
+          bv = take ? sr : bv;
+          bi = take ? c + e : bi;
+        } else {
+          win_update(bv, bi, logp + g, c + e);
         }
       }
     }
   }
-  unsigned long long kr = bir >= 0 ? win_key(bvr, (uint32_t)bir) : 0ull;
-  unsigned long long kp = bip >= 0 ? win_key(bvp, (uint32_t)bip) : 0ull;
-  block_max_key2(kr, kp);
+  const unsigned long long key = block_max_key(bi >= 0 ? win_key(bv, (uint32_t)bi) : 0ull);
+  // waves 1..3 are done; wave 0 publishes and, if last, finishes the request
+  if (threadIdx.x >= 64) return;
+  unsigned long long* rk = a.rkey + verify_key_index(b);
+  unsigned* cnt = a.cnt + verify_counter_index(b);
+  int last = 0;
   if (threadIdx.x == 0) {
-    unsigned long long* rk = a.rkey + 2 * b;
-    const unsigned long long p0 = atomicMax(rk, kr);
-    const unsigned long long p1 = atomicMax(rk + 1, kp);
-    asm volatile("" ::"v"(p0), "v"(p1));  // keep the returning forms
+    const unsigned long long prev = atomicMax(rk, key);
+    asm volatile("" ::"v"(prev));  // keep the returning form
     wait_vmem();
-    unsigned* cnt = a.cnt + verify_counter_index(b);
-    if (atomicAdd(cnt, 1u) == (unsigned)a.NC - 1u) {
-      // every block of the request has published: read and clear the keys
-      const unsigned long long KR = atomicExch(rk, 0ull);
-      const unsigned long long KP = atomicExch(rk + 1, 0ull);
-      atomicExch(cnt, 0u);
-      const int token = (int)win_col((mode == 1 && KR != 0ull) ? KR : KP);
-      for (int i = 0; i <= K; ++i) {
-        int v = -1;
-        if (i < j) {
-          v = a.draft[b * K + i];
-          if (v < 0 || v >= V) v = 0;
-        } else if (i == j) {
-          v = token;
-        }
-        a.out_tokens[(size_t)b * (K + 1) + i] = v;
-      }
-      a.num_accepted[b] = j;
-    }
+    last = atomicAdd(cnt, 1u) == (unsigned)a.NR - 1u;
   }
+  last = __shfl(last, 0);
+  if (!last) return;
+  // every block of the request has published: read and clear the key
+  unsigned long long KEY = 0ull;
+  if (threadIdx.x == 0) {
+    KEY = atomicExch(rk, 0ull);
+    atomicExch(cnt, 0u);
+  }
+  KEY = __shfl(KEY, 0);
+  if (resid && KEY == 0ull) KEY = wave_draw_p(a, trow, d);
+  const int token = (int)win_col(KEY);
+  const int i = threadIdx.x;
+  if (i <= K) {
+    int v = -1;
+    if (i < j) {
+      v = a.draft[b * K + i];
+      if (v < 0 || v >= V) v = 0;
+    } else if (i == j) {
+      v = token;
+    }
+    a.out_tokens[(size_t)b * (K + 1) + i] = v;
+  }
+  if (i == 0) a.num_accepted[b] = j;
 }
 
 __global__ void debug_noise_kernel(int n, const int32_t* cols, long long seed, long long pos, uint32_t salt,
@@ -545,7 +617,10 @@ hipError_t launch_decide(const VerifyArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_residual(const VerifyArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(residual_kernel, dim3(a.NC, a.B), dim3(kThreads), 0, st, a);
+  if (a.cache_bf16)
+    hipLaunchKernelGGL(residual_kernel<true>, dim3(a.NR, a.B), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(residual_kernel<false>, dim3(a.NR, a.B), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
