@@ -84,7 +84,7 @@ int draft_path_choice() {
 
 struct VerifyLayout {
   int NC;
-  size_t tpart, qpart, rowstat, qlse, topp, req, total;
+  size_t tpart, qpart, rowstat, qlse, tq, topp, req, total;
 };
 
 // [status block][per-request counters, fixed size][partials and per-row state]
@@ -100,6 +100,8 @@ VerifyLayout verify_layout(int B, int K, int V, bool top_p, bool has_lse) {
   o += up((size_t)B * (K + 1) * sizeof(mds::RowStat));
   L.qlse = o;
   o += up((size_t)B * K * sizeof(float));
+  L.tq = o;
+  o += up((size_t)B * K * 8);
   L.topp = top_p ? o : 0;
   if (top_p) o += up((size_t)B * (K + 1) * sizeof(mds::TopP));
   L.req = o;
@@ -116,6 +118,7 @@ void verify_workspace_args(mds::VerifyArgs& a, unsigned char* ws, const VerifyLa
   a.qpart = has_lse ? nullptr : (unsigned long long*)(ws + L.qpart);
   a.rowstat = (mds::RowStat*)(ws + L.rowstat);
   a.qlse = (float*)(ws + L.qlse);
+  a.tq = (unsigned long long*)(ws + L.tq);
   a.topp = top_p ? (mds::TopP*)(ws + L.topp) : nullptr;
   a.req = (mds::ReqState*)(ws + L.req);
   a.rkey = (unsigned long long*)(ws + mds::kVerifyCounterOffset);

@@ -118,6 +118,7 @@ struct VerifyArgs {
   unsigned long long* qpart;  // [NC][B*K] packed partials of the cache rows (draft_lse null)
   RowStat* rowstat;           // [B*(K+1)]
   float* qlse;                // [B*K] draft log-normalisers (copied or combined)
+  unsigned long long* tq;     // [B*K] (target, cache) logits at the draft tokens, packed
   TopP* topp;                 // [B*(K+1)] or null
   ReqState* req;              // [B]
   unsigned long long* rkey;   // winner keys of the final draws, at verify_key_index(b)

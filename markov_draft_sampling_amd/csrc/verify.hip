@@ -164,7 +164,21 @@ struct ReqLds {
   float m[kMaxK + 1], lz[kMaxK + 1], lq[kMaxK], qm[kMaxK];
   unsigned long long key[kMaxK + 1], qkey[kMaxK];
   int acc[kMaxK];
+  int x[kMaxK];             // draft tokens (sampled requests: clamped into [0, V))
+  float tx[kMaxK], cx[kMaxK];  // target and cache logits at the draft tokens
 };
+
+// Draft token k of request b and the target / cache logits at it. A token
+// outside [0, V) is replaced by 0 and flagged in the status word.
+__device__ __forceinline__ void draft_point(const VerifyArgs& a, int b, int k, int& x, float& tx, float& cx) {
+  x = a.draft[b * a.K + k];
+  if (x < 0 || x >= a.V) {
+    set_status(a.status, kStatusBadDraft);
+    x = 0;
+  }
+  tx = a.target[(long long)(b * (a.K + 1) + k) * a.target_rs + x];
+  cx = load_f32_or_bf16(a.cache, (long long)b * a.cache_rs + (long long)k * a.cache_ss + x, a.cache_bf16);
+}
 
 constexpr int kStage = 1024;  // partials a combining wave stages in LDS at a time
 
@@ -178,10 +192,11 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 // One wave combines nrows consecutive rows of NC packed partials, partial
 // (row, chunk) at p[chunk * cstride + row]: the max of the words (keys) or
-// their (max, sum exp) merge, in chunk order. Partials are read with
-// device-scope atomic loads, staged in LDS a page at a time (all loads of a
-// page in flight together), then lane j merges row j of the page. Results go
-// to om / os / okey [row].
+// their (max, sum exp) merge. Partials are read with device-scope atomic
+// loads and staged in LDS a page at a time (all loads of a page in flight
+// together); each row of the page is then merged by a group of lanes (a
+// power of two) and the group's results by shuffles. Results go to
+// om / os / okey [row].
 __device__ void wave_combine(const unsigned long long* p, size_t cstride, int nrows, int NC, bool keys,
                              unsigned long long* stage, float* om, float* os, unsigned long long* okey) {
   const int lane = threadIdx.x & 63;
@@ -189,6 +204,10 @@ __device__ void wave_combine(const unsigned long long* p, size_t cstride, int nr
   const int rpp = kStage / cpp;               // rows per page, >= 1
   for (int r0 = 0; r0 < nrows; r0 += rpp) {
     const int nr = nrows - r0 < rpp ? nrows - r0 : rpp;
+    // lanes per row: the largest power of two with nr * lpr <= 64 (1 if nr > 32)
+    int lpr = 64;
+    while (lpr > 1 && lpr * nr > 64) lpr >>= 1;
+    const int grp = lane / lpr, sub = lane - grp * lpr;  // lane's row of the page, and its place in the group
     float m = -INFINITY, s = 0.0f;
     unsigned long long key = 0ull;
     for (int c0 = 0; c0 < NC; c0 += cpp) {
@@ -198,22 +217,24 @@ __device__ void wave_combine(const unsigned long long* p, size_t cstride, int nr
         unsigned long long w[16];
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
-          int t = t0 + u * 64 + lane;
-          t = t < n ? t : n - 1;
-          const int rr = t / nc, cc = t - rr * nc;
-          w[u] = __hip_atomic_load(p + (size_t)(c0 + cc) * cstride + (r0 + rr), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+          if (t0 + u * 64 < n) {  // wave-uniform: only batches holding some partial
+            int t = t0 + u * 64 + lane;
+            t = t < n ? t : n - 1;
+            const int rr = t / nc, cc = t - rr * nc;
+            w[u] = __hip_atomic_load(p + (size_t)(c0 + cc) * cstride + (r0 + rr), __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+          }
         }
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
           const int t = t0 + u * 64 + lane;
-          if (t < n) stage[t] = w[u];
+          if (t0 + u * 64 < n && t < n) stage[t] = w[u];
         }
       }
       wave_lds_sync();
-      if (lane < nr) {
-        for (int cc = 0; cc < nc; ++cc) {
-          const unsigned long long x = stage[lane * nc + cc];
+      if (grp < nr) {  // nr <= 33 rows, so every row has a group of its own
+        for (int cc = sub; cc < nc; cc += lpr) {
+          const unsigned long long x = stage[grp * nc + cc];
           if (keys)
             key = x > key ? x : key;
           else
@@ -222,10 +243,17 @@ __device__ void wave_combine(const unsigned long long* p, size_t cstride, int nr
       }
       wave_lds_sync();
     }
-    if (lane < nr) {
-      om[r0 + lane] = m;
-      os[r0 + lane] = s;
-      okey[r0 + lane] = key;
+    // merge the lpr lanes of each group (xor within the aligned group)
+    for (int off = 1; off < lpr; off <<= 1) {
+      const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(s, off);
+      const unsigned long long k2 = __shfl_xor(key, off);
+      lse_merge(m, s, m2, s2);
+      key = k2 > key ? k2 : key;
+    }
+    if (sub == 0 && grp < nr) {
+      om[r0 + grp] = m;
+      os[r0 + grp] = s;
+      okey[r0 + grp] = key;
     }
   }
   wave_lds_sync();
@@ -243,23 +271,17 @@ __device__ void decide(const VerifyArgs& a, int b, ReqLds& L) {
   const float invT = greedy ? 1.0f : 1.0f / T;
   if (lane < K) {
     const int k = lane;
-    int x = a.draft[b * K + k];
+    const int x = L.x[k];
     bool ok;
     if (greedy) {
       ok = x == (int32_t)win_col(L.key[k]);
     } else {
-      if (x < 0 || x >= V) {
-        set_status(a.status, kStatusBadDraft);
-        x = 0;
-      }
       const int row = b * (K + 1) + k;
-      const float tx = a.target[(long long)row * a.target_rs + x];
+      const float tx = L.tx[k];
       float logp = -INFINITY;
       if (!a.topp || kept(a.topp[row], tx, x)) logp = div_t(tx, T, invT) - L.m[k] - L.lz[k];
       const float p = expf(logp);
-      const long long coff = (long long)b * a.cache_rs + (long long)k * a.cache_ss + x;
-      const float cx = load_f32_or_bf16(a.cache, coff, a.cache_bf16);
-      const float q = expf(div_t(cx, T, invT) - L.lq[k]);
+      const float q = expf(div_t(L.cx[k], T, invT) - L.lq[k]);
       const unsigned long long sd = (unsigned long long)a.seeds[b];
       const unsigned long long pk = (unsigned long long)(a.anchor_pos[b] + k);
       const Philox4 w = philox4x32_10(0u, (uint32_t)pk, (uint32_t)(pk >> 32), kSaltAccept, (uint32_t)sd,
@@ -306,6 +328,19 @@ __device__ void combine_request(const VerifyArgs& a, int b, ReqLds& L, unsigned 
   const int K = a.K, NC = a.NC;
   const int lane = threadIdx.x & 63;
   const bool greedy = !(a.temp[b] > 0.0f);
+  // the draft tokens, and the logits at them that block 0 of each target row
+  // published, load together with the partials
+  if (lane < K) {
+    const int x = a.draft[b * K + lane];
+    if (greedy) {
+      L.x[lane] = x;
+    } else {
+      const unsigned long long w = __hip_atomic_load(a.tq + b * K + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      L.x[lane] = (x < 0 || x >= a.V) ? 0 : x;
+      L.tx[lane] = unpack_m(w);
+      L.cx[lane] = unpack_s(w);
+    }
+  }
   wave_combine(a.tpart + (size_t)b * (K + 1), (size_t)a.B * (K + 1), K + 1, NC, greedy, stage, L.m, L.lz, L.key);
   if (lane <= K) {
     const float s = L.lz[lane];
@@ -344,14 +379,17 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(VerifyArgs a) {
   if (row >= n_rows) return;
   const bool is_target = row < n_t;
   const int b = is_target ? row / (K + 1) : (row - n_t) / K;
-  const float T = a.temp[b];
-  const bool greedy = !(T > 0.0f);
   const int c0 = chunk * kStatsChunk;
   unsigned long long* slot = nullptr;
   unsigned long long word = 0ull;
   if (is_target) {
+    // the row's loads go out first: nothing about them depends on T, and a
+    // branch on T placed above them would hold them behind the load of T
     float v[kPerThread];
     load_block<false>(a.target + (long long)row * a.target_rs, V, c0, a.vec_target != 0, 0.0f, v);
+    asm volatile("" ::: "memory");
+    const float T = a.temp[b];
+    const bool greedy = !(T > 0.0f);
     if (greedy) {
       word = block_max_key(thread_key(v, c0, V));
     } else {
@@ -361,7 +399,8 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(VerifyArgs a) {
       word = pack_ms(m, s);
     }
     slot = a.tpart + (size_t)chunk * n_t + row;
-  } else if (!greedy) {
+  } else if (a.temp[b] > 0.0f) {
+    const float T = a.temp[b];
     const int q = row - n_t, k = q - b * K;
     const long long off = (long long)b * a.cache_rs + (long long)k * a.cache_ss;
     float v[kPerThread];
@@ -384,6 +423,16 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(VerifyArgs a) {
       const unsigned long long prev = atomicExch(slot, word);
       asm volatile("" ::"v"(prev));  // keep the returning form
     }
+    // block 0 of target row k < K of a sampled request also publishes the
+    // target and cache logits at draft token k, for the accept test
+    const int k = row - b * (K + 1);
+    if (is_target && chunk == 0 && k < K && a.temp[b] > 0.0f) {
+      int x;
+      float tx, cx;
+      draft_point(a, b, k, x, tx, cx);
+      const unsigned long long prev = atomicExch(a.tq + b * K + k, pack_ms(tx, cx));
+      asm volatile("" ::"v"(prev));
+    }
     wait_vmem();
     const unsigned n_wg = (unsigned)NC * (unsigned)(K + 1 + (a.qpart ? K : 0));
     last = atomicAdd(a.cnt + verify_counter_index(b), 1u) == n_wg - 1;
@@ -404,7 +453,14 @@ __global__ __launch_bounds__(64) void decide_kernel(VerifyArgs a) {
     L.m[j] = rs.m;
     L.lz[j] = tp.on ? tp.log_z : rs.lz;
     L.key[j] = rs.key;
-    if (j < K) L.lq[j] = a.qlse[b * K + j];
+    if (j < K) {
+      L.lq[j] = a.qlse[b * K + j];
+      if (a.temp[b] > 0.0f) {
+        draft_point(a, b, j, L.x[j], L.tx[j], L.cx[j]);
+      } else {
+        L.x[j] = a.draft[b * K + j];
+      }
+    }
   }
   wave_lds_sync();
   decide(a, b, L);
