@@ -101,7 +101,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="do not flush caches between timed steps")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain 256 MiB device copy (reference dispatch for counter scaling)")
+                    help="also run a plain 256 MiB elementwise copy (reference dispatch for counter scaling)")
     a = ap.parse_args()
     if a.gpus != 1:
         print("bench.py runs on one GPU only: the path is measured on a single MI355X "
@@ -228,11 +228,13 @@ def main():
         "timed_wall_s": wall,
     }
     if a.copy_calibration:
+        # an elementwise kernel (a same-size tensor copy would go to a DMA
+        # engine, which the shader counters do not see)
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
             flush.sum()
-            dst.copy_(src)
+            torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         res["copy_calibration_bytes"] = {"read": src.numel() * 4, "write": dst.numel() * 4}
     if not a.no_cpu_baseline:

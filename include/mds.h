@@ -125,9 +125,9 @@ int mds_verify_workspace_bytes(int B, int K, int V, int has_top_p, int has_draft
  * free for the duration of the call (one work-group per CU, grid barriers
  * between steps with a bounded wait, see MDS_STATUS_BARRIER_TIMEOUT).
  * Otherwise one launch per step streams w2 each time. The environment
- * variable MDS_DRAFT_PATH selects: "stream" (the default) the streaming
- * kernel, "auto" the resident kernel when w2 fits, "resident" requires it
- * (MDS_ERR_UNSUPPORTED if it does not fit).
+ * variable MDS_DRAFT_PATH selects: "stream" (the default) one streaming
+ * launch per step, "auto" the resident kernel when w2 fits, "resident"
+ * requires it (MDS_ERR_UNSUPPORTED if it does not fit).
  */
 int mds_markov_draft_loop(int B, int K, int V, int r,
                           const void* base, int base_dtype, int64_t base_req_stride, int64_t base_step_stride,
