@@ -40,7 +40,8 @@ def _logsumexp(x64: np.ndarray) -> float:
 
 
 def draft_loop(base, base_dtype: str, w1_bits, w2_bits, anchor_tokens, anchor_pos, seeds, temperature,
-               cache_dtype: str, K: int | None = None, teacher=None, want_scores: bool = False) -> dict:
+               cache_dtype: str, K: int | None = None, teacher=None, want_scores: bool = False,
+               idx_map=None, row_mapping=None, sample_pos=None, cache_init=None) -> dict:
     """Run the K-step Markov draft loop for every request.
 
     base: [B, >=K, V] float32, or uint16 bf16 bit patterns when base_dtype is "bf16";
@@ -50,9 +51,22 @@ def draft_loop(base, base_dtype: str, w1_bits, w2_bits, anchor_tokens, anchor_po
     previous token instead of the oracle's own sample (each step then checks
     independently against another implementation's tokens).
 
-    Returns tokens [B, K] int32, cache [B, K, V] (float32 or uint16 bf16 bits),
-    lse [B, K] float64 (log-sum-exp of cache / T; NaN for greedy rows) and
-    margin [B, K] float64 (top-two gap of the float32 scores).
+    Request-state indexing (the API page's ``_sample_logits`` / ``gumbel_sample``
+    call: per-row ``idx_map``, ``sample_pos`` and the cache's ``row_mapping``):
+    idx_map [B, K] gives the state slot of row b at step k; temperature and
+    seeds are then indexed by slot, the draw is keyed by sample_pos[b, k] - 1
+    (the position before the predicted token) instead of anchor_pos[b] + k, and
+    the cache row is row_mapping[slot] (the slot itself without a mapping) in
+    a cache of cache_init's shape [R, K, V] (cache_init is copied, so rows the
+    call does not write keep their values). A negative slot makes that step of
+    the row inert (the page's padding slots: no cache write): its token is -1
+    and its lse NaN; a later non-inert step of the row then has no valid
+    previous token, and uses token 0 (flagged by bad_prev).
+
+    Returns tokens [B, K] int32, cache [B, K, V] (float32 or uint16 bf16 bits;
+    [R, K, V] with idx_map), lse [B, K] float64 (log-sum-exp of cache / T; NaN
+    for greedy rows) and margin [B, K] float64 (top-two gap of the float32
+    scores).
     """
     base = np.asarray(base)
     B, _, V = base.shape
@@ -60,29 +74,50 @@ def draft_loop(base, base_dtype: str, w1_bits, w2_bits, anchor_tokens, anchor_po
     w1 = bf16_to_f64(w1_bits)
     w2t = np.ascontiguousarray(bf16_to_f64(w2_bits).T)  # [r, V]
     tokens = np.zeros((B, K), np.int32)
-    cache = np.zeros((B, K, V), np.uint16 if cache_dtype == "bf16" else np.float32)
+    if idx_map is None:
+        cache = np.zeros((B, K, V), np.uint16 if cache_dtype == "bf16" else np.float32)
+    else:
+        cache = np.array(cache_init, copy=True)
+        idx_map = np.asarray(idx_map, np.int64)
     lse = np.full((B, K), np.nan)
     margin = np.zeros((B, K))
     scores_out = np.zeros((B, K, V), np.float32) if want_scores else None
     prev = np.asarray(anchor_tokens, dtype=np.int64).copy()
-    if (prev < 0).any() or (prev >= V).any():
+    bad_prev = False
+    if idx_map is None and ((prev < 0).any() or (prev >= V).any()):
         raise ValueError("anchor token out of range")
     for k in range(K):
+        live = np.ones(B, bool) if idx_map is None else idx_map[:, k] >= 0
+        if ((prev < 0) | (prev >= V))[live].any():
+            if idx_map is None:
+                raise ValueError("previous token out of range")
+            bad_prev = True
+        prev = np.where((prev >= 0) & (prev < V), prev, 0)
         emb = w1[prev]  # [B, r]: row gather (markov_embed)
         bias = emb @ w2t  # [B, V]: markov_bias, exact products, float64 sums
         row = bf16_to_f64(base[:, k]) if base_dtype == "bf16" else base[:, k].astype(np.float64)
         z32 = (row + bias).astype(np.float32)  # one rounding
         if cache_dtype == "bf16":
             cbits = bf16_rne(z32)
-            cache[:, k] = cbits
             cval = bf16_to_f64(cbits)
         else:
-            cache[:, k] = z32
+            cbits = z32
             cval = z32.astype(np.float64)
         for b in range(B):
-            T = np.float32(temperature[b])
+            if idx_map is None:
+                slot, crow, key = b, b, int(anchor_pos[b]) + k
+            else:
+                slot = int(idx_map[b, k])
+                if slot < 0:  # inert: no cache write, no sample
+                    tokens[b, k] = -1
+                    margin[b, k] = np.inf
+                    continue
+                crow = slot if row_mapping is None else int(row_mapping[slot])
+                key = (int(sample_pos[b, k]) - 1) if sample_pos is not None else int(anchor_pos[b]) + k
+            cache[crow, k] = cbits[b]
+            T = np.float32(temperature[slot])
             if T > 0:
-                g32 = gumbel_row(int(seeds[b]), int(anchor_pos[b]) + k, SALT_DRAFT, V).astype(np.float32)
+                g32 = gumbel_row(int(seeds[slot]), key, SALT_DRAFT, V).astype(np.float32)
                 s = (z32[b] / T).astype(np.float32) + g32
                 lse[b, k] = _logsumexp(cval[b] / np.float64(T))
             else:
@@ -92,7 +127,7 @@ def draft_loop(base, base_dtype: str, w1_bits, w2_bits, anchor_tokens, anchor_po
             if want_scores:
                 scores_out[b, k] = s
         prev = tokens[:, k].astype(np.int64) if teacher is None else np.asarray(teacher, np.int64)[:, k]
-    out = {"tokens": tokens, "cache": cache, "lse": lse, "margin": margin}
+    out = {"tokens": tokens, "cache": cache, "lse": lse, "margin": margin, "bad_prev": bad_prev}
     if want_scores:
         out["scores"] = scores_out
     return out

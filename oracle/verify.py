@@ -23,7 +23,15 @@ Readings where the pages are silent (each listed in the design doc):
   their argmax is taken over float32 scores;
 * a residual with zero total mass (p == q, or a draft row holding NaN, which
   makes every q NaN) falls back to sampling from p;
-* top_p >= 1 disables top-p for a request.
+* top_p >= 1 disables top-p for a request;
+* a draft token of -1 is a placeholder (PR #65007, Tests: rejection sampling
+  with -1 placeholder drafts): the request's drafts end there, so the draw
+  after the accepted run is taken from p of that row, as when all K drafts
+  are accepted;
+* request-state indexing: idx_map [B] gives the state slot of request b
+  (temperature, seeds and top_p are indexed by slot) and its cache rows are
+  row_mapping[slot] (the slot itself without a mapping); a negative slot is a
+  padding request: no work, every output token -1 and 0 accepted.
 """
 from __future__ import annotations
 
@@ -66,12 +74,14 @@ def top_p_keep(t_row, T: float, p: float):
     return mask, bool(near)
 
 
-def verify(target, cache, cache_dtype: str, draft_tokens, temperature, top_p, seeds, anchor_pos) -> dict:
+def verify(target, cache, cache_dtype: str, draft_tokens, temperature, top_p, seeds, anchor_pos,
+           idx_map=None, row_mapping=None) -> dict:
     """Verify the drafts of every request.
 
     target: [B*(K+1), V] float32, row b*(K+1)+j is position P0+1+j of request b;
     cache: [B, K, V] float32 or uint16 bf16 bits (pre-temperature draft logits);
-    draft_tokens: [B, K]; temperature [B] (0 = greedy); top_p [B] or None.
+    draft_tokens: [B, K] (-1 = placeholder); temperature, seeds, top_p [B], or
+    [slots] with idx_map (0 = greedy; top_p may be None).
 
     Returns out_tokens [B, K+1] int32 (accepted drafts, then the final token,
     then -1), num_accepted [B], and diagnostics: accept_margin (the smallest
@@ -90,15 +100,24 @@ def verify(target, cache, cache_dtype: str, draft_tokens, temperature, top_p, se
     near_tp = np.zeros(B, bool)
     final_row = np.zeros(B, np.int32)
     for b in range(B):
-        T = float(np.float32(temperature[b]))
+        slot, crow = b, b
+        if idx_map is not None:
+            slot = int(idx_map[b])
+            if slot < 0:  # padding request
+                continue
+            crow = slot if row_mapping is None else int(row_mapping[slot])
+        T = float(np.float32(temperature[slot]))
         rows = target[b * (K + 1):(b + 1) * (K + 1)]
-        if np.any(draft_tokens[b] < 0) or np.any(draft_tokens[b] >= V):
+        d = np.asarray(draft_tokens[b], np.int64)
+        if np.any(d < -1) or np.any(d >= V):
             raise ValueError("draft token out of range")
+        ph = np.nonzero(d == -1)[0]
+        Kb = int(ph[0]) if ph.size else K  # drafts end at the first placeholder
         if T == 0.0:
             # greedy: accept while the draft equals the target argmax
             a = [argmax_rule(rows[j]) for j in range(K + 1)]
             n = 0
-            while n < K and int(draft_tokens[b, n]) == a[n]:
+            while n < Kb and int(draft_tokens[b, n]) == a[n]:
                 n += 1
             out[b, :n] = draft_tokens[b, :n]
             out[b, n] = a[n]
@@ -106,7 +125,7 @@ def verify(target, cache, cache_dtype: str, draft_tokens, temperature, top_p, se
             final_row[b] = n
             smp_margin[b] = top_two_margin(rows[n])
             continue
-        tp = None if top_p is None else float(top_p[b])
+        tp = None if top_p is None else float(top_p[slot])
         p_rows = []
         for j in range(K + 1):
             pj = _softmax(rows[j].astype(np.float64) / T)
@@ -119,13 +138,13 @@ def verify(target, cache, cache_dtype: str, draft_tokens, temperature, top_p, se
                 p_rows.append((pj, False))
         n = 0
         rejected = False
-        for k in range(K):
+        for k in range(Kb):
             x = int(draft_tokens[b, k])
-            crow = bf16_to_f64(cache[b, k]) if cache_dtype == "bf16" else np.asarray(cache[b, k], np.float64)
-            qk = _softmax(crow / T) if not np.isnan(crow).any() else np.full(V, np.nan)
+            cr = bf16_to_f64(cache[crow, k]) if cache_dtype == "bf16" else np.asarray(cache[crow, k], np.float64)
+            qk = _softmax(cr / T) if not np.isnan(cr).any() else np.full(V, np.nan)
             pk, near = p_rows[k]
             near_tp[b] |= near
-            u = accept_uniform(int(seeds[b]), int(anchor_pos[b]) + k)
+            u = accept_uniform(int(seeds[slot]), int(anchor_pos[b]) + k)
             p32, q32 = np.float32(pk[x]), np.float32(qk[x])
             ok = bool(p32 >= np.float32(np.float32(u) * q32))  # False when q is NaN
             if np.isnan(qk[x]):
@@ -137,7 +156,7 @@ def verify(target, cache, cache_dtype: str, draft_tokens, temperature, top_p, se
             acc_margin[b] = min(acc_margin[b], m)
             if not ok:
                 rejected = True
-                g = gumbel_row(int(seeds[b]), int(anchor_pos[b]) + k, SALT_RESAMPLE, V)
+                g = gumbel_row(int(seeds[slot]), int(anchor_pos[b]) + k, SALT_RESAMPLE, V)
                 if np.isnan(qk).any():
                     r = np.zeros(V)
                 else:
@@ -151,15 +170,15 @@ def verify(target, cache, cache_dtype: str, draft_tokens, temperature, top_p, se
                 break
             n += 1
         if not rejected:
-            pK, near = p_rows[K]
+            pK, near = p_rows[Kb]
             near_tp[b] |= near
-            g = gumbel_row(int(seeds[b]), int(anchor_pos[b]) + K, SALT_RESAMPLE, V)
+            g = gumbel_row(int(seeds[slot]), int(anchor_pos[b]) + Kb, SALT_RESAMPLE, V)
             with np.errstate(divide="ignore"):
                 s = np.log(pK) + g
-            out[b, :K] = draft_tokens[b]
-            out[b, K] = argmax_rule(s.astype(np.float32))
+            out[b, :Kb] = draft_tokens[b, :Kb]
+            out[b, Kb] = argmax_rule(s.astype(np.float32))
             smp_margin[b] = top_two_margin(s)
-            final_row[b] = K
+            final_row[b] = Kb
         nacc[b] = n
     return {"out_tokens": out, "num_accepted": nacc, "accept_margin": acc_margin, "sample_margin": smp_margin,
             "near_top_p": near_tp, "final_row": final_row}
