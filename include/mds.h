@@ -59,6 +59,8 @@ extern "C" {
 #define MDS_STATUS_BAD_DRAFT 2u       /* a draft token given to verification was outside [0, V); token 0 was used */
 #define MDS_STATUS_BARRIER_TIMEOUT 4u /* the resident draft kernel gave up waiting at a step barrier; the
                                          draft outputs of that call are invalid */
+#define MDS_STATUS_BAD_INDEX 8u       /* an indexed call met a state slot >= n_slots or a cache row outside
+                                         [0, n_cache_rows); that row was treated as padding */
 
 /* sampling salts: the draft salt is the pages' draft-noise salt (1 << 30) */
 #define MDS_SALT_DRAFT (1u << 30)
@@ -158,6 +160,11 @@ int mds_markov_draft_loop(int B, int K, int V, int r,
  *         q_j is NaN) and when all K are accepted from p_K: Gumbel-max over
  *         log of that distribution plus noise of the MDS_SALT_RESAMPLE
  *         stream keyed (seed_b, P0+j).
+ * A draft token of -1 is a placeholder (PR #65007, Tests: rejection sampling
+ * with -1 placeholder drafts): the request's drafts end at its first -1, and
+ * when all drafts before it are accepted the final token is drawn from p of
+ * that row (the argmax of that row for a greedy request). Any other token
+ * outside [0, V) is out of contract (token 0 is used, MDS_STATUS_BAD_DRAFT).
  * Outputs: out_tokens int32 [B, K+1] = accepted drafts, the final token, then
  * -1 padding; num_accepted int32 [B].
  *
@@ -183,6 +190,61 @@ int mds_rejection_verify(int B, int K, int V,
                          const int64_t* seeds, const int64_t* anchor_pos,
                          int32_t* out_tokens, int32_t* num_accepted,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mds_markov_draft_loop_indexed - mds_markov_draft_loop with the pages'
+ * request-state indexing (DSparkSpeculator API page, _sample_logits and
+ * _sample_markov_chain: per-row idx_map and sample_pos, the cache's
+ * row_mapping; _sample_sequential_sharded: padding slots are inert, with no
+ * draft-logits cache writes).
+ *
+ * Batch row b at step k uses state slot s = idx_map[b*K + k]:
+ *   temperature[s], seeds[s]   its temperature and seed (arrays of n_slots);
+ *   sample_pos[b*K + k]        the position P of the predicted token; the draw
+ *                              is keyed by P - 1 (the plain call's P0 + k);
+ *   cache row                  row_mapping[s] (s itself if row_mapping is NULL)
+ *                              of a [n_cache_rows, K, V] cache, written at
+ *                              column k (strides as in the plain call).
+ * base rows, anchor_tokens, draft_tokens and draft_lse stay batch-indexed.
+ * s < 0 makes the row inert at that step: no cache write, draft token -1,
+ * draft_lse NaN; a later step of that row that is not inert has no previous
+ * token and uses token 0 (MDS_STATUS_BAD_ANCHOR). A slot >= n_slots or a
+ * mapped row outside [0, n_cache_rows) is treated as inert and sets
+ * MDS_STATUS_BAD_INDEX. Always runs the streaming kernels (MDS_DRAFT_PATH=
+ * resident returns MDS_ERR_UNSUPPORTED). Workspace and errors as for
+ * mds_markov_draft_loop.
+ */
+int mds_markov_draft_loop_indexed(int B, int K, int V, int r,
+                                  const void* base, int base_dtype, int64_t base_req_stride, int64_t base_step_stride,
+                                  const void* w1, const void* w2,
+                                  const int32_t* anchor_tokens, const int32_t* idx_map, const int64_t* sample_pos,
+                                  int n_slots, const float* temperature, const int64_t* seeds,
+                                  const int32_t* row_mapping, int n_cache_rows,
+                                  void* cache, int cache_dtype, int64_t cache_row_stride, int64_t cache_step_stride,
+                                  int32_t* draft_tokens, float* draft_lse,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mds_rejection_verify_indexed - mds_rejection_verify with request-state
+ * indexing: request b uses state slot s = idx_map[b] (temperature[s],
+ * seeds[s], top_p[s], arrays of n_slots) and draft-logits cache rows
+ * row_mapping[s] (s itself if row_mapping is NULL) of a [n_cache_rows, K, V]
+ * cache. target rows, draft_tokens, draft_lse, anchor_pos and the outputs
+ * stay batch-indexed. s < 0 is a padding request: nothing is read, every
+ * output token is -1 and num_accepted 0. A slot >= n_slots or a mapped row
+ * outside [0, n_cache_rows) is treated as padding and sets
+ * MDS_STATUS_BAD_INDEX. Workspace: mds_verify_workspace_bytes(B, ...).
+ */
+int mds_rejection_verify_indexed(int B, int K, int V,
+                                 const float* target, int64_t target_row_stride,
+                                 const void* cache, int cache_dtype, int64_t cache_row_stride,
+                                 int64_t cache_step_stride, int n_cache_rows,
+                                 const float* draft_lse, const int32_t* draft_tokens,
+                                 const int32_t* idx_map, int n_slots,
+                                 const float* temperature, const float* top_p, const int64_t* seeds,
+                                 const int32_t* row_mapping, const int64_t* anchor_pos,
+                                 int32_t* out_tokens, int32_t* num_accepted,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * mds_markov_draft_loop_timed - mds_markov_draft_loop that also records

@@ -23,7 +23,7 @@ __all__ = [
 ]
 
 F32, BF16 = 0, 1
-STATUS_BAD_ANCHOR, STATUS_BAD_DRAFT, STATUS_BARRIER_TIMEOUT = 1, 2, 4
+STATUS_BAD_ANCHOR, STATUS_BAD_DRAFT, STATUS_BARRIER_TIMEOUT, STATUS_BAD_INDEX = 1, 2, 4, 8
 SALT_DRAFT, SALT_ACCEPT, SALT_RESAMPLE = 1 << 30, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -53,6 +53,12 @@ _SIGS = {
                                                     ctypes.POINTER(_c_int)], _c_int),
     "mds_rejection_verify": ([_c_int] * 3 + [_vp, _c_i64, _vp, _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp,
                                              _vp, _vp, _vp, _c_sz, _vp], _c_int),
+    "mds_markov_draft_loop_indexed": ([_c_int] * 4 + [_vp, _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _c_int,
+                                                      _vp, _vp, _vp, _c_int, _vp, _c_int, _c_i64, _c_i64, _vp, _vp,
+                                                      _vp, _c_sz, _vp], _c_int),
+    "mds_rejection_verify_indexed": ([_c_int] * 3 + [_vp, _c_i64, _vp, _c_int, _c_i64, _c_i64, _c_int, _vp, _vp, _vp,
+                                                     _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp],
+                                     _c_int),
     "mds_debug_noise": ([_c_int, _vp, _c_i64, _c_i64, ctypes.c_uint32, _vp, _vp, _vp], _c_int),
     "mds_debug_gumbel": ([_c_int, _vp, _vp, _vp], _c_int),
     "mds_debug_top_p": ([_c_int, _c_int, _vp, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp], _c_int),
@@ -230,6 +236,98 @@ def rejection_verify(target, cache, draft_tokens, temperature, seeds, anchor_pos
                                      _ptr(num_accepted), _ptr(workspace), workspace.numel(),
                                      _stream(stream, target.device))
     _check(rc, "rejection_verify")
+    return workspace
+
+
+def markov_draft_loop_indexed(base, w1, w2, anchor_tokens, idx_map, sample_pos, temperature, seeds, cache,
+                              draft_tokens, row_mapping=None, draft_lse=None, workspace=None, stream=None):
+    """Draft loop with request-state indexing (mds_markov_draft_loop_indexed).
+
+    idx_map int32 [B, K] (state slot per row and step, < 0 inert), sample_pos
+    int64 [B, K] (predicted position P; the draw is keyed by P - 1),
+    temperature / seeds [n_slots], row_mapping int32 [n_slots] or None, cache
+    [n_cache_rows, K, V]. base, anchor_tokens, draft_tokens, draft_lse are
+    batch-indexed.
+    """
+    import torch
+    B, K = draft_tokens.shape
+    V = base.shape[2]
+    _need(base.is_cuda and base.dim() == 3 and base.stride(2) == 1 and base.shape[0] == B and base.shape[1] >= K,
+          "base must be a GPU tensor [B, >=K, V] with unit column stride")
+    _need(cache.dim() == 3 and cache.shape[1] == K and cache.shape[2] == V and cache.stride(2) == 1,
+          "cache must be [n_cache_rows, K, V] with unit column stride")
+    _need(w1.dtype == torch.bfloat16 and w2.dtype == torch.bfloat16 and w1.is_contiguous() and w2.is_contiguous()
+          and w1.shape == w2.shape and w1.shape[0] == V, "w1 and w2 must be contiguous bf16 [V, r]")
+    _need(anchor_tokens.dtype == torch.int32 and anchor_tokens.numel() == B and anchor_tokens.is_contiguous(),
+          "anchor_tokens must be int32 [B]")
+    _need(idx_map.dtype == torch.int32 and idx_map.numel() == B * K and idx_map.is_contiguous(),
+          "idx_map must be int32 [B, K]")
+    _need(sample_pos.dtype == torch.int64 and sample_pos.numel() == B * K and sample_pos.is_contiguous(),
+          "sample_pos must be int64 [B, K]")
+    n_slots = temperature.numel()
+    _need(temperature.dtype == torch.float32 and temperature.is_contiguous(), "temperature must be float32 [n_slots]")
+    _need(seeds.dtype == torch.int64 and seeds.numel() == n_slots and seeds.is_contiguous(),
+          "seeds must be int64 [n_slots]")
+    if row_mapping is not None:
+        _need(row_mapping.dtype == torch.int32 and row_mapping.numel() == n_slots and row_mapping.is_contiguous(),
+              "row_mapping must be int32 [n_slots]")
+    _need(draft_tokens.dtype == torch.int32 and draft_tokens.is_contiguous(), "draft_tokens must be int32 [B, K]")
+    if draft_lse is not None:
+        _need(draft_lse.dtype == torch.float32 and draft_lse.is_contiguous() and draft_lse.numel() == B * K,
+              "draft_lse must be float32 [B, K]")
+    if workspace is None:
+        workspace = new_workspace(draft_workspace_bytes(B, K, V, w1.shape[1]), base.device)
+    rc = _lib().mds_markov_draft_loop_indexed(
+        B, K, V, w1.shape[1], _ptr(base), _dtype_code(base), base.stride(0), base.stride(1), _ptr(w1), _ptr(w2),
+        _ptr(anchor_tokens), _ptr(idx_map), _ptr(sample_pos), n_slots, _ptr(temperature), _ptr(seeds),
+        _ptr(row_mapping), cache.shape[0], _ptr(cache), _dtype_code(cache), cache.stride(0), cache.stride(1),
+        _ptr(draft_tokens), _ptr(draft_lse), _ptr(workspace), workspace.numel(), _stream(stream, base.device))
+    _check(rc, "markov_draft_loop_indexed")
+    return workspace
+
+
+def rejection_verify_indexed(target, cache, draft_tokens, idx_map, temperature, seeds, anchor_pos, out_tokens,
+                             num_accepted, row_mapping=None, draft_lse=None, top_p=None, workspace=None,
+                             stream=None):
+    """Verification with request-state indexing (mds_rejection_verify_indexed).
+
+    idx_map int32 [B] (state slot per request, < 0 padding); temperature,
+    seeds, top_p [n_slots]; row_mapping int32 [n_slots] or None; cache
+    [n_cache_rows, K, V].
+    """
+    import torch
+    B, K = draft_tokens.shape
+    V = target.shape[1]
+    _need(target.is_cuda and target.dtype == torch.float32 and target.dim() == 2 and target.shape[0] == B * (K + 1)
+          and target.stride(1) == 1, "target must be float32 [B*(K+1), V] with unit column stride")
+    _need(cache.dim() == 3 and cache.shape[1] == K and cache.shape[2] == V and cache.stride(2) == 1,
+          "cache must be [n_cache_rows, K, V]")
+    _need(idx_map.dtype == torch.int32 and idx_map.numel() == B and idx_map.is_contiguous(), "idx_map must be int32 [B]")
+    n_slots = temperature.numel()
+    _need(temperature.dtype == torch.float32 and temperature.is_contiguous(), "temperature must be float32 [n_slots]")
+    _need(seeds.dtype == torch.int64 and seeds.numel() == n_slots and seeds.is_contiguous(),
+          "seeds must be int64 [n_slots]")
+    if top_p is not None:
+        _need(top_p.dtype == torch.float32 and top_p.numel() == n_slots and top_p.is_contiguous(),
+              "top_p must be float32 [n_slots]")
+    if row_mapping is not None:
+        _need(row_mapping.dtype == torch.int32 and row_mapping.numel() == n_slots and row_mapping.is_contiguous(),
+              "row_mapping must be int32 [n_slots]")
+    _need(out_tokens.dtype == torch.int32 and out_tokens.is_contiguous() and out_tokens.numel() == B * (K + 1),
+          "out_tokens must be int32 [B, K+1]")
+    _need(num_accepted.dtype == torch.int32 and num_accepted.numel() == B, "num_accepted must be int32 [B]")
+    _need(draft_tokens.dtype == torch.int32 and draft_tokens.is_contiguous(), "draft_tokens must be int32 [B, K]")
+    if draft_lse is not None:
+        _need(draft_lse.dtype == torch.float32 and draft_lse.numel() == B * K, "draft_lse: float32 [B, K]")
+    if workspace is None:
+        workspace = new_workspace(verify_workspace_bytes(B, K, V, top_p is not None, draft_lse is not None),
+                                  target.device)
+    rc = _lib().mds_rejection_verify_indexed(
+        B, K, V, _ptr(target), target.stride(0), _ptr(cache), _dtype_code(cache), cache.stride(0), cache.stride(1),
+        cache.shape[0], _ptr(draft_lse), _ptr(draft_tokens), _ptr(idx_map), n_slots, _ptr(temperature), _ptr(top_p),
+        _ptr(seeds), _ptr(row_mapping), _ptr(anchor_pos), _ptr(out_tokens), _ptr(num_accepted), _ptr(workspace),
+        workspace.numel(), _stream(stream, target.device))
+    _check(rc, "rejection_verify_indexed")
     return workspace
 
 

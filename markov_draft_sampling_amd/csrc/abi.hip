@@ -130,20 +130,35 @@ int hip_fail(hipError_t e, const char* where) {
   return fail(MDS_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
 }
 
+// Request-state indexing of a call (all null for the plain entry points).
+struct Indexing {
+  const int32_t* idx_map = nullptr;
+  const int32_t* row_map = nullptr;
+  const int64_t* sample_pos = nullptr;
+  int n_slots = 0, n_rows = 0;
+};
+
+int check_indexing(const Indexing& ix) {
+  if (!ix.idx_map) return MDS_OK;
+  if (ix.n_slots < 1 || ix.n_rows < 1) return fail(MDS_ERR_INVALID_ARG, "n_slots and n_cache_rows must be >= 1");
+  return MDS_OK;
+}
+
 int draft_impl(int B, int K, int V, int r, const void* base, int base_dtype, int64_t base_rs, int64_t base_ss,
                const void* w1, const void* w2, const int32_t* anchor, const int64_t* anchor_pos,
                const float* temperature, const int64_t* seeds, void* cache, int cache_dtype, int64_t cache_rs,
                int64_t cache_ss, int32_t* draft_tokens, float* draft_lse, void* workspace, size_t ws_bytes,
-               void* stream, void* ev_begin, void* ev_end, int* n_launches) {
+               void* stream, void* ev_begin, void* ev_end, int* n_launches, const Indexing& ix = Indexing()) {
   int rc;
-  if ((rc = check_sizes(B, K, V)) || (rc = check_rank(r))) return rc;
-  if (!base || !w1 || !w2 || !anchor || !anchor_pos || !temperature || !seeds || !cache || !draft_tokens ||
-      !workspace)
+  if ((rc = check_sizes(B, K, V)) || (rc = check_rank(r)) || (rc = check_indexing(ix))) return rc;
+  if (!base || !w1 || !w2 || !anchor || (!anchor_pos && !ix.sample_pos) || !temperature || !seeds || !cache ||
+      !draft_tokens || !workspace)
     return fail(MDS_ERR_INVALID_ARG, "a required pointer is NULL");
   if ((base_dtype != MDS_F32 && base_dtype != MDS_BF16) || (cache_dtype != MDS_F32 && cache_dtype != MDS_BF16))
     return fail(MDS_ERR_INVALID_ARG, "dtype must be MDS_F32 or MDS_BF16");
   if (base_rs < 0 || base_ss < 0) return fail(MDS_ERR_INVALID_ARG, "base strides must be >= 0");
-  if (!rows_disjoint(B, K, V, cache_rs, cache_ss))
+  const int n_rows = ix.idx_map ? ix.n_rows : B;
+  if (!rows_disjoint(n_rows, K, V, cache_rs, cache_ss))
     return fail(MDS_ERR_INVALID_ARG, "cache strides make rows overlap or are shorter than V");
   if (!aligned(w1, 16) || !aligned(w2, 16)) return fail(MDS_ERR_INVALID_ARG, "w1 and w2 must be 16-byte aligned");
   if (!aligned(workspace, kAlign)) return fail(MDS_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
@@ -178,8 +193,16 @@ int draft_impl(int B, int K, int V, int r, const void* base, int base_dtype, int
   a.status = (uint32_t*)ws;
   a.bar = (unsigned*)(ws + L.bar);
   a.abort_flag = a.bar + K;
+  a.idx_map = ix.idx_map;
+  a.row_map = ix.idx_map ? ix.row_map : nullptr;
+  a.sample_pos = (const long long*)ix.sample_pos;
+  a.n_slots = ix.idx_map ? ix.n_slots : B;
+  a.n_rows = n_rows;
   const int choice = draft_path_choice();
   if (choice < 0) return fail(MDS_ERR_INVALID_ARG, "MDS_DRAFT_PATH must be auto, stream or resident");
+  const bool indexed = ix.idx_map || ix.sample_pos;
+  if (choice == 2 && indexed)
+    return fail(MDS_ERR_UNSUPPORTED, "the resident draft kernel does not take request-state indexing");
   int dev = 0, cus = 0, lds_max = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -187,7 +210,7 @@ int draft_impl(int B, int K, int V, int r, const void* base, int base_dtype, int
   if (e != hipSuccess) return hip_fail(e, "device query");
   int n_lds = 0;
   size_t res_lds = 0;
-  const bool resident = choice != 1 && cus <= mds::kDraftMaxSlabs &&
+  const bool resident = choice != 1 && !indexed && cus <= mds::kDraftMaxSlabs &&
                         mds::draft_resident_plan(V, r, cus, (size_t)lds_max, &n_lds, &res_lds) == hipSuccess;
   if (choice == 2 && !resident) return fail(MDS_ERR_UNSUPPORTED, "w2 does not fit on chip for the resident kernel");
   const bool wave_kernel = !resident && r <= 256;
@@ -206,8 +229,64 @@ int draft_impl(int B, int K, int V, int r, const void* base, int base_dtype, int
   }
   if (ev_end && (e = hipEventRecord((hipEvent_t)ev_end, st)) != hipSuccess) return hip_fail(e, "event record");
   if (n_launches) *n_launches = resident ? 1 : K;
-  mds::DraftFinalArgs f{B, K, a.G, a.keys, a.qpart, temperature, draft_tokens, draft_lse};
+  mds::DraftFinalArgs f{B, K, a.G, a.keys, a.qpart, temperature, draft_tokens, draft_lse,
+                        a.idx_map, a.row_map, a.n_slots, a.n_rows};
   if ((e = mds::launch_draft_finalize(f, st)) != hipSuccess) return hip_fail(e, "draft finalize launch");
+  return ok();
+}
+
+int verify_impl(int B, int K, int V, const float* target, int64_t target_row_stride, const void* cache,
+                int cache_dtype, int64_t cache_req_stride, int64_t cache_step_stride, const float* draft_lse,
+                const int32_t* draft_tokens, const float* temperature, const float* top_p, const int64_t* seeds,
+                const int64_t* anchor_pos, int32_t* out_tokens, int32_t* num_accepted, void* workspace,
+                size_t workspace_bytes, void* stream, const Indexing& ix) {
+  int rc;
+  if ((rc = check_sizes(B, K, V)) || (rc = check_indexing(ix))) return rc;
+  if (!target || !cache || !draft_tokens || !temperature || !seeds || !anchor_pos || !out_tokens || !num_accepted ||
+      !workspace)
+    return fail(MDS_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (cache_dtype != MDS_F32 && cache_dtype != MDS_BF16)
+    return fail(MDS_ERR_INVALID_ARG, "cache dtype must be MDS_F32 or MDS_BF16");
+  if (target_row_stride < V) return fail(MDS_ERR_INVALID_ARG, "target_row_stride must be >= V");
+  if (cache_req_stride < 0 || cache_step_stride < 0) return fail(MDS_ERR_INVALID_ARG, "cache strides must be >= 0");
+  const int n_rows = ix.idx_map ? ix.n_rows : B;
+  if (!aligned(workspace, kAlign)) return fail(MDS_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const VerifyLayout L = verify_layout(B, K, V, top_p != nullptr, draft_lse != nullptr);
+  if (workspace_bytes < L.total) return fail(MDS_ERR_WORKSPACE, "workspace too small for verification");
+  unsigned char* ws = (unsigned char*)workspace;
+  hipStream_t st = (hipStream_t)stream;
+  mds::VerifyArgs a{};
+  a.B = B;
+  a.K = K;
+  a.V = V;
+  a.target = target;
+  a.target_rs = target_row_stride;
+  a.vec_target = aligned(target, 16) && target_row_stride % 4 == 0;
+  a.cache = cache;
+  a.cache_bf16 = cache_dtype == MDS_BF16;
+  a.vec_cache = vec_ok(cache, cache_dtype, cache_req_stride, cache_step_stride);
+  a.cache_rs = cache_req_stride;
+  a.cache_ss = cache_step_stride;
+  a.draft_lse = draft_lse;
+  a.draft = draft_tokens;
+  a.temp = temperature;
+  a.top_p = top_p;
+  a.seeds = (const long long*)seeds;
+  a.anchor_pos = (const long long*)anchor_pos;
+  a.out_tokens = out_tokens;
+  a.num_accepted = num_accepted;
+  verify_workspace_args(a, ws, L, top_p != nullptr, draft_lse != nullptr);
+  a.idx_map = ix.idx_map;
+  a.row_map = ix.idx_map ? ix.row_map : nullptr;
+  a.n_slots = ix.idx_map ? ix.n_slots : B;
+  a.n_rows = n_rows;
+  hipError_t e;
+  if ((e = mds::launch_verify_stats(a, st)) != hipSuccess) return hip_fail(e, "verify stats launch");
+  if (top_p) {
+    if ((e = mds::launch_top_p(a, st)) != hipSuccess) return hip_fail(e, "top-p launch");
+    if ((e = mds::launch_decide(a, st)) != hipSuccess) return hip_fail(e, "decide launch");
+  }
+  if ((e = mds::launch_residual(a, st)) != hipSuccess) return hip_fail(e, "residual launch");
   return ok();
 }
 
@@ -301,49 +380,46 @@ int mds_rejection_verify(int B, int K, int V, const float* target, int64_t targe
                          const float* draft_lse, const int32_t* draft_tokens, const float* temperature,
                          const float* top_p, const int64_t* seeds, const int64_t* anchor_pos, int32_t* out_tokens,
                          int32_t* num_accepted, void* workspace, size_t workspace_bytes, void* stream) {
-  int rc;
-  if ((rc = check_sizes(B, K, V))) return rc;
-  if (!target || !cache || !draft_tokens || !temperature || !seeds || !anchor_pos || !out_tokens || !num_accepted ||
-      !workspace)
-    return fail(MDS_ERR_INVALID_ARG, "a required pointer is NULL");
-  if (cache_dtype != MDS_F32 && cache_dtype != MDS_BF16)
-    return fail(MDS_ERR_INVALID_ARG, "cache dtype must be MDS_F32 or MDS_BF16");
-  if (target_row_stride < V) return fail(MDS_ERR_INVALID_ARG, "target_row_stride must be >= V");
-  if (cache_req_stride < 0 || cache_step_stride < 0) return fail(MDS_ERR_INVALID_ARG, "cache strides must be >= 0");
-  if (!aligned(workspace, kAlign)) return fail(MDS_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  const VerifyLayout L = verify_layout(B, K, V, top_p != nullptr, draft_lse != nullptr);
-  if (workspace_bytes < L.total) return fail(MDS_ERR_WORKSPACE, "workspace too small for verification");
-  unsigned char* ws = (unsigned char*)workspace;
-  hipStream_t st = (hipStream_t)stream;
-  mds::VerifyArgs a{};
-  a.B = B;
-  a.K = K;
-  a.V = V;
-  a.target = target;
-  a.target_rs = target_row_stride;
-  a.vec_target = aligned(target, 16) && target_row_stride % 4 == 0;
-  a.cache = cache;
-  a.cache_bf16 = cache_dtype == MDS_BF16;
-  a.vec_cache = vec_ok(cache, cache_dtype, cache_req_stride, cache_step_stride);
-  a.cache_rs = cache_req_stride;
-  a.cache_ss = cache_step_stride;
-  a.draft_lse = draft_lse;
-  a.draft = draft_tokens;
-  a.temp = temperature;
-  a.top_p = top_p;
-  a.seeds = (const long long*)seeds;
-  a.anchor_pos = (const long long*)anchor_pos;
-  a.out_tokens = out_tokens;
-  a.num_accepted = num_accepted;
-  verify_workspace_args(a, ws, L, top_p != nullptr, draft_lse != nullptr);
-  hipError_t e;
-  if ((e = mds::launch_verify_stats(a, st)) != hipSuccess) return hip_fail(e, "verify stats launch");
-  if (top_p) {
-    if ((e = mds::launch_top_p(a, st)) != hipSuccess) return hip_fail(e, "top-p launch");
-    if ((e = mds::launch_decide(a, st)) != hipSuccess) return hip_fail(e, "decide launch");
-  }
-  if ((e = mds::launch_residual(a, st)) != hipSuccess) return hip_fail(e, "residual launch");
-  return ok();
+  return verify_impl(B, K, V, target, target_row_stride, cache, cache_dtype, cache_req_stride, cache_step_stride,
+                     draft_lse, draft_tokens, temperature, top_p, seeds, anchor_pos, out_tokens, num_accepted,
+                     workspace, workspace_bytes, stream, Indexing());
+}
+
+int mds_rejection_verify_indexed(int B, int K, int V, const float* target, int64_t target_row_stride,
+                                 const void* cache, int cache_dtype, int64_t cache_row_stride,
+                                 int64_t cache_step_stride, int n_cache_rows, const float* draft_lse,
+                                 const int32_t* draft_tokens, const int32_t* idx_map, int n_slots,
+                                 const float* temperature, const float* top_p, const int64_t* seeds,
+                                 const int32_t* row_mapping, const int64_t* anchor_pos, int32_t* out_tokens,
+                                 int32_t* num_accepted, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!idx_map) return fail(MDS_ERR_INVALID_ARG, "idx_map is NULL");
+  Indexing ix;
+  ix.idx_map = idx_map;
+  ix.row_map = row_mapping;
+  ix.n_slots = n_slots;
+  ix.n_rows = n_cache_rows;
+  return verify_impl(B, K, V, target, target_row_stride, cache, cache_dtype, cache_row_stride, cache_step_stride,
+                     draft_lse, draft_tokens, temperature, top_p, seeds, anchor_pos, out_tokens, num_accepted,
+                     workspace, workspace_bytes, stream, ix);
+}
+
+int mds_markov_draft_loop_indexed(int B, int K, int V, int r, const void* base, int base_dtype,
+                                  int64_t base_req_stride, int64_t base_step_stride, const void* w1, const void* w2,
+                                  const int32_t* anchor_tokens, const int32_t* idx_map, const int64_t* sample_pos,
+                                  int n_slots, const float* temperature, const int64_t* seeds,
+                                  const int32_t* row_mapping, int n_cache_rows, void* cache, int cache_dtype,
+                                  int64_t cache_row_stride, int64_t cache_step_stride, int32_t* draft_tokens,
+                                  float* draft_lse, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!idx_map || !sample_pos) return fail(MDS_ERR_INVALID_ARG, "idx_map and sample_pos must not be NULL");
+  Indexing ix;
+  ix.idx_map = idx_map;
+  ix.row_map = row_mapping;
+  ix.sample_pos = sample_pos;
+  ix.n_slots = n_slots;
+  ix.n_rows = n_cache_rows;
+  return draft_impl(B, K, V, r, base, base_dtype, base_req_stride, base_step_stride, w1, w2, anchor_tokens, nullptr,
+                    temperature, seeds, cache, cache_dtype, cache_row_stride, cache_step_stride, draft_tokens,
+                    draft_lse, workspace, workspace_bytes, stream, nullptr, nullptr, nullptr, ix);
 }
 
 int mds_debug_noise(int n, const int32_t* cols, int64_t seed, int64_t pos_key, uint32_t salt, uint32_t* words,

@@ -164,18 +164,20 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftStepArgs a) {
     erow[e] = j / (kCW / 4);
     ecol[e] = (j % (kCW / 4)) * 4;
     const int b = b0 + erow[e];
-    ev[e] = b < a.B;
-    const int bb = ev[e] ? b : 0;
-    Tv[e] = a.temp[bb];
+    const int sl = draft_slot(a, b);  // -1: past the batch or inert at this step
+    ev[e] = sl >= 0;
+    const int bb = b < a.B ? b : 0;
+    const int ss = ev[e] ? sl : 0;
+    Tv[e] = a.temp[ss];
     invT[e] = Tv[e] > 0.0f ? 1.0f / Tv[e] : 0.0f;
-    const unsigned long long sd = (unsigned long long)a.seeds[bb];
-    const unsigned long long pk = (unsigned long long)(a.anchor_pos[bb] + k);
+    const unsigned long long sd = (unsigned long long)a.seeds[ss];
+    const unsigned long long pk = (unsigned long long)draft_pos_key(a, bb);
     sk0[e] = (uint32_t)sd;
     sk1[e] = (uint32_t)(sd >> 32);
     pk0[e] = (uint32_t)pk;
     pk1[e] = (uint32_t)(pk >> 32);
     rbase[e] = (long long)bb * a.base_rs + (long long)k * a.base_ss;
-    rcache[e] = (long long)bb * a.cache_rs + (long long)k * a.cache_ss;
+    rcache[e] = (long long)(ev[e] ? draft_cache_row(a, b, sl) : 0) * a.cache_rs + (long long)k * a.cache_ss;
   }
   float bv[EPT], qm[EPT], qs[EPT];
   int bi[EPT];
@@ -254,9 +256,9 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftStepArgs a) {
   // previous token of every request of the tile
   for (int i = tid; i < NB; i += 256) {
     const int b = b0 + i;
-    int prev = 0;
-    if (b < a.B) {
-      long long t = (k == 0) ? (long long)a.anchor[b] : (long long)win_col(a.keys[(size_t)(k - 1) * a.B + b]);
+    int prev = -1;  // rows that are not served get a zero embedding
+    if (draft_slot(a, b) >= 0) {
+      long long t = (k == 0) ? (long long)a.anchor[b] : (long long)(int32_t)win_col(a.keys[(size_t)(k - 1) * a.B + b]);
       if (t < 0 || t >= V) {
         set_status(a.status, kStatusBadAnchor);
         t = 0;
@@ -266,11 +268,11 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftStepArgs a) {
     s_prev[i] = prev;
   }
   __syncthreads();
-  // Markov embeddings w1[prev] -> LDS (zero rows past the batch)
+  // Markov embeddings w1[prev] -> LDS
   for (int i = tid; i < NB * cpr; i += 256) {
     const int row = i / cpr, ch = i - row * cpr;
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (b0 + row < a.B) v = *(const u32x4*)(a.w1 + (size_t)s_prev[row] * r + ch * 8);
+    if (s_prev[row] >= 0) v = *(const u32x4*)(a.w1 + (size_t)s_prev[row] * r + ch * 8);
     *(u32x4*)(s_e + row * rs + ch * 8) = v;
   }
 
@@ -386,7 +388,7 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftStepArgs a) {
   __syncthreads();
   for (int i = tid; i < NB; i += 256) {
     const int b = b0 + i;
-    if (b >= a.B) continue;
+    if (draft_slot(a, b) < 0) continue;  // no winner and no partial for rows that are not served
     const unsigned long long key = s_key[i];
     if (key) atomicMax(&a.keys[(size_t)k * a.B + b], key);
     a.qpart[((size_t)k * a.B + b) * a.G + g] = make_float2(s_qm[i], s_qs[i]);
@@ -406,8 +408,14 @@ __global__ __launch_bounds__(256) void draft_finalize_kernel(DraftFinalArgs a) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= a.B * a.K) return;
   const int b = row / a.K, k = row - b * a.K;
+  // inert rows keep key 0, i.e. token -1
   if (lane == 0) a.tokens[row] = (int32_t)win_col(a.keys[(size_t)k * a.B + b]);
   if (!a.lse) return;
+  const int sl = draft_slot(a.idx_map, a.row_map, a.B, a.K, a.n_slots, a.n_rows, nullptr, b, k);
+  if (sl < 0) {
+    if (lane == 0) a.lse[row] = NAN;
+    return;
+  }
   float m = -INFINITY, s = 0.0f;
   const float2* qp = a.qpart + ((size_t)k * a.B + b) * a.G;
   for (int i = lane; i < a.G; i += 64) {
@@ -417,7 +425,7 @@ __global__ __launch_bounds__(256) void draft_finalize_kernel(DraftFinalArgs a) {
   wave_lse_merge(m, s);
   if (lane == 0) {
     float out;
-    if (!(a.temp[b] > 0.0f) || s != s)
+    if (!(a.temp[sl] > 0.0f) || s != s)
       out = NAN;
     else
       out = m + __logf(s);

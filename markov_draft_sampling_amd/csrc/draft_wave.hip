@@ -71,18 +71,20 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int b = b0 + nt * 16 + lr;
-    valid[nt] = b < a.B;
-    const int bb = valid[nt] ? b : a.B - 1;
-    Tv[nt] = a.temp[bb];
+    const int sl = draft_slot(a, b);  // -1: past the batch or inert at this step
+    valid[nt] = sl >= 0;
+    const int bb = b < a.B ? b : a.B - 1;
+    const int ss = valid[nt] ? sl : 0;  // a readable slot for rows that are not served
+    Tv[nt] = a.temp[ss];
     invT[nt] = Tv[nt] > 0.0f ? 1.0f / Tv[nt] : 0.0f;
-    const unsigned long long sd = (unsigned long long)a.seeds[bb];
-    const unsigned long long pk = (unsigned long long)(a.anchor_pos[bb] + k);
+    const unsigned long long sd = (unsigned long long)a.seeds[ss];
+    const unsigned long long pk = (unsigned long long)draft_pos_key(a, bb);
     sk0[nt] = (uint32_t)sd;
     sk1[nt] = (uint32_t)(sd >> 32);
     pk0[nt] = (uint32_t)pk;
     pk1[nt] = (uint32_t)(pk >> 32);
     rbase[nt] = (long long)bb * a.base_rs + (long long)k * a.base_ss;
-    rcache[nt] = (long long)bb * a.cache_rs + (long long)k * a.cache_ss;
+    rcache[nt] = (long long)(valid[nt] ? draft_cache_row(a, b, sl) : 0) * a.cache_rs + (long long)k * a.cache_ss;
   }
 
   // Tile loaders. w2 rows past V are read from row V - 1: they only feed
@@ -141,9 +143,10 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
   const int cpr = r >> 3;  // 16-byte chunks per embedding row
   for (int i = tid; i < NB; i += 256) {
     const int b = b0 + i;
-    int prev = 0;
-    if (b < a.B) {
-      long long tk = (k == 0) ? (long long)a.anchor[b] : (long long)win_col(a.keys[(size_t)(k - 1) * a.B + b]);
+    int prev = -1;  // rows that are not served get a zero embedding
+    if (draft_slot(a, b) >= 0) {
+      // the previous step's winner (key 0, i.e. -1, when that step was inert)
+      long long tk = (k == 0) ? (long long)a.anchor[b] : (long long)(int32_t)win_col(a.keys[(size_t)(k - 1) * a.B + b]);
       if (tk < 0 || tk >= V) {
         set_status(a.status, kStatusBadAnchor);
         tk = 0;
@@ -153,11 +156,11 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
     s_prev[i] = prev;
   }
   __syncthreads();
-  // Markov embeddings w1[prev] -> LDS (zero rows past the batch)
+  // Markov embeddings w1[prev] -> LDS
   for (int i = tid; i < NB * cpr; i += 256) {
     const int row = i / cpr, ch = i - row * cpr;
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (b0 + row < a.B) v = *(const u32x4*)(a.w1 + (size_t)s_prev[row] * r + ch * 8);
+    if (s_prev[row] >= 0) v = *(const u32x4*)(a.w1 + (size_t)s_prev[row] * r + ch * 8);
     *(u32x4*)(s_e + row * rs + ch * 8) = v;
   }
   __syncthreads();
@@ -185,7 +188,10 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
     all_sampled &= Tv[nt] > 0.0f;
     all_t1 &= Tv[nt] == 1.0f;
   }
-  const bool fast_req = b0 + NB <= a.B && a.vec_cache && __all(all_sampled);
+  bool all_valid = true;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) all_valid &= valid[nt];
+  const bool fast_req = a.vec_cache && __all(all_sampled && all_valid);
   const bool t1 = __all(all_t1);
 
   for (int t = t_first; t < mt_end; t += 4) {
@@ -364,7 +370,7 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
   __syncthreads();
   for (int i = tid; i < NB; i += 256) {
     const int b = b0 + i;
-    if (b >= a.B) continue;
+    if (draft_slot(a, b) < 0) continue;  // no winner and no partial for rows that are not served
     unsigned long long key = s_key[i];
     float m = s_qm[i], s = s_qs[i];
 #pragma unroll

@@ -21,6 +21,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kStatusBadAnchor = 1u;
 constexpr uint32_t kStatusBadDraft = 2u;
+constexpr uint32_t kStatusBadIndex = 8u;
 constexpr uint32_t kSaltDraft = 1u << 30;
 constexpr uint32_t kSaltAccept = 1u;
 constexpr uint32_t kSaltResample = 2u;

@@ -31,6 +31,11 @@ struct DraftStepArgs {
   unsigned* abort_flag;      // set when a barrier wait times out (resident kernel)
   int n_lds_tiles;           // resident kernel: LDS tiles per work-group (max)
   int zero;                  // always 0 (an offset the compiler cannot fold)
+  // request-state indexing (all null / B for the plain call)
+  const int32_t* idx_map;    // [B][K] state slot of row b at step k, < 0 inert; null: slot = b
+  const int32_t* row_map;    // [n_slots] cache row of a slot; null: row = slot
+  const long long* sample_pos;  // [B][K] predicted position P (draw keyed by P - 1); null: anchor_pos + k
+  int n_slots, n_rows;
 };
 
 struct DraftFinalArgs {
@@ -40,7 +45,38 @@ struct DraftFinalArgs {
   const float* temp;
   int32_t* tokens;
   float* lse;
+  const int32_t* idx_map;
+  const int32_t* row_map;
+  int n_slots, n_rows;
 };
+
+// The state slot of batch row b at draft step k, or -1 when the row is inert
+// there (past the batch, a negative slot, or a slot / cache row out of range,
+// the last two flagged in the status word).
+__device__ __forceinline__ int draft_slot(const int32_t* idx_map, const int32_t* row_map, int B, int K, int n_slots,
+                                          int n_rows, uint32_t* status, int b, int k) {
+  if (b >= B) return -1;
+  if (!idx_map) return b;
+  const int s = idx_map[(size_t)b * K + k];
+  if (s < 0) return -1;
+  const int row = s < n_slots ? (row_map ? row_map[s] : s) : -1;
+  if (row < 0 || row >= n_rows) {
+    if (status) atomicOr(status, 8u);
+    return -1;
+  }
+  return s;
+}
+__device__ __forceinline__ int draft_slot(const DraftStepArgs& a, int b) {
+  return draft_slot(a.idx_map, a.row_map, a.B, a.K, a.n_slots, a.n_rows, a.status, b, a.k);
+}
+// cache row of a live slot s of batch row b
+__device__ __forceinline__ int draft_cache_row(const DraftStepArgs& a, int b, int s) {
+  return !a.idx_map ? b : (a.row_map ? a.row_map[s] : s);
+}
+// key of the draw of batch row b (< B) at step k: the position before the predicted token
+__device__ __forceinline__ long long draft_pos_key(const DraftStepArgs& a, int b) {
+  return a.sample_pos ? a.sample_pos[(size_t)b * a.K + a.k] - 1 : a.anchor_pos[b] + a.k;
+}
 
 int draft_nb(int B, int r);
 int draft_slabs(int V, int cus);
@@ -127,7 +163,28 @@ struct VerifyArgs {
   int vec_target;
   int decide;                 // the statistics pass also takes the accept decision (no top-p)
   int NR;                     // residual blocks per request (kResCols columns each)
+  // request-state indexing (null / B for the plain call)
+  const int32_t* idx_map;     // [B] state slot of request b, < 0 padding; null: slot = b
+  const int32_t* row_map;     // [n_slots] cache row of a slot; null: row = slot
+  int n_slots, n_rows;
 };
+
+// The state slot of request b, or -1 for a padding request (a negative slot,
+// or a slot / cache row out of range, the latter flagged in the status word).
+__device__ __forceinline__ int verify_slot(const VerifyArgs& a, int b) {
+  if (!a.idx_map) return b;
+  const int s = a.idx_map[b];
+  if (s < 0) return -1;
+  const int row = s < a.n_slots ? (a.row_map ? a.row_map[s] : s) : -1;
+  if (row < 0 || row >= a.n_rows) {
+    if (a.status) atomicOr(a.status, 8u);
+    return -1;
+  }
+  return s;
+}
+__device__ __forceinline__ int verify_cache_row(const VerifyArgs& a, int b, int s) {
+  return !a.idx_map ? b : (a.row_map ? a.row_map[s] : s);
+}
 
 constexpr int kResCols = 2048;  // columns per residual work-group
 

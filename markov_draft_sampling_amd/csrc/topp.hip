@@ -98,8 +98,9 @@ __global__ __launch_bounds__(kTp) void top_p_kernel(VerifyArgs a) {
 
   const int row = blockIdx.x;
   const int b = row / (a.K + 1);
-  const float T = a.temp[b];
-  const float p = a.top_p[b];
+  const int sl = verify_slot(a, b);
+  const float T = sl >= 0 ? a.temp[sl] : 0.0f;  // padding requests: off
+  const float p = sl >= 0 ? a.top_p[sl] : 1.0f;
   TopP* out = a.topp + row;
   if (!(T > 0.0f) || !(p < 1.0f)) {
     if (threadIdx.x == 0) *out = TopP{0u, 0, 0.0f, 0};

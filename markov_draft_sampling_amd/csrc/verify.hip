@@ -168,16 +168,33 @@ struct ReqLds {
   float tx[kMaxK], cx[kMaxK];  // target and cache logits at the draft tokens
 };
 
-// Draft token k of request b and the target / cache logits at it. A token
-// outside [0, V) is replaced by 0 and flagged in the status word.
-__device__ __forceinline__ void draft_point(const VerifyArgs& a, int b, int k, int& x, float& tx, float& cx) {
+// Draft token k of request b (state slot s) and the target / cache logits at
+// it. -1 is a placeholder (no draft from here on; the logits are not read);
+// any other token outside [0, V) is replaced by 0 and flagged in the status
+// word.
+__device__ __forceinline__ void draft_point(const VerifyArgs& a, int b, int s, int k, int& x, float& tx, float& cx) {
   x = a.draft[b * a.K + k];
+  tx = cx = 0.0f;
+  if (x == -1) return;
   if (x < 0 || x >= a.V) {
     set_status(a.status, kStatusBadDraft);
     x = 0;
   }
   tx = a.target[(long long)(b * (a.K + 1) + k) * a.target_rs + x];
-  cx = load_f32_or_bf16(a.cache, (long long)b * a.cache_rs + (long long)k * a.cache_ss + x, a.cache_bf16);
+  cx = load_f32_or_bf16(a.cache, (long long)verify_cache_row(a, b, s) * a.cache_rs + (long long)k * a.cache_ss + x,
+                        a.cache_bf16);
+}
+
+// A padding request: every output token -1, none accepted, no residual draw.
+__device__ void finish_padding(const VerifyArgs& a, int b) {
+  const int lane = threadIdx.x & 63;
+  if (lane <= a.K) a.out_tokens[(size_t)b * (a.K + 1) + lane] = -1;
+  if (lane == 0) {
+    a.num_accepted[b] = 0;
+    ReqState r{};
+    r.mode = 2;
+    a.req[b] = r;
+  }
 }
 
 constexpr int kStage = 1024;  // partials a combining wave stages in LDS at a time
@@ -263,13 +280,17 @@ __device__ void wave_combine(const unsigned long long* p, size_t cstride, int nr
 // run), then ReqState for the residual draw. Greedy requests are finished
 // here: the final token is the argmax of row n_acc. Run by one wave with L
 // filled.
-__device__ void decide(const VerifyArgs& a, int b, ReqLds& L) {
+__device__ void decide(const VerifyArgs& a, int b, int sl, ReqLds& L) {
   const int K = a.K, V = a.V;
   const int lane = threadIdx.x & 63;
-  const float T = a.temp[b];
+  const float T = a.temp[sl];
   const bool greedy = !(T > 0.0f);
   const float invT = greedy ? 1.0f : 1.0f / T;
-  if (lane < K) {
+  // the drafts end at the first -1 placeholder
+  int mb = K;
+  for (int k = K - 1; k >= 0; --k)
+    if (L.x[k] == -1) mb = k;
+  if (lane < mb) {
     const int k = lane;
     const int x = L.x[k];
     bool ok;
@@ -282,7 +303,7 @@ __device__ void decide(const VerifyArgs& a, int b, ReqLds& L) {
       if (!a.topp || kept(a.topp[row], tx, x)) logp = div_t(tx, T, invT) - L.m[k] - L.lz[k];
       const float p = expf(logp);
       const float q = expf(div_t(L.cx[k], T, invT) - L.lq[k]);
-      const unsigned long long sd = (unsigned long long)a.seeds[b];
+      const unsigned long long sd = (unsigned long long)a.seeds[sl];
       const unsigned long long pk = (unsigned long long)(a.anchor_pos[b] + k);
       const Philox4 w = philox4x32_10(0u, (uint32_t)pk, (uint32_t)(pk >> 32), kSaltAccept, (uint32_t)sd,
                                       (uint32_t)(sd >> 32));
@@ -293,7 +314,7 @@ __device__ void decide(const VerifyArgs& a, int b, ReqLds& L) {
   }
   wave_lds_sync();
   int n = 0;
-  while (n < K && L.acc[n]) ++n;
+  while (n < mb && L.acc[n]) ++n;
   if (greedy && lane <= K) {
     const int i = lane;
     int v = -1;
@@ -308,7 +329,7 @@ __device__ void decide(const VerifyArgs& a, int b, ReqLds& L) {
   if (lane == 0) {
     ReqState r;
     r.n_acc = n;
-    r.mode = greedy ? 2 : (n < K ? ((L.lq[n] != L.lq[n]) ? 3 : 1) : 0);
+    r.mode = greedy ? 2 : (n < mb ? ((L.lq[n] != L.lq[n]) ? 3 : 1) : 0);
     r.M = L.m[n];
     r.LZ = L.lz[n];
     r.LQ = r.mode == 1 ? L.lq[n] : 0.0f;
@@ -324,10 +345,15 @@ __device__ void decide(const VerifyArgs& a, int b, ReqLds& L) {
 // Run by wave 0 of the last work-group of request b: combine every partial of
 // the request, write the row statistics and, without top-p, decide. Resets
 // the request's counter.
-__device__ void combine_request(const VerifyArgs& a, int b, ReqLds& L, unsigned long long* stage) {
+__device__ void combine_request(const VerifyArgs& a, int b, int sl, ReqLds& L, unsigned long long* stage) {
   const int K = a.K, NC = a.NC;
   const int lane = threadIdx.x & 63;
-  const bool greedy = !(a.temp[b] > 0.0f);
+  if (sl < 0) {  // padding request: nothing was published
+    if (lane == 0) atomicExch(a.cnt + verify_counter_index(b), 0u);
+    if (a.decide) finish_padding(a, b);
+    return;
+  }
+  const bool greedy = !(a.temp[sl] > 0.0f);
   // the draft tokens, and the logits at them that block 0 of each target row
   // published, load together with the partials
   if (lane < K) {
@@ -336,7 +362,7 @@ __device__ void combine_request(const VerifyArgs& a, int b, ReqLds& L, unsigned 
       L.x[lane] = x;
     } else {
       const unsigned long long w = __hip_atomic_load(a.tq + b * K + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      L.x[lane] = (x < 0 || x >= a.V) ? 0 : x;
+      L.x[lane] = (x == -1) ? -1 : ((x < 0 || x >= a.V) ? 0 : x);
       L.tx[lane] = unpack_m(w);
       L.cx[lane] = unpack_s(w);
     }
@@ -363,7 +389,7 @@ __device__ void combine_request(const VerifyArgs& a, int b, ReqLds& L, unsigned 
   }
   if (lane == 0) atomicExch(a.cnt + verify_counter_index(b), 0u);
   wave_lds_sync();
-  if (a.decide) decide(a, b, L);
+  if (a.decide) decide(a, b, sl, L);
 }
 
 // Grid (NC, rows) with rows = B(K+1) target rows, then B*K cache rows when
@@ -382,13 +408,14 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(VerifyArgs a) {
   const int c0 = chunk * kStatsChunk;
   unsigned long long* slot = nullptr;
   unsigned long long word = 0ull;
-  if (is_target) {
+  const int sl = verify_slot(a, b);  // -1: padding request (its blocks only arrive)
+  if (is_target && sl >= 0) {
     // the row's loads go out first: nothing about them depends on T, and a
     // branch on T placed above them would hold them behind the load of T
     float v[kPerThread];
     load_block<false>(a.target + (long long)row * a.target_rs, V, c0, a.vec_target != 0, 0.0f, v);
     asm volatile("" ::: "memory");
-    const float T = a.temp[b];
+    const float T = a.temp[sl];
     const bool greedy = !(T > 0.0f);
     if (greedy) {
       word = block_max_key(thread_key(v, c0, V));
@@ -399,10 +426,10 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(VerifyArgs a) {
       word = pack_ms(m, s);
     }
     slot = a.tpart + (size_t)chunk * n_t + row;
-  } else if (a.temp[b] > 0.0f) {
-    const float T = a.temp[b];
+  } else if (!is_target && sl >= 0 && a.temp[sl] > 0.0f) {
+    const float T = a.temp[sl];
     const int q = row - n_t, k = q - b * K;
-    const long long off = (long long)b * a.cache_rs + (long long)k * a.cache_ss;
+    const long long off = (long long)verify_cache_row(a, b, sl) * a.cache_rs + (long long)k * a.cache_ss;
     float v[kPerThread];
     if (a.cache_bf16)
       load_block<true>((const uint16_t*)a.cache + off, V, c0, a.vec_cache != 0, 0.0f, v);
@@ -426,10 +453,10 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(VerifyArgs a) {
     // block 0 of target row k < K of a sampled request also publishes the
     // target and cache logits at draft token k, for the accept test
     const int k = row - b * (K + 1);
-    if (is_target && chunk == 0 && k < K && a.temp[b] > 0.0f) {
+    if (is_target && chunk == 0 && k < K && sl >= 0 && a.temp[sl] > 0.0f) {
       int x;
       float tx, cx;
-      draft_point(a, b, k, x, tx, cx);
+      draft_point(a, b, sl, k, x, tx, cx);
       const unsigned long long prev = atomicExch(a.tq + b * K + k, pack_ms(tx, cx));
       asm volatile("" ::"v"(prev));
     }
@@ -439,7 +466,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(VerifyArgs a) {
   }
   last = __shfl(last, 0);
   if (!last) return;
-  combine_request(a, b, L, stage);
+  combine_request(a, b, sl, L, stage);
 }
 
 // With top-p: one wave per request after the top-p kernel.
@@ -447,6 +474,11 @@ __global__ __launch_bounds__(64) void decide_kernel(VerifyArgs a) {
   __shared__ ReqLds L;
   const int b = blockIdx.x, K = a.K;
   const int j = threadIdx.x;
+  const int sl = verify_slot(a, b);
+  if (sl < 0) {
+    finish_padding(a, b);
+    return;
+  }
   if (j <= K) {
     const RowStat rs = a.rowstat[b * (K + 1) + j];
     const TopP tp = a.topp ? a.topp[b * (K + 1) + j] : TopP{0u, 0, 0.0f, 0};
@@ -455,15 +487,15 @@ __global__ __launch_bounds__(64) void decide_kernel(VerifyArgs a) {
     L.key[j] = rs.key;
     if (j < K) {
       L.lq[j] = a.qlse[b * K + j];
-      if (a.temp[b] > 0.0f) {
-        draft_point(a, b, j, L.x[j], L.tx[j], L.cx[j]);
+      if (a.temp[sl] > 0.0f) {
+        draft_point(a, b, sl, j, L.x[j], L.tx[j], L.cx[j]);
       } else {
         L.x[j] = a.draft[b * K + j];
       }
     }
   }
   wave_lds_sync();
-  decide(a, b, L);
+  decide(a, b, sl, L);
 }
 
 // Score of column c for the final draw: log residual + g (mode 1; only a
@@ -507,14 +539,15 @@ __global__ __launch_bounds__(kThreads) void residual_kernel(VerifyArgs a) {
   if (rq.mode == 2) return;
   const int K = a.K, V = a.V;
   const int j = rq.n_acc, mode = rq.mode;
+  const int sl = verify_slot(a, b);  // live: padding requests are in mode 2
   DrawCtx d;
-  d.T = a.temp[b];
+  d.T = a.temp[sl];
   d.invT = 1.0f / d.T;
   d.M = rq.M;
   d.LZ = rq.LZ;
   d.LQ = rq.LQ;
   d.tp = rq.tp;
-  const unsigned long long sd = (unsigned long long)a.seeds[b];
+  const unsigned long long sd = (unsigned long long)a.seeds[sl];
   const unsigned long long pk = (unsigned long long)(a.anchor_pos[b] + j);
   d.pk0 = (uint32_t)pk;
   d.pk1 = (uint32_t)(pk >> 32);
@@ -522,7 +555,7 @@ __global__ __launch_bounds__(kThreads) void residual_kernel(VerifyArgs a) {
   d.sk1 = (uint32_t)(sd >> 32);
   const bool resid = mode == 1;
   const float* trow = a.target + (long long)(b * (K + 1) + j) * a.target_rs;
-  const long long crow = (long long)b * a.cache_rs + (long long)j * a.cache_ss;
+  const long long crow = (long long)verify_cache_row(a, b, sl) * a.cache_rs + (long long)j * a.cache_ss;
   const int c0 = chunk * kResCols;
   const int tc = c0 + (int)threadIdx.x * 4;
   float tv[kPer], cv[kPer];
