@@ -41,7 +41,7 @@ def _logsumexp(x64: np.ndarray) -> float:
 
 def draft_loop(base, base_dtype: str, w1_bits, w2_bits, anchor_tokens, anchor_pos, seeds, temperature,
                cache_dtype: str, K: int | None = None, teacher=None, want_scores: bool = False,
-               idx_map=None, row_mapping=None, sample_pos=None, cache_init=None) -> dict:
+               idx_map=None, row_mapping=None, sample_pos=None, cache_init=None, fp64_gumbel: bool = False) -> dict:
     """Run the K-step Markov draft loop for every request.
 
     base: [B, >=K, V] float32, or uint16 bf16 bit patterns when base_dtype is "bf16";
@@ -63,6 +63,10 @@ def draft_loop(base, base_dtype: str, w1_bits, w2_bits, anchor_tokens, anchor_po
     and its lse NaN; a later non-inert step of the row then has no valid
     previous token, and uses token 0 (flagged by bad_prev).
 
+    fp64_gumbel (the API page's ``use_fp64_gumbel``): the Gumbel variate and the
+    score z / T + g stay in float64 (the same uniforms) and the winner is
+    taken over the float64 scores.
+
     Returns tokens [B, K] int32, cache [B, K, V] (float32 or uint16 bf16 bits;
     [R, K, V] with idx_map), lse [B, K] float64 (log-sum-exp of cache / T; NaN
     for greedy rows) and margin [B, K] float64 (top-two gap of the float32
@@ -81,7 +85,7 @@ def draft_loop(base, base_dtype: str, w1_bits, w2_bits, anchor_tokens, anchor_po
         idx_map = np.asarray(idx_map, np.int64)
     lse = np.full((B, K), np.nan)
     margin = np.zeros((B, K))
-    scores_out = np.zeros((B, K, V), np.float32) if want_scores else None
+    scores_out = np.zeros((B, K, V), np.float64 if fp64_gumbel else np.float32) if want_scores else None
     prev = np.asarray(anchor_tokens, dtype=np.int64).copy()
     bad_prev = False
     if idx_map is None and ((prev < 0).any() or (prev >= V).any()):
@@ -117,8 +121,11 @@ def draft_loop(base, base_dtype: str, w1_bits, w2_bits, anchor_tokens, anchor_po
             cache[crow, k] = cbits[b]
             T = np.float32(temperature[slot])
             if T > 0:
-                g32 = gumbel_row(int(seeds[slot]), key, SALT_DRAFT, V).astype(np.float32)
-                s = (z32[b] / T).astype(np.float32) + g32
+                g64 = gumbel_row(int(seeds[slot]), key, SALT_DRAFT, V)
+                if fp64_gumbel:
+                    s = z32[b].astype(np.float64) / np.float64(T) + g64
+                else:
+                    s = (z32[b] / T).astype(np.float32) + g64.astype(np.float32)
                 lse[b, k] = _logsumexp(cval[b] / np.float64(T))
             else:
                 s = z32[b]
