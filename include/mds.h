@@ -191,14 +191,19 @@ int mds_rejection_verify(int B, int K, int V,
                          int32_t* out_tokens, int32_t* num_accepted,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* flags of mds_markov_draft_loop_ex */
+#define MDS_DRAFT_FP64_GUMBEL 1u /* the API page's use_fp64_gumbel: Gumbel variate and score in float64 */
+
 /*
- * mds_markov_draft_loop_indexed - mds_markov_draft_loop with the pages'
- * request-state indexing (DSparkSpeculator API page, _sample_logits and
- * _sample_markov_chain: per-row idx_map and sample_pos, the cache's
- * row_mapping; _sample_sequential_sharded: padding slots are inert, with no
- * draft-logits cache writes).
+ * mds_markov_draft_loop_ex - mds_markov_draft_loop with the pages'
+ * request-state indexing and options (DSparkSpeculator API page,
+ * _sample_logits and _sample_markov_chain: per-row idx_map and sample_pos,
+ * the cache's row_mapping, use_fp64_gumbel; _sample_sequential_sharded:
+ * padding slots are inert, with no draft-logits cache writes).
  *
- * Batch row b at step k uses state slot s = idx_map[b*K + k]:
+ * Batch row b at step k uses state slot s = idx_map[b*K + k] (s = b when
+ * idx_map is NULL; then row_mapping must be NULL and n_slots, n_cache_rows
+ * >= B):
  *   temperature[s], seeds[s]   its temperature and seed (arrays of n_slots);
  *   sample_pos[b*K + k]        the position P of the predicted token; the draw
  *                              is keyed by P - 1 (the plain call's P0 + k);
@@ -210,19 +215,23 @@ int mds_rejection_verify(int B, int K, int V,
  * draft_lse NaN; a later step of that row that is not inert has no previous
  * token and uses token 0 (MDS_STATUS_BAD_ANCHOR). A slot >= n_slots or a
  * mapped row outside [0, n_cache_rows) is treated as inert and sets
- * MDS_STATUS_BAD_INDEX. Always runs the streaming kernels (MDS_DRAFT_PATH=
- * resident returns MDS_ERR_UNSUPPORTED). Workspace and errors as for
- * mds_markov_draft_loop.
+ * MDS_STATUS_BAD_INDEX.
+ * flags: MDS_DRAFT_FP64_GUMBEL computes g = -ln(-ln u) (same u) and the score
+ * z/T + g in float64; the winner is the first NaN, else the first maximum of
+ * the float64 scores at a resolution of 2^-28 relative (candidates closer
+ * than that go to the lower column); needs r <= 256.
+ * Always runs the streaming kernels (MDS_DRAFT_PATH=resident returns
+ * MDS_ERR_UNSUPPORTED). Workspace and errors as for mds_markov_draft_loop.
  */
-int mds_markov_draft_loop_indexed(int B, int K, int V, int r,
-                                  const void* base, int base_dtype, int64_t base_req_stride, int64_t base_step_stride,
-                                  const void* w1, const void* w2,
-                                  const int32_t* anchor_tokens, const int32_t* idx_map, const int64_t* sample_pos,
-                                  int n_slots, const float* temperature, const int64_t* seeds,
-                                  const int32_t* row_mapping, int n_cache_rows,
-                                  void* cache, int cache_dtype, int64_t cache_row_stride, int64_t cache_step_stride,
-                                  int32_t* draft_tokens, float* draft_lse,
-                                  void* workspace, size_t workspace_bytes, void* stream);
+int mds_markov_draft_loop_ex(int B, int K, int V, int r,
+                             const void* base, int base_dtype, int64_t base_req_stride, int64_t base_step_stride,
+                             const void* w1, const void* w2,
+                             const int32_t* anchor_tokens, const int32_t* idx_map, const int64_t* sample_pos,
+                             int n_slots, const float* temperature, const int64_t* seeds,
+                             const int32_t* row_mapping, int n_cache_rows,
+                             void* cache, int cache_dtype, int64_t cache_row_stride, int64_t cache_step_stride,
+                             int32_t* draft_tokens, float* draft_lse, uint32_t flags,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * mds_rejection_verify_indexed - mds_rejection_verify with request-state

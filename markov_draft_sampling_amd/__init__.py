@@ -25,6 +25,7 @@ __all__ = [
 F32, BF16 = 0, 1
 STATUS_BAD_ANCHOR, STATUS_BAD_DRAFT, STATUS_BARRIER_TIMEOUT, STATUS_BAD_INDEX = 1, 2, 4, 8
 SALT_DRAFT, SALT_ACCEPT, SALT_RESAMPLE = 1 << 30, 1, 2
+DRAFT_FP64_GUMBEL = 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -53,9 +54,9 @@ _SIGS = {
                                                     ctypes.POINTER(_c_int)], _c_int),
     "mds_rejection_verify": ([_c_int] * 3 + [_vp, _c_i64, _vp, _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp,
                                              _vp, _vp, _vp, _c_sz, _vp], _c_int),
-    "mds_markov_draft_loop_indexed": ([_c_int] * 4 + [_vp, _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _c_int,
-                                                      _vp, _vp, _vp, _c_int, _vp, _c_int, _c_i64, _c_i64, _vp, _vp,
-                                                      _vp, _c_sz, _vp], _c_int),
+    "mds_markov_draft_loop_ex": ([_c_int] * 4 + [_vp, _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _c_int, _vp,
+                                                 _vp, _vp, _c_int, _vp, _c_int, _c_i64, _c_i64, _vp, _vp,
+                                                 ctypes.c_uint32, _vp, _c_sz, _vp], _c_int),
     "mds_rejection_verify_indexed": ([_c_int] * 3 + [_vp, _c_i64, _vp, _c_int, _c_i64, _c_i64, _c_int, _vp, _vp, _vp,
                                                      _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp],
                                      _c_int),
@@ -239,14 +240,15 @@ def rejection_verify(target, cache, draft_tokens, temperature, seeds, anchor_pos
     return workspace
 
 
-def markov_draft_loop_indexed(base, w1, w2, anchor_tokens, idx_map, sample_pos, temperature, seeds, cache,
-                              draft_tokens, row_mapping=None, draft_lse=None, workspace=None, stream=None):
-    """Draft loop with request-state indexing (mds_markov_draft_loop_indexed).
+def markov_draft_loop_ex(base, w1, w2, anchor_tokens, idx_map, sample_pos, temperature, seeds, cache, draft_tokens,
+                         row_mapping=None, draft_lse=None, fp64_gumbel=False, workspace=None, stream=None):
+    """Draft loop with request-state indexing and options (mds_markov_draft_loop_ex).
 
-    idx_map int32 [B, K] (state slot per row and step, < 0 inert), sample_pos
-    int64 [B, K] (predicted position P; the draw is keyed by P - 1),
-    temperature / seeds [n_slots], row_mapping int32 [n_slots] or None, cache
-    [n_cache_rows, K, V]. base, anchor_tokens, draft_tokens, draft_lse are
+    idx_map int32 [B, K] (state slot per row and step, < 0 inert) or None
+    (slot = batch row), sample_pos int64 [B, K] (predicted position P; the
+    draw is keyed by P - 1), temperature / seeds [n_slots], row_mapping int32
+    [n_slots] or None, cache [n_cache_rows, K, V]; fp64_gumbel: float64 Gumbel
+    variates and scores. base, anchor_tokens, draft_tokens, draft_lse are
     batch-indexed.
     """
     import torch
@@ -260,8 +262,9 @@ def markov_draft_loop_indexed(base, w1, w2, anchor_tokens, idx_map, sample_pos, 
           and w1.shape == w2.shape and w1.shape[0] == V, "w1 and w2 must be contiguous bf16 [V, r]")
     _need(anchor_tokens.dtype == torch.int32 and anchor_tokens.numel() == B and anchor_tokens.is_contiguous(),
           "anchor_tokens must be int32 [B]")
-    _need(idx_map.dtype == torch.int32 and idx_map.numel() == B * K and idx_map.is_contiguous(),
-          "idx_map must be int32 [B, K]")
+    if idx_map is not None:
+        _need(idx_map.dtype == torch.int32 and idx_map.numel() == B * K and idx_map.is_contiguous(),
+              "idx_map must be int32 [B, K]")
     _need(sample_pos.dtype == torch.int64 and sample_pos.numel() == B * K and sample_pos.is_contiguous(),
           "sample_pos must be int64 [B, K]")
     n_slots = temperature.numel()
@@ -277,12 +280,13 @@ def markov_draft_loop_indexed(base, w1, w2, anchor_tokens, idx_map, sample_pos, 
               "draft_lse must be float32 [B, K]")
     if workspace is None:
         workspace = new_workspace(draft_workspace_bytes(B, K, V, w1.shape[1]), base.device)
-    rc = _lib().mds_markov_draft_loop_indexed(
+    rc = _lib().mds_markov_draft_loop_ex(
         B, K, V, w1.shape[1], _ptr(base), _dtype_code(base), base.stride(0), base.stride(1), _ptr(w1), _ptr(w2),
         _ptr(anchor_tokens), _ptr(idx_map), _ptr(sample_pos), n_slots, _ptr(temperature), _ptr(seeds),
         _ptr(row_mapping), cache.shape[0], _ptr(cache), _dtype_code(cache), cache.stride(0), cache.stride(1),
-        _ptr(draft_tokens), _ptr(draft_lse), _ptr(workspace), workspace.numel(), _stream(stream, base.device))
-    _check(rc, "markov_draft_loop_indexed")
+        _ptr(draft_tokens), _ptr(draft_lse), DRAFT_FP64_GUMBEL if fp64_gumbel else 0, _ptr(workspace),
+        workspace.numel(), _stream(stream, base.device))
+    _check(rc, "markov_draft_loop_ex")
     return workspace
 
 

@@ -136,9 +136,11 @@ struct Indexing {
   const int32_t* row_map = nullptr;
   const int64_t* sample_pos = nullptr;
   int n_slots = 0, n_rows = 0;
+  uint32_t flags = 0;
 };
 
 int check_indexing(const Indexing& ix) {
+  if (ix.flags & ~MDS_DRAFT_FP64_GUMBEL) return fail(MDS_ERR_INVALID_ARG, "unknown flag bits");
   if (!ix.idx_map) return MDS_OK;
   if (ix.n_slots < 1 || ix.n_rows < 1) return fail(MDS_ERR_INVALID_ARG, "n_slots and n_cache_rows must be >= 1");
   return MDS_OK;
@@ -160,6 +162,8 @@ int draft_impl(int B, int K, int V, int r, const void* base, int base_dtype, int
   const int n_rows = ix.idx_map ? ix.n_rows : B;
   if (!rows_disjoint(n_rows, K, V, cache_rs, cache_ss))
     return fail(MDS_ERR_INVALID_ARG, "cache strides make rows overlap or are shorter than V");
+  const bool fp64 = (ix.flags & MDS_DRAFT_FP64_GUMBEL) != 0;
+  if (fp64 && r > 256) return fail(MDS_ERR_UNSUPPORTED, "the fp64 Gumbel option needs r <= 256");
   if (!aligned(w1, 16) || !aligned(w2, 16)) return fail(MDS_ERR_INVALID_ARG, "w1 and w2 must be 16-byte aligned");
   if (!aligned(workspace, kAlign)) return fail(MDS_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   const DraftLayout L = draft_layout(B, K, V);
@@ -198,11 +202,12 @@ int draft_impl(int B, int K, int V, int r, const void* base, int base_dtype, int
   a.sample_pos = (const long long*)ix.sample_pos;
   a.n_slots = ix.idx_map ? ix.n_slots : B;
   a.n_rows = n_rows;
+  a.fp64 = fp64;
   const int choice = draft_path_choice();
   if (choice < 0) return fail(MDS_ERR_INVALID_ARG, "MDS_DRAFT_PATH must be auto, stream or resident");
-  const bool indexed = ix.idx_map || ix.sample_pos;
+  const bool indexed = ix.idx_map || ix.sample_pos || fp64;
   if (choice == 2 && indexed)
-    return fail(MDS_ERR_UNSUPPORTED, "the resident draft kernel does not take request-state indexing");
+    return fail(MDS_ERR_UNSUPPORTED, "the resident draft kernel takes neither request-state indexing nor fp64 noise");
   int dev = 0, cus = 0, lds_max = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -230,7 +235,7 @@ int draft_impl(int B, int K, int V, int r, const void* base, int base_dtype, int
   if (ev_end && (e = hipEventRecord((hipEvent_t)ev_end, st)) != hipSuccess) return hip_fail(e, "event record");
   if (n_launches) *n_launches = resident ? 1 : K;
   mds::DraftFinalArgs f{B, K, a.G, a.keys, a.qpart, temperature, draft_tokens, draft_lse,
-                        a.idx_map, a.row_map, a.n_slots, a.n_rows};
+                        a.idx_map, a.row_map, a.n_slots, a.n_rows, a.fp64};
   if ((e = mds::launch_draft_finalize(f, st)) != hipSuccess) return hip_fail(e, "draft finalize launch");
   return ok();
 }
@@ -403,20 +408,23 @@ int mds_rejection_verify_indexed(int B, int K, int V, const float* target, int64
                      workspace, workspace_bytes, stream, ix);
 }
 
-int mds_markov_draft_loop_indexed(int B, int K, int V, int r, const void* base, int base_dtype,
-                                  int64_t base_req_stride, int64_t base_step_stride, const void* w1, const void* w2,
-                                  const int32_t* anchor_tokens, const int32_t* idx_map, const int64_t* sample_pos,
-                                  int n_slots, const float* temperature, const int64_t* seeds,
-                                  const int32_t* row_mapping, int n_cache_rows, void* cache, int cache_dtype,
-                                  int64_t cache_row_stride, int64_t cache_step_stride, int32_t* draft_tokens,
-                                  float* draft_lse, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!idx_map || !sample_pos) return fail(MDS_ERR_INVALID_ARG, "idx_map and sample_pos must not be NULL");
+int mds_markov_draft_loop_ex(int B, int K, int V, int r, const void* base, int base_dtype, int64_t base_req_stride,
+                             int64_t base_step_stride, const void* w1, const void* w2, const int32_t* anchor_tokens,
+                             const int32_t* idx_map, const int64_t* sample_pos, int n_slots, const float* temperature,
+                             const int64_t* seeds, const int32_t* row_mapping, int n_cache_rows, void* cache,
+                             int cache_dtype, int64_t cache_row_stride, int64_t cache_step_stride,
+                             int32_t* draft_tokens, float* draft_lse, uint32_t flags, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (!sample_pos) return fail(MDS_ERR_INVALID_ARG, "sample_pos must not be NULL");
+  if (!idx_map && (row_mapping || n_slots < B || n_cache_rows < B))
+    return fail(MDS_ERR_INVALID_ARG, "without idx_map: no row_mapping, n_slots >= B and n_cache_rows >= B");
   Indexing ix;
   ix.idx_map = idx_map;
   ix.row_map = row_mapping;
   ix.sample_pos = sample_pos;
   ix.n_slots = n_slots;
   ix.n_rows = n_cache_rows;
+  ix.flags = flags;
   return draft_impl(B, K, V, r, base, base_dtype, base_req_stride, base_step_stride, w1, w2, anchor_tokens, nullptr,
                     temperature, seeds, cache, cache_dtype, cache_row_stride, cache_step_stride, draft_tokens,
                     draft_lse, workspace, workspace_bytes, stream, nullptr, nullptr, nullptr, ix);

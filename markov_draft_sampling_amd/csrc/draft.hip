@@ -409,7 +409,7 @@ __global__ __launch_bounds__(256) void draft_finalize_kernel(DraftFinalArgs a) {
   if (row >= a.B * a.K) return;
   const int b = row / a.K, k = row - b * a.K;
   // inert rows keep key 0, i.e. token -1
-  if (lane == 0) a.tokens[row] = (int32_t)win_col(a.keys[(size_t)k * a.B + b]);
+  if (lane == 0) a.tokens[row] = key_col(a.keys[(size_t)k * a.B + b], a.fp64 != 0);
   if (!a.lse) return;
   const int sl = draft_slot(a.idx_map, a.row_map, a.B, a.K, a.n_slots, a.n_rows, nullptr, b, k);
   if (sl < 0) {

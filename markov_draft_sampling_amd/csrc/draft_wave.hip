@@ -30,8 +30,10 @@ namespace {
 
 constexpr int kRKMax = 8;  // rank slices of 32 (r <= 256)
 
-template <int NB, bool BBF16, bool CBF16>
+// F64: the fp64 Gumbel option (scores and the running winner in float64).
+template <int NB, bool BBF16, bool CBF16, bool F64>
 __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
+  using Score = typename std::conditional<F64, double, float>::type;
   constexpr int NT = NB / 16;
   const int r = a.r, V = a.V, k = a.k;
   const int RK = r >> 5;
@@ -146,7 +148,7 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
     int prev = -1;  // rows that are not served get a zero embedding
     if (draft_slot(a, b) >= 0) {
       // the previous step's winner (key 0, i.e. -1, when that step was inert)
-      long long tk = (k == 0) ? (long long)a.anchor[b] : (long long)(int32_t)win_col(a.keys[(size_t)(k - 1) * a.B + b]);
+      long long tk = (k == 0) ? (long long)a.anchor[b] : (long long)key_col(a.keys[(size_t)(k - 1) * a.B + b], F64);
       if (tk < 0 || tk >= V) {
         set_status(a.status, kStatusBadAnchor);
         tk = 0;
@@ -169,7 +171,8 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
   // at the lane's first column (value -inf), so a later column replaces it
   // only when strictly larger or the first NaN: the first-max rule.
   const int c_first = t_first * 16 + lg * 4;
-  float bv[NT], qm[NT], qs[NT];
+  Score bv[NT];
+  float qm[NT], qs[NT];
   int bi[NT];
   bool qnan[NT];
 #pragma unroll
@@ -252,7 +255,11 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float sv = y[i] + gumbel_from_word(wd[i]);
+          Score sv;
+          if (F64)
+            sv = (T1 ? (double)z[i] : (double)z[i] / (double)Tv[nt]) + gumbel64_from_word(wd[i]);
+          else
+            sv = y[i] + gumbel_from_word(wd[i]);
           const bool take = (sv > bv[nt]) || ((sv != sv) && (bv[nt] == bv[nt]));
           bv[nt] = take ? sv : bv[nt];
           bi[nt] = take ? c + i : bi[nt];
@@ -317,7 +324,11 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
         float xm = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float sv = div_t(z[i], Tv[nt], invT[nt]) + gumbel_from_word(wd[i]);
+          Score sv;
+          if (F64)
+            sv = (double)z[i] / (double)Tv[nt] + gumbel64_from_word(wd[i]);
+          else
+            sv = div_t(z[i], Tv[nt], invT[nt]) + gumbel_from_word(wd[i]);
           if (i < n) win_update(bv[nt], bi[nt], sv, c + i);
           const float xv = div_t(cv[i], Tv[nt], invT[nt]);
           qnan[nt] |= (i < n) && (xv != xv);
@@ -335,7 +346,7 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (i < n) win_update(bv[nt], bi[nt], z[i], c + i);
+          if (i < n) win_update(bv[nt], bi[nt], (Score)z[i], c + i);
       }
     }
     }
@@ -352,7 +363,7 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
   // merge the 4 lanes of each request row (lanes lr, lr + 16, lr + 32, lr + 48)
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    unsigned long long key = bi[nt] >= 0 ? win_key(bv[nt], (uint32_t)bi[nt]) : 0ull;
+    unsigned long long key = bi[nt] >= 0 ? win_key_of(bv[nt], (uint32_t)bi[nt]) : 0ull;
     float m = qm[nt], s = qnan[nt] ? NAN : qs[nt];
 #pragma unroll
     for (int off = 16; off < 64; off <<= 1) {
@@ -384,19 +395,20 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
   }
 }
 
-template <int NB, bool BBF16, bool CBF16>
+template <int NB, bool BBF16, bool CBF16, bool F64>
 hipError_t launch_wave(const DraftStepArgs& a, int bt, hipStream_t st) {
   DraftStepArgs b = a;
   b.BT = bt;
-  hipLaunchKernelGGL((draft_wave_kernel<NB, BBF16, CBF16>), dim3(a.G * bt), dim3(256), draft_wave_lds(NB, a.r), st,
-                     b);
+  hipLaunchKernelGGL((draft_wave_kernel<NB, BBF16, CBF16, F64>), dim3(a.G * bt), dim3(256), draft_wave_lds(NB, a.r),
+                     st, b);
   return hipGetLastError();
 }
 
-template <int NB>
+template <int NB, bool F64>
 hipError_t launch_wave_nb(const DraftStepArgs& a, int bt, hipStream_t st) {
-  if (a.base_bf16) return a.cache_bf16 ? launch_wave<NB, true, true>(a, bt, st) : launch_wave<NB, true, false>(a, bt, st);
-  return a.cache_bf16 ? launch_wave<NB, false, true>(a, bt, st) : launch_wave<NB, false, false>(a, bt, st);
+  if (a.base_bf16)
+    return a.cache_bf16 ? launch_wave<NB, true, true, F64>(a, bt, st) : launch_wave<NB, true, false, F64>(a, bt, st);
+  return a.cache_bf16 ? launch_wave<NB, false, true, F64>(a, bt, st) : launch_wave<NB, false, false, F64>(a, bt, st);
 }
 
 }  // namespace
@@ -409,7 +421,9 @@ hipError_t launch_draft_wave(const DraftStepArgs& a, hipStream_t st) {
   if (a.r > 32 * kRKMax) return hipErrorNotSupported;
   const int nb = draft_nb(a.B, a.r);
   const int bt = (a.B + nb - 1) / nb;
-  return nb == 16 ? launch_wave_nb<16>(a, bt, st) : launch_wave_nb<32>(a, bt, st);
+  if (a.fp64)
+    return nb == 16 ? launch_wave_nb<16, true>(a, bt, st) : launch_wave_nb<32, true>(a, bt, st);
+  return nb == 16 ? launch_wave_nb<16, false>(a, bt, st) : launch_wave_nb<32, false>(a, bt, st);
 }
 
 }  // namespace mds

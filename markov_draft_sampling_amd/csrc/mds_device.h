@@ -81,12 +81,37 @@ __device__ __forceinline__ uint64_t win_key(float x, uint32_t col) {
 }
 __device__ __forceinline__ uint32_t win_col(uint64_t key) { return ~(uint32_t)key; }
 
+// fp64 option: the same uniform, -ln(-ln u) and the score in float64. The
+// cross-work-group key keeps the top 40 bits of the ordered float64 (2^-28
+// relative) above the column's 24 bits, so candidates within that resolution
+// go to the lower column.
+__device__ __forceinline__ double gumbel64_from_word(uint32_t w) {
+  const double u = (double)uniform24(w);  // exact: an odd multiple of 2^-24
+  return -log(-log(u));
+}
+__device__ __forceinline__ uint64_t ord_f64(double x) {
+  if (x != x) return ~0ull;
+  const uint64_t b = (uint64_t)__double_as_longlong(x + 0.0);
+  return (b >> 63) ? ~b : (b | (1ull << 63));
+}
+__device__ __forceinline__ uint64_t win_key64(double x, uint32_t col) {
+  return (ord_f64(x) & ~0xFFFFFFull) | (0xFFFFFFu - col);
+}
+// column of a key in either format; key 0 (no candidate) gives -1
+__device__ __forceinline__ int key_col(uint64_t key, bool f64) {
+  if (!key) return -1;
+  return f64 ? (int)(0xFFFFFFu - (uint32_t)(key & 0xFFFFFFu)) : (int)(~(uint32_t)key);
+}
+
 // In-order update of a running winner (columns arrive in increasing order).
-__device__ __forceinline__ void win_update(float& bv, int& bi, float s, int col) {
+template <typename S>
+__device__ __forceinline__ void win_update(S& bv, int& bi, S s, int col) {
   const bool take = (s > bv) || ((s != s) && (bv == bv)) || (bi < 0);
   bv = take ? s : bv;
   bi = take ? col : bi;
 }
+__device__ __forceinline__ uint64_t win_key_of(float x, uint32_t col) { return win_key(x, col); }
+__device__ __forceinline__ uint64_t win_key_of(double x, uint32_t col) { return win_key64(x, col); }
 
 // ------------------------------------------------------------------ bf16 --
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }

@@ -36,6 +36,7 @@ struct DraftStepArgs {
   const int32_t* row_map;    // [n_slots] cache row of a slot; null: row = slot
   const long long* sample_pos;  // [B][K] predicted position P (draw keyed by P - 1); null: anchor_pos + k
   int n_slots, n_rows;
+  int fp64;                  // fp64 Gumbel option: float64 scores, 64-bit keys of the fp64 format
 };
 
 struct DraftFinalArgs {
@@ -48,6 +49,7 @@ struct DraftFinalArgs {
   const int32_t* idx_map;
   const int32_t* row_map;
   int n_slots, n_rows;
+  int fp64;  // keys in the fp64 format
 };
 
 // The state slot of batch row b at draft step k, or -1 when the row is inert

@@ -1,0 +1,102 @@
+"""GPU parity of the fp64 Gumbel option (mds_markov_draft_loop_ex, MDS_DRAFT_FP64_GUMBEL).
+
+Draft tokens against the oracle's float64 scores under teacher forcing
+(mismatch excused only at a float64 top-two gap <= 1e-3), planted ties and NaN
+columns decided exactly, cache and log-sum-exp as in the float32 mode.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from parity import CACHE_TOL, TOK_MARGIN, cache_to_numpy, dev_tensors
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(wl, fp64=True):
+    import torch
+    import markov_draft_sampling_amd as mds
+    d = dev_tensors(wl)
+    spos = torch.from_numpy(wl.anchor_pos[:, None] + 1 + np.arange(wl.K)[None, :]).cuda()
+    ws = mds.new_workspace(mds.draft_workspace_bytes(wl.B, wl.K, wl.V, wl.r), torch.device("cuda"))
+    mds.markov_draft_loop_ex(d["base"], d["w1"], d["w2"], d["anchor_tokens"], None, spos, d["temperature"], d["seeds"],
+                             d["cache"], d["draft_tokens"], draft_lse=d["draft_lse"], fp64_gumbel=fp64, workspace=ws)
+    torch.cuda.synchronize()
+    assert mds.workspace_status(ws) == 0
+    return d
+
+
+def _check(wl, d, rows):
+    rows = np.asarray(rows)
+    toks = d["draft_tokens"].cpu().numpy()
+    ref = oracle.draft_loop(wl.draft_base[rows], wl.base_dtype, wl.w1, wl.w2, wl.anchor_tokens[rows],
+                            wl.anchor_pos[rows], wl.seeds[rows], wl.temperature[rows], wl.cache_dtype,
+                            teacher=toks[rows], fp64_gumbel=True)
+    mism = ref["tokens"] != toks[rows]
+    bad = mism & (ref["margin"] > TOK_MARGIN)
+    assert not bad.any(), (np.argwhere(bad)[:5], toks[rows][bad][:5], ref["tokens"][bad][:5])
+    gc = cache_to_numpy(d["cache"], wl.cache_dtype)[rows]
+    if wl.cache_dtype == "bf16":
+        g = workloads.bf16_bits_to_f32(gc).astype(np.float64)
+        o = workloads.bf16_bits_to_f32(ref["cache"]).astype(np.float64)
+        tol = np.maximum(CACHE_TOL, np.abs(o) * 2.0 ** -7 * 1.01)
+    else:
+        g, o = gc.astype(np.float64), ref["cache"].astype(np.float64)
+        tol = CACHE_TOL
+    ok = (np.abs(g - o) <= tol) | (np.isnan(g) & np.isnan(o))
+    assert ok.all()
+    lse = d["draft_lse"].cpu().numpy()[rows]
+    samp = np.broadcast_to((wl.temperature[rows] > 0)[:, None], lse.shape)
+    err = np.abs(lse - ref["lse"])[samp]
+    both_nan = (np.isnan(lse) & np.isnan(ref["lse"]))[samp]
+    assert ((err <= 1e-4 + 1e-5 * np.abs(ref["lse"][samp])) | both_nan).all()
+    return toks, ref
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 5])
+def test_fp64_gumbel_matches_oracle(cfg):
+    wl = workloads.make_workload(cfg, B=None if cfg == 1 else 8)
+    d = _run(wl)
+    toks, ref = _check(wl, d, np.arange(wl.B))
+    # planted ties and NaN columns are decided by rule, exactly
+    for b, k, cols in wl.nan_rows:
+        if b < wl.B and k < wl.K:
+            assert toks[b, k] == ref["tokens"][b, k]
+    for b in wl.tie_requests:
+        if b < wl.B:
+            np.testing.assert_array_equal(toks[b], ref["tokens"][b])
+
+
+def test_fp64_gumbel_headline_rows():
+    wl = workloads.make_workload(4, B=32)
+    d = _run(wl)
+    _check(wl, d, [0, 11, 31])
+
+
+def test_fp64_and_fp32_runs_agree_on_clear_steps():
+    wl = workloads.make_workload(2, B=8)
+    d64 = _run(wl, fp64=True)
+    t64 = d64["draft_tokens"].cpu().numpy()
+    d32 = _run(wl, fp64=False)
+    t32 = d32["draft_tokens"].cpu().numpy()
+    ref = oracle.draft_loop(wl.draft_base, wl.base_dtype, wl.w1, wl.w2, wl.anchor_tokens, wl.anchor_pos, wl.seeds,
+                            wl.temperature, wl.cache_dtype, teacher=t32)
+    first = np.argmax(np.concatenate([t64 != t32, np.ones((wl.B, 1), bool)], axis=1), axis=1)
+    for b in range(wl.B):  # until the chains part, a step differs only where float32 rounding decides
+        for k in range(min(first[b] + 1, wl.K)):
+            if t64[b, k] != t32[b, k]:
+                assert ref["margin"][b, k] <= 1e-4
+
+
+def test_fp64_gumbel_needs_rank_up_to_256():
+    import torch
+    import markov_draft_sampling_amd as mds
+    wl = workloads.make_custom(1000, 288, 2, 2, seed=1)
+    d = dev_tensors(wl)
+    spos = torch.from_numpy(wl.anchor_pos[:, None] + 1 + np.arange(wl.K)[None, :]).cuda()
+    with pytest.raises(mds.MdsError):
+        mds.markov_draft_loop_ex(d["base"], d["w1"], d["w2"], d["anchor_tokens"], None, spos, d["temperature"],
+                                 d["seeds"], d["cache"], d["draft_tokens"], fp64_gumbel=True)

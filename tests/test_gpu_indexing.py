@@ -1,6 +1,6 @@
 """GPU parity of request-state indexing, padding rows and -1 placeholder drafts.
 
-The indexed draft loop and verification (mds_markov_draft_loop_indexed,
+The indexed draft loop and verification (mds_markov_draft_loop_ex,
 mds_rejection_verify_indexed) against the oracle's indexed runs, and the plain
 verification with placeholder drafts; same parity rules as tests/parity.py.
 """
@@ -56,7 +56,7 @@ def _run_draft(wl, ix):
         cache = torch.full((ix["n_rows"], wl.K, wl.V), SENT_F32, dtype=cdt, device="cuda")
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
     ws = mds.new_workspace(mds.draft_workspace_bytes(wl.B, wl.K, wl.V, wl.r), torch.device("cuda"))
-    mds.markov_draft_loop_indexed(d["base"], d["w1"], d["w2"], d["anchor_tokens"], t(ix["idx"]), t(ix["spos"]),
+    mds.markov_draft_loop_ex(d["base"], d["w1"], d["w2"], d["anchor_tokens"], t(ix["idx"]), t(ix["spos"]),
                                   t(ix["temp"]), t(ix["seeds"]), cache, d["draft_tokens"], row_mapping=t(ix["rowmap"]),
                                   draft_lse=d["draft_lse"], workspace=ws)
     torch.cuda.synchronize()
