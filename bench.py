@@ -100,6 +100,9 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=32, help="requests the CPU oracle baseline runs on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="do not flush caches between timed steps")
+    ap.add_argument("--variant", choices=("plain", "indexed", "fp64"), default="plain",
+                    help="plain: batch-indexed draft + verify; indexed: the same work through request-state slots, "
+                         "a row mapping and per-step sample positions; fp64: the float64 Gumbel option")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB elementwise copy (reference dispatch for counter scaling)")
     a = ap.parse_args()
@@ -138,14 +141,42 @@ def main():
     ws_v = mds.new_workspace(mds.verify_workspace_bytes(B, K, V, False, True), dev)
     flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)  # 512 MiB, read to evict caches
     stream = torch.cuda.current_stream(dev)
+    spos = (apos[:, None] + 1 + torch.arange(K, device=dev)[None, :]).contiguous()
+    if a.variant == "indexed":
+        # request b lives in slot perm[b] of 2B slots; slot s owns cache row rowmap[s]
+        rng = np.random.default_rng(17)
+        n_slots = 2 * B
+        perm = rng.permutation(n_slots)[:B].astype(np.int32)
+        rowmap = rng.integers(0, B, n_slots).astype(np.int32)
+        rowmap[perm] = rng.permutation(B)
+        s_temp = np.full(n_slots, 0.5, np.float32)
+        s_seed = rng.integers(0, 2**63, n_slots, dtype=np.int64)
+        s_temp[perm], s_seed[perm] = wl.temperature, wl.seeds
+        idx_b = torch.from_numpy(perm).to(dev)
+        idx_bk = idx_b[:, None].expand(B, K).contiguous()
+        rmap = torch.from_numpy(rowmap).to(dev)
+        s_temp, s_seed = torch.from_numpy(s_temp).to(dev), torch.from_numpy(s_seed).to(dev)
 
     def step(events=None):
-        if events is None:
-            mds.markov_draft_loop(base, w1, w2, anchor, apos, temp, seeds, cache, toks, lse, workspace=ws_d)
+        if a.variant == "plain":
+            if events is None:
+                mds.markov_draft_loop(base, w1, w2, anchor, apos, temp, seeds, cache, toks, lse, workspace=ws_d)
+            else:
+                launches.append(mds.markov_draft_loop_timed(base, w1, w2, anchor, apos, temp, seeds, cache, toks, lse,
+                                                            ws_d, events[0], events[1]))
+            mds.rejection_verify(target, cache, toks, temp, seeds, apos, out, nacc, draft_lse=lse, workspace=ws_v)
+            return
+        ix = a.variant == "indexed"
+        r_ = mds.markov_draft_loop_ex(base, w1, w2, anchor, idx_bk if ix else None, spos, s_temp if ix else temp,
+                                      s_seed if ix else seeds, cache, toks, row_mapping=rmap if ix else None,
+                                      draft_lse=lse, fp64_gumbel=a.variant == "fp64", workspace=ws_d, events=events)
+        if events is not None:
+            launches.append(r_[1])
+        if ix:
+            mds.rejection_verify_indexed(target, cache, toks, idx_b, s_temp, s_seed, apos, out, nacc,
+                                         row_mapping=rmap, draft_lse=lse, workspace=ws_v)
         else:
-            launches.append(mds.markov_draft_loop_timed(base, w1, w2, anchor, apos, temp, seeds, cache, toks, lse,
-                                                        ws_d, events[0], events[1]))
-        mds.rejection_verify(target, cache, toks, temp, seeds, apos, out, nacc, draft_lse=lse, workspace=ws_v)
+            mds.rejection_verify(target, cache, toks, temp, seeds, apos, out, nacc, draft_lse=lse, workspace=ws_v)
 
     for _ in range(a.warmup):
         step()
@@ -192,7 +223,7 @@ def main():
     else:
         traffic = recorded_traffic("draft_wave_kernel_hbm_traffic_V200064_B32.md",
                                    ("draft_wave.hip", "mds_device.h", "mds_internal.h"))
-    if B != 32:
+    if B != 32 or a.variant != "plain":
         traffic = None
     status = mds.workspace_status(ws_d) | mds.workspace_status(ws_v)
 
@@ -210,8 +241,10 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"Markov draft loop + rejection verify, V={V} r={r} K={K} B={B}, fp32 base/target/"
-                               f"cache, bf16 w1/w2, T=1",
-                   "V": V, "r": r, "K": K, "B": B, "cache_flushed_between_steps": not a.no_flush},
+                               f"cache, bf16 w1/w2, T=1" + {"plain": "", "indexed": ", request-state slots + row "
+                               "mapping", "fp64": ", float64 Gumbel"}[a.variant],
+                   "V": V, "r": r, "K": K, "B": B, "variant": a.variant,
+                   "cache_flushed_between_steps": not a.no_flush},
         "hbm": {"algorithmic_bytes_per_step": draft_b + verify_b, "achieved_GBps": step_gbps,
                 "peak_GBps": HBM_PEAK_GBPS, "frac": step_gbps / HBM_PEAK_GBPS},
         "roofline": {"kernel": ("draft_resident_kernel (all K Markov steps, w2 held on chip)" if n_launch == 1 else

@@ -222,6 +222,9 @@ int mds_rejection_verify(int B, int K, int V,
  * than that go to the lower column); needs r <= 256.
  * Always runs the streaming kernels (MDS_DRAFT_PATH=resident returns
  * MDS_ERR_UNSUPPORTED). Workspace and errors as for mds_markov_draft_loop.
+ * ev_begin / ev_end (hipEvent_t as void*, or NULL) are recorded on `stream`
+ * around the Markov step launches and *n_step_launches (if not NULL) gets
+ * their count, as in mds_markov_draft_loop_timed.
  */
 int mds_markov_draft_loop_ex(int B, int K, int V, int r,
                              const void* base, int base_dtype, int64_t base_req_stride, int64_t base_step_stride,
@@ -231,7 +234,8 @@ int mds_markov_draft_loop_ex(int B, int K, int V, int r,
                              const int32_t* row_mapping, int n_cache_rows,
                              void* cache, int cache_dtype, int64_t cache_row_stride, int64_t cache_step_stride,
                              int32_t* draft_tokens, float* draft_lse, uint32_t flags,
-                             void* workspace, size_t workspace_bytes, void* stream);
+                             void* workspace, size_t workspace_bytes, void* stream,
+                             void* ev_begin, void* ev_end, int* n_step_launches);
 
 /*
  * mds_rejection_verify_indexed - mds_rejection_verify with request-state

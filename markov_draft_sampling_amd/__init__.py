@@ -56,7 +56,8 @@ _SIGS = {
                                              _vp, _vp, _vp, _c_sz, _vp], _c_int),
     "mds_markov_draft_loop_ex": ([_c_int] * 4 + [_vp, _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _c_int, _vp,
                                                  _vp, _vp, _c_int, _vp, _c_int, _c_i64, _c_i64, _vp, _vp,
-                                                 ctypes.c_uint32, _vp, _c_sz, _vp], _c_int),
+                                                 ctypes.c_uint32, _vp, _c_sz, _vp, _vp, _vp, ctypes.POINTER(_c_int)],
+                                 _c_int),
     "mds_rejection_verify_indexed": ([_c_int] * 3 + [_vp, _c_i64, _vp, _c_int, _c_i64, _c_i64, _c_int, _vp, _vp, _vp,
                                                      _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp],
                                      _c_int),
@@ -241,7 +242,8 @@ def rejection_verify(target, cache, draft_tokens, temperature, seeds, anchor_pos
 
 
 def markov_draft_loop_ex(base, w1, w2, anchor_tokens, idx_map, sample_pos, temperature, seeds, cache, draft_tokens,
-                         row_mapping=None, draft_lse=None, fp64_gumbel=False, workspace=None, stream=None):
+                         row_mapping=None, draft_lse=None, fp64_gumbel=False, workspace=None, stream=None,
+                         events=None):
     """Draft loop with request-state indexing and options (mds_markov_draft_loop_ex).
 
     idx_map int32 [B, K] (state slot per row and step, < 0 inert) or None
@@ -249,7 +251,9 @@ def markov_draft_loop_ex(base, w1, w2, anchor_tokens, idx_map, sample_pos, tempe
     draw is keyed by P - 1), temperature / seeds [n_slots], row_mapping int32
     [n_slots] or None, cache [n_cache_rows, K, V]; fp64_gumbel: float64 Gumbel
     variates and scores. base, anchor_tokens, draft_tokens, draft_lse are
-    batch-indexed.
+    batch-indexed. events: optional (begin, end) torch.cuda.Event pair
+    recorded around the Markov step launches; then returns (workspace, number
+    of launches).
     """
     import torch
     B, K = draft_tokens.shape
@@ -280,14 +284,22 @@ def markov_draft_loop_ex(base, w1, w2, anchor_tokens, idx_map, sample_pos, tempe
               "draft_lse must be float32 [B, K]")
     if workspace is None:
         workspace = new_workspace(draft_workspace_bytes(B, K, V, w1.shape[1]), base.device)
+    ev = (None, None)
+    if events is not None:
+        st = stream if stream is not None else torch.cuda.current_stream(base.device)
+        for e in events:  # torch creates the underlying HIP event on its first record
+            if not e.cuda_event:
+                e.record(st)
+        ev = (_vp(events[0].cuda_event), _vp(events[1].cuda_event))
+    n = _c_int(0)
     rc = _lib().mds_markov_draft_loop_ex(
         B, K, V, w1.shape[1], _ptr(base), _dtype_code(base), base.stride(0), base.stride(1), _ptr(w1), _ptr(w2),
         _ptr(anchor_tokens), _ptr(idx_map), _ptr(sample_pos), n_slots, _ptr(temperature), _ptr(seeds),
         _ptr(row_mapping), cache.shape[0], _ptr(cache), _dtype_code(cache), cache.stride(0), cache.stride(1),
         _ptr(draft_tokens), _ptr(draft_lse), DRAFT_FP64_GUMBEL if fp64_gumbel else 0, _ptr(workspace),
-        workspace.numel(), _stream(stream, base.device))
+        workspace.numel(), _stream(stream, base.device), ev[0], ev[1], ctypes.byref(n))
     _check(rc, "markov_draft_loop_ex")
-    return workspace
+    return (workspace, n.value) if events is not None else workspace
 
 
 def rejection_verify_indexed(target, cache, draft_tokens, idx_map, temperature, seeds, anchor_pos, out_tokens,

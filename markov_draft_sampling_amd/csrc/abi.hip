@@ -414,7 +414,8 @@ int mds_markov_draft_loop_ex(int B, int K, int V, int r, const void* base, int b
                              const int64_t* seeds, const int32_t* row_mapping, int n_cache_rows, void* cache,
                              int cache_dtype, int64_t cache_row_stride, int64_t cache_step_stride,
                              int32_t* draft_tokens, float* draft_lse, uint32_t flags, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+                             size_t workspace_bytes, void* stream, void* ev_begin, void* ev_end,
+                             int* n_step_launches) {
   if (!sample_pos) return fail(MDS_ERR_INVALID_ARG, "sample_pos must not be NULL");
   if (!idx_map && (row_mapping || n_slots < B || n_cache_rows < B))
     return fail(MDS_ERR_INVALID_ARG, "without idx_map: no row_mapping, n_slots >= B and n_cache_rows >= B");
@@ -427,7 +428,7 @@ int mds_markov_draft_loop_ex(int B, int K, int V, int r, const void* base, int b
   ix.flags = flags;
   return draft_impl(B, K, V, r, base, base_dtype, base_req_stride, base_step_stride, w1, w2, anchor_tokens, nullptr,
                     temperature, seeds, cache, cache_dtype, cache_row_stride, cache_step_stride, draft_tokens,
-                    draft_lse, workspace, workspace_bytes, stream, nullptr, nullptr, nullptr, ix);
+                    draft_lse, workspace, workspace_bytes, stream, ev_begin, ev_end, n_step_launches, ix);
 }
 
 int mds_debug_noise(int n, const int32_t* cols, int64_t seed, int64_t pos_key, uint32_t salt, uint32_t* words,
