@@ -55,3 +55,22 @@ def top_two_margin(scores) -> float:
     if not np.isfinite(s[w]):
         return 0.0 if rest.max() == s[w] else float("inf")
     return float(s[w] - rest.max())
+
+
+def topk_columns(row, k: int) -> np.ndarray:
+    """Columns of the k largest entries of a row, in increasing column order.
+
+    DSparkSpeculator API page, ``_sample_sequential_topk``: the candidates are
+    the top-k of a step's base logits. The order among equal values is not
+    stated there; the reading taken is the winner rule's total order, so a NaN
+    ranks above every number, -0.0 equals +0.0, and of equal values the lower
+    column ranks higher.
+    """
+    v = np.asarray(row, dtype=np.float64)
+    if not 1 <= k <= v.size:
+        raise ValueError("k must be in [1, V]")
+    nan = np.isnan(v)
+    val = np.where(nan, 0.0, v) + 0.0  # adding +0.0 turns -0.0 into +0.0
+    # lexsort's last key is the primary one: NaN first, then value descending, then column
+    order = np.lexsort((np.arange(v.size), -val, ~nan))
+    return np.sort(order[:k])

@@ -21,12 +21,18 @@ Readings where the pages are silent (each listed in the design doc):
   float32 because the pages' Gumbel noise is float32 by default (PR #65007,
   the fp64 Gumbel option listed under Part 1's unsupported configurations);
 * the winner is the first NaN, otherwise the first maximum (``argmax_rule``).
+
+Top-k Markov drafting (the API page's ``_sample_sequential_topk``): the
+candidates of each step are chosen once, from the base logits alone
+(``topk_columns``); at every step the Markov bias is applied at those columns
+only, through the gathered rows of w2, every other entry of the step's row is
+-inf, and that row then goes through the same sampler and cache write.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .core import argmax_rule, bf16_rne, bf16_to_f64, top_two_margin
+from .core import argmax_rule, bf16_rne, bf16_to_f64, top_two_margin, topk_columns
 from .noise import SALT_DRAFT, gumbel_row
 
 
@@ -41,7 +47,8 @@ def _logsumexp(x64: np.ndarray) -> float:
 
 def draft_loop(base, base_dtype: str, w1_bits, w2_bits, anchor_tokens, anchor_pos, seeds, temperature,
                cache_dtype: str, K: int | None = None, teacher=None, want_scores: bool = False,
-               idx_map=None, row_mapping=None, sample_pos=None, cache_init=None, fp64_gumbel: bool = False) -> dict:
+               idx_map=None, row_mapping=None, sample_pos=None, cache_init=None, fp64_gumbel: bool = False,
+               topk: int | None = None) -> dict:
     """Run the K-step Markov draft loop for every request.
 
     base: [B, >=K, V] float32, or uint16 bf16 bit patterns when base_dtype is "bf16";
@@ -67,6 +74,11 @@ def draft_loop(base, base_dtype: str, w1_bits, w2_bits, anchor_tokens, anchor_po
     score z / T + g stay in float64 (the same uniforms) and the winner is
     taken over the float64 scores.
 
+    topk (the API page's top-k Markov drafting): the k candidate columns of
+    step k of request b are the top-k of base[b, k]; the biased logit there is
+    base + (w2[candidate rows] @ embedding), every other column holds -inf,
+    and the row is then sampled and cached as in the dense loop.
+
     Returns tokens [B, K] int32, cache [B, K, V] (float32 or uint16 bf16 bits;
     [R, K, V] with idx_map), lse [B, K] float64 (log-sum-exp of cache / T; NaN
     for greedy rows) and margin [B, K] float64 (top-two gap of the float32
@@ -88,6 +100,9 @@ def draft_loop(base, base_dtype: str, w1_bits, w2_bits, anchor_tokens, anchor_po
     scores_out = np.zeros((B, K, V), np.float64 if fp64_gumbel else np.float32) if want_scores else None
     prev = np.asarray(anchor_tokens, dtype=np.int64).copy()
     bad_prev = False
+    if topk is not None:  # candidate selection, once for all steps, from the base logits alone
+        cand = [[topk_columns(bf16_to_f64(base[b, k]) if base_dtype == "bf16" else base[b, k], int(topk))
+                 for k in range(K)] for b in range(B)]
     if idx_map is None and ((prev < 0).any() or (prev >= V).any()):
         raise ValueError("anchor token out of range")
     for k in range(K):
@@ -98,9 +113,17 @@ def draft_loop(base, base_dtype: str, w1_bits, w2_bits, anchor_tokens, anchor_po
             bad_prev = True
         prev = np.where((prev >= 0) & (prev < V), prev, 0)
         emb = w1[prev]  # [B, r]: row gather (markov_embed)
-        bias = emb @ w2t  # [B, V]: markov_bias, exact products, float64 sums
         row = bf16_to_f64(base[:, k]) if base_dtype == "bf16" else base[:, k].astype(np.float64)
-        z32 = (row + bias).astype(np.float32)  # one rounding
+        if topk is None:
+            bias = emb @ w2t  # [B, V]: markov_bias, exact products, float64 sums
+            z32 = (row + bias).astype(np.float32)  # one rounding
+        else:
+            # bias at the candidates only, through the gathered rows of w2;
+            # every other entry of the row is -inf
+            z32 = np.full((B, V), -np.inf, np.float32)
+            for b in range(B):
+                c = cand[b][k]
+                z32[b, c] = (row[b, c] + emb[b] @ w2t[:, c]).astype(np.float32)
         if cache_dtype == "bf16":
             cbits = bf16_rne(z32)
             cval = bf16_to_f64(cbits)
