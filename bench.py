@@ -43,6 +43,17 @@ def algorithmic_bytes(B, K, V, r, s_base=4, s_cache=4, s_tgt=4):
     return draft_step, draft, verify
 
 
+def topk_bytes(B, K, V, r, topk, s_base=4, s_cache=4):
+    """Top-k drafting: bytes of the selection launch (base logits read once,
+    the -inf cache rows written, the chunk candidates written) and of the
+    whole draft call (plus the merge and the K-step chain over gathered rows)."""
+    NC = -(-V // 8192)
+    select = B * K * V * (s_base + s_cache) + B * K * NC * topk * 8
+    merge = B * K * NC * topk * 8 + B * K * topk * 4
+    chain = B * K * (topk * (r * 2 + s_base + s_cache + 4) + r * 2)
+    return select, select + merge + chain
+
+
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "markov_draft_sampling_amd", "csrc")
 
@@ -65,8 +76,9 @@ def recorded_traffic(profile: str, sources) -> float | None:
     return float(fields["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(wl, n_req: int, repeats: int = 2):
-    """The oracle, as it stands, on the first n_req requests of the workload."""
+def cpu_baseline(wl, n_req: int, repeats: int = 2, **draft_kw):
+    """The oracle, as it stands, on the first n_req requests of the workload
+    (draft_kw: the draft loop's options, topk or fp64_gumbel)."""
     import numpy as np
     import oracle
     try:
@@ -80,7 +92,7 @@ def cpu_baseline(wl, n_req: int, repeats: int = 2):
     t0 = time.perf_counter()
     for _ in range(repeats):
         d = oracle.draft_loop(wl.draft_base[rows], wl.base_dtype, wl.w1, wl.w2, wl.anchor_tokens[rows],
-                              wl.anchor_pos[rows], wl.seeds[rows], wl.temperature[rows], wl.cache_dtype)
+                              wl.anchor_pos[rows], wl.seeds[rows], wl.temperature[rows], wl.cache_dtype, **draft_kw)
         oracle.verify(tgt, d["cache"], wl.cache_dtype, d["tokens"], wl.temperature[rows],
                       None if wl.top_p is None else wl.top_p[rows], wl.seeds[rows], wl.anchor_pos[rows])
     dt = (time.perf_counter() - t0) / repeats
@@ -100,9 +112,11 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=32, help="requests the CPU oracle baseline runs on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="do not flush caches between timed steps")
-    ap.add_argument("--variant", choices=("plain", "indexed", "fp64"), default="plain",
+    ap.add_argument("--variant", choices=("plain", "indexed", "fp64", "topk"), default="plain",
                     help="plain: batch-indexed draft + verify; indexed: the same work through request-state slots, "
-                         "a row mapping and per-step sample positions; fp64: the float64 Gumbel option")
+                         "a row mapping and per-step sample positions; fp64: the float64 Gumbel option; topk: "
+                         "top-k Markov drafting (--topk candidates per row)")
+    ap.add_argument("--topk", type=int, default=64, help="candidates per row of --variant topk")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB elementwise copy (reference dispatch for counter scaling)")
     a = ap.parse_args()
@@ -137,7 +151,8 @@ def main():
     lse = torch.empty((B, K), dtype=torch.float32, device=dev)
     out = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
     nacc = torch.empty((B,), dtype=torch.int32, device=dev)
-    ws_d = mds.new_workspace(mds.draft_workspace_bytes(B, K, V, r), dev)
+    ws_d = mds.new_workspace(mds.draft_topk_workspace_bytes(B, K, V, r, a.topk) if a.variant == "topk" else
+                             mds.draft_workspace_bytes(B, K, V, r), dev)
     ws_v = mds.new_workspace(mds.verify_workspace_bytes(B, K, V, False, True), dev)
     flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)  # 512 MiB, read to evict caches
     stream = torch.cuda.current_stream(dev)
@@ -164,6 +179,13 @@ def main():
             else:
                 launches.append(mds.markov_draft_loop_timed(base, w1, w2, anchor, apos, temp, seeds, cache, toks, lse,
                                                             ws_d, events[0], events[1]))
+            mds.rejection_verify(target, cache, toks, temp, seeds, apos, out, nacc, draft_lse=lse, workspace=ws_v)
+            return
+        if a.variant == "topk":
+            mds.markov_draft_loop_topk(base, w1, w2, anchor, None, spos, temp, seeds, cache, toks, a.topk,
+                                       draft_lse=lse, workspace=ws_d, events=events)
+            if events is not None:
+                launches.append(1)
             mds.rejection_verify(target, cache, toks, temp, seeds, apos, out, nacc, draft_lse=lse, workspace=ws_v)
             return
         ix = a.variant == "indexed"
@@ -214,6 +236,8 @@ def main():
     draft_step_b, draft_b, verify_b = algorithmic_bytes(B, K, V, r)
     kern_avg_ms = float(np.mean(draft_span_ms)) / n_launch
     bytes_per_launch = draft_b / n_launch
+    if a.variant == "topk":
+        bytes_per_launch, draft_b = topk_bytes(B, K, V, r, a.topk)
     achieved = bytes_per_launch / (kern_avg_ms * 1e-3) / 1e9
     step_gbps = (draft_b + verify_b) / (ms * 1e-3) / 1e9
     acc_len = float((nacc.float() + 1).mean().item())
@@ -223,7 +247,10 @@ def main():
     else:
         traffic = recorded_traffic("draft_wave_kernel_hbm_traffic_V200064_B32.md",
                                    ("draft_wave.hip", "mds_device.h", "mds_internal.h"))
-    if B != 32 or a.variant != "plain":
+    if a.variant == "topk":
+        traffic = recorded_traffic("topk_chunk_kernel_hbm_traffic_V200064_B32.md",
+                                   ("draft_topk.hip", "mds_device.h", "mds_internal.h"))
+    if B != 32 or a.variant not in ("plain", "topk") or (a.variant == "topk" and a.topk != 64):
         traffic = None
     status = mds.workspace_status(ws_d) | mds.workspace_status(ws_v)
 
@@ -242,12 +269,16 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"Markov draft loop + rejection verify, V={V} r={r} K={K} B={B}, fp32 base/target/"
                                f"cache, bf16 w1/w2, T=1" + {"plain": "", "indexed": ", request-state slots + row "
-                               "mapping", "fp64": ", float64 Gumbel"}[a.variant],
+                               "mapping", "fp64": ", float64 Gumbel",
+                               "topk": f", top-k Markov drafting k={a.topk}"}[a.variant],
                    "V": V, "r": r, "K": K, "B": B, "variant": a.variant,
+                   **({"topk": a.topk} if a.variant == "topk" else {}),
                    "cache_flushed_between_steps": not a.no_flush},
         "hbm": {"algorithmic_bytes_per_step": draft_b + verify_b, "achieved_GBps": step_gbps,
                 "peak_GBps": HBM_PEAK_GBPS, "frac": step_gbps / HBM_PEAK_GBPS},
-        "roofline": {"kernel": ("draft_resident_kernel (all K Markov steps, w2 held on chip)" if n_launch == 1 else
+        "roofline": {"kernel": ("topk_chunk_kernel (base logits streamed once, -inf cache rows, chunk top-k)"
+                                if a.variant == "topk" else
+                                "draft_resident_kernel (all K Markov steps, w2 held on chip)" if n_launch == 1 else
                                 "draft_wave_kernel (one Markov step, w2 streamed)"),
                      "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
@@ -271,7 +302,8 @@ def main():
         torch.cuda.synchronize()
         res["copy_calibration_bytes"] = {"read": src.numel() * 4, "write": dst.numel() * 4}
     if not a.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(wl, min(a.cpu_sample, B))
+        kw = {"topk": a.topk} if a.variant == "topk" else ({"fp64_gumbel": True} if a.variant == "fp64" else {})
+        res["cpu_baseline"] = cpu_baseline(wl, min(a.cpu_sample, B), **kw)
     print(json.dumps(res), flush=True)
 
 

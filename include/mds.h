@@ -238,6 +238,57 @@ int mds_markov_draft_loop_ex(int B, int K, int V, int r,
                              void* ev_begin, void* ev_end, int* n_step_launches);
 
 /*
+ * mds_draft_topk_workspace_bytes - workspace size of mds_markov_draft_loop_topk:
+ * 256 bytes of status, 8 * B*K*ceil(V/8192)*topk bytes of per-chunk
+ * candidates and 4 * B*K*topk bytes of candidate columns (each 256-aligned).
+ * Errors as for mds_markov_draft_loop_topk's size checks.
+ */
+int mds_draft_topk_workspace_bytes(int B, int K, int V, int r, int topk, size_t* out_bytes);
+
+/*
+ * mds_markov_draft_loop_topk - top-k Markov drafting (DSparkSpeculator API
+ * page, _sample_sequential_topk): the draft loop of mds_markov_draft_loop_ex
+ * with the Markov bias applied only to each step's topk candidates.
+ *
+ * For every (b, k) that is not inert, the candidates are the topk largest of
+ * base[b, k, :], chosen once from the base logits alone: ordered by value
+ * with NaN above every number, -0 equal to +0, and the lower column first
+ * among equal values. The cache row (b, k) (mapped as in _ex) is then written
+ * in full: -inf at every other column and, at candidate v,
+ *   z_v = fp32(base[b,k,v]) + sum_j w2[v,j] * w1[prev_b, j]
+ * (float32 accumulation), rounded to the cache dtype. The draft token is the
+ * Gumbel-max winner of that row exactly as in the dense loop (noise keyed by
+ * column, (seed, sample_pos - 1), MDS_SALT_DRAFT; temperature; the first NaN,
+ * else the first maximum, so a row of -inf only gives token 0), and draft_lse
+ * is the log-sum-exp of the row / T over the candidates (NaN for greedy and
+ * inert rows). Verification reads the cache unchanged.
+ *
+ * Arguments as for mds_markov_draft_loop_ex, plus:
+ *   topk        1 <= topk <= min(256, V), and ceil(V/8192) * topk <= 7168
+ *               (else MDS_ERR_INVALID_ARG / MDS_ERR_UNSUPPORTED);
+ *   flags       MDS_DRAFT_FP64_GUMBEL: float64 variates and scores, winner
+ *               taken exactly over the float64 scores;
+ *   workspace   >= mds_draft_topk_workspace_bytes(B, K, V, r, topk) bytes,
+ *               256-byte aligned, status word zeroed before first use;
+ *   ev_begin / ev_end  hipEvent_t (as void*) or NULL: recorded around the
+ *               candidate-selection launch (the kernel that streams the base
+ *               logits and writes the -inf cache rows).
+ * Launches three kernels on `stream`: selection (one work-group per
+ * 8192-column chunk of a row), merge (one per row) and the K-step chain (one
+ * per request).
+ */
+int mds_markov_draft_loop_topk(int B, int K, int V, int r, int topk,
+                               const void* base, int base_dtype, int64_t base_req_stride,
+                               int64_t base_step_stride, const void* w1, const void* w2,
+                               const int32_t* anchor_tokens, const int32_t* idx_map, const int64_t* sample_pos,
+                               int n_slots, const float* temperature, const int64_t* seeds,
+                               const int32_t* row_mapping, int n_cache_rows,
+                               void* cache, int cache_dtype, int64_t cache_row_stride, int64_t cache_step_stride,
+                               int32_t* draft_tokens, float* draft_lse, uint32_t flags,
+                               void* workspace, size_t workspace_bytes, void* stream,
+                               void* ev_begin, void* ev_end);
+
+/*
  * mds_rejection_verify_indexed - mds_rejection_verify with request-state
  * indexing: request b uses state slot s = idx_map[b] (temperature[s],
  * seeds[s], top_p[s], arrays of n_slots) and draft-logits cache rows

@@ -58,6 +58,10 @@ _SIGS = {
                                                  _vp, _vp, _c_int, _vp, _c_int, _c_i64, _c_i64, _vp, _vp,
                                                  ctypes.c_uint32, _vp, _c_sz, _vp, _vp, _vp, ctypes.POINTER(_c_int)],
                                  _c_int),
+    "mds_draft_topk_workspace_bytes": ([_c_int] * 5 + [ctypes.POINTER(_c_sz)], _c_int),
+    "mds_markov_draft_loop_topk": ([_c_int] * 5 + [_vp, _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _c_int, _vp,
+                                                   _vp, _vp, _c_int, _vp, _c_int, _c_i64, _c_i64, _vp, _vp,
+                                                   ctypes.c_uint32, _vp, _c_sz, _vp, _vp, _vp], _c_int),
     "mds_rejection_verify_indexed": ([_c_int] * 3 + [_vp, _c_i64, _vp, _c_int, _c_i64, _c_i64, _c_int, _vp, _vp, _vp,
                                                      _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp],
                                      _c_int),
@@ -300,6 +304,67 @@ def markov_draft_loop_ex(base, w1, w2, anchor_tokens, idx_map, sample_pos, tempe
         workspace.numel(), _stream(stream, base.device), ev[0], ev[1], ctypes.byref(n))
     _check(rc, "markov_draft_loop_ex")
     return (workspace, n.value) if events is not None else workspace
+
+
+def draft_topk_workspace_bytes(B: int, K: int, V: int, r: int, topk: int) -> int:
+    out = _c_sz()
+    _check(_lib().mds_draft_topk_workspace_bytes(B, K, V, r, topk, ctypes.byref(out)), "draft_topk_workspace_bytes")
+    return out.value
+
+
+def markov_draft_loop_topk(base, w1, w2, anchor_tokens, idx_map, sample_pos, temperature, seeds, cache, draft_tokens,
+                           topk, row_mapping=None, draft_lse=None, fp64_gumbel=False, workspace=None, stream=None,
+                           events=None):
+    """Top-k Markov drafting (mds_markov_draft_loop_topk).
+
+    Arguments as for markov_draft_loop_ex, plus topk (candidates per row,
+    1..256). events: optional (begin, end) torch.cuda.Event pair recorded
+    around the candidate-selection launch.
+    """
+    import torch
+    B, K = draft_tokens.shape
+    V = base.shape[2]
+    _need(base.is_cuda and base.dim() == 3 and base.stride(2) == 1 and base.shape[0] == B and base.shape[1] >= K,
+          "base must be a GPU tensor [B, >=K, V] with unit column stride")
+    _need(cache.dim() == 3 and cache.shape[1] == K and cache.shape[2] == V and cache.stride(2) == 1,
+          "cache must be [n_cache_rows, K, V] with unit column stride")
+    _need(w1.dtype == torch.bfloat16 and w2.dtype == torch.bfloat16 and w1.is_contiguous() and w2.is_contiguous()
+          and w1.shape == w2.shape and w1.shape[0] == V, "w1 and w2 must be contiguous bf16 [V, r]")
+    _need(anchor_tokens.dtype == torch.int32 and anchor_tokens.numel() == B and anchor_tokens.is_contiguous(),
+          "anchor_tokens must be int32 [B]")
+    if idx_map is not None:
+        _need(idx_map.dtype == torch.int32 and idx_map.numel() == B * K and idx_map.is_contiguous(),
+              "idx_map must be int32 [B, K]")
+    _need(sample_pos.dtype == torch.int64 and sample_pos.numel() == B * K and sample_pos.is_contiguous(),
+          "sample_pos must be int64 [B, K]")
+    n_slots = temperature.numel()
+    _need(temperature.dtype == torch.float32 and temperature.is_contiguous(), "temperature must be float32 [n_slots]")
+    _need(seeds.dtype == torch.int64 and seeds.numel() == n_slots and seeds.is_contiguous(),
+          "seeds must be int64 [n_slots]")
+    if row_mapping is not None:
+        _need(row_mapping.dtype == torch.int32 and row_mapping.numel() == n_slots and row_mapping.is_contiguous(),
+              "row_mapping must be int32 [n_slots]")
+    _need(draft_tokens.dtype == torch.int32 and draft_tokens.is_contiguous(), "draft_tokens must be int32 [B, K]")
+    if draft_lse is not None:
+        _need(draft_lse.dtype == torch.float32 and draft_lse.is_contiguous() and draft_lse.numel() == B * K,
+              "draft_lse must be float32 [B, K]")
+    if workspace is None:
+        workspace = new_workspace(draft_topk_workspace_bytes(B, K, V, w1.shape[1], int(topk)), base.device)
+    ev = (None, None)
+    if events is not None:
+        st = stream if stream is not None else torch.cuda.current_stream(base.device)
+        for e in events:  # torch creates the underlying HIP event on its first record
+            if not e.cuda_event:
+                e.record(st)
+        ev = (_vp(events[0].cuda_event), _vp(events[1].cuda_event))
+    rc = _lib().mds_markov_draft_loop_topk(
+        B, K, V, w1.shape[1], int(topk), _ptr(base), _dtype_code(base), base.stride(0), base.stride(1), _ptr(w1),
+        _ptr(w2), _ptr(anchor_tokens), _ptr(idx_map), _ptr(sample_pos), n_slots, _ptr(temperature), _ptr(seeds),
+        _ptr(row_mapping), cache.shape[0], _ptr(cache), _dtype_code(cache), cache.stride(0), cache.stride(1),
+        _ptr(draft_tokens), _ptr(draft_lse), DRAFT_FP64_GUMBEL if fp64_gumbel else 0, _ptr(workspace),
+        workspace.numel(), _stream(stream, base.device), ev[0], ev[1])
+    _check(rc, "markov_draft_loop_topk")
+    return workspace
 
 
 def rejection_verify_indexed(target, cache, draft_tokens, idx_map, temperature, seeds, anchor_pos, out_tokens,

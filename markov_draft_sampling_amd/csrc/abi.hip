@@ -295,6 +295,97 @@ int verify_impl(int B, int K, int V, const float* target, int64_t target_row_str
   return ok();
 }
 
+// Top-k drafting workspace: [status | chunk keys B*K*NC*topk u64 | candidate
+// columns B*K*topk int32]
+struct TopkLayout {
+  int NC;
+  size_t ckeys, cand, total;
+};
+
+TopkLayout topk_layout(int B, int K, int V, int topk) {
+  TopkLayout L;
+  L.NC = (V + mds::kTopkChunk - 1) / mds::kTopkChunk;
+  L.ckeys = kAlign;
+  L.cand = L.ckeys + up((size_t)B * K * L.NC * topk * 8);
+  L.total = L.cand + up((size_t)B * K * topk * 4);
+  return L;
+}
+
+int check_topk(int B, int K, int V, int topk) {
+  if (topk < 1 || topk > mds::kTopkMax || topk > V) return fail(MDS_ERR_INVALID_ARG, "topk must be in [1, min(256, V)]");
+  const long long NC = (V + mds::kTopkChunk - 1) / mds::kTopkChunk;
+  if (NC * topk > mds::kTopkMergeKeys)
+    return fail(MDS_ERR_UNSUPPORTED, "ceil(V / 8192) * topk must be <= 7168");
+  if (NC * B * K > 0x7FFFFFFFLL) return fail(MDS_ERR_UNSUPPORTED, "too many selection work-groups");
+  return MDS_OK;
+}
+
+int topk_impl(int B, int K, int V, int r, int topk, const void* base, int base_dtype, int64_t base_rs,
+              int64_t base_ss, const void* w1, const void* w2, const int32_t* anchor, const float* temperature,
+              const int64_t* seeds, void* cache, int cache_dtype, int64_t cache_rs, int64_t cache_ss,
+              int32_t* draft_tokens, float* draft_lse, void* workspace, size_t ws_bytes, void* stream,
+              void* ev_begin, void* ev_end, const Indexing& ix) {
+  int rc;
+  if ((rc = check_sizes(B, K, V)) || (rc = check_rank(r)) || (rc = check_indexing(ix)) ||
+      (rc = check_topk(B, K, V, topk)))
+    return rc;
+  if (!base || !w1 || !w2 || !anchor || !ix.sample_pos || !temperature || !seeds || !cache || !draft_tokens ||
+      !workspace)
+    return fail(MDS_ERR_INVALID_ARG, "a required pointer is NULL");
+  if ((base_dtype != MDS_F32 && base_dtype != MDS_BF16) || (cache_dtype != MDS_F32 && cache_dtype != MDS_BF16))
+    return fail(MDS_ERR_INVALID_ARG, "dtype must be MDS_F32 or MDS_BF16");
+  if (base_rs < 0 || base_ss < 0) return fail(MDS_ERR_INVALID_ARG, "base strides must be >= 0");
+  const int n_rows = ix.idx_map ? ix.n_rows : B;
+  if (!rows_disjoint(n_rows, K, V, cache_rs, cache_ss))
+    return fail(MDS_ERR_INVALID_ARG, "cache strides make rows overlap or are shorter than V");
+  if (!aligned(w1, 16) || !aligned(w2, 16)) return fail(MDS_ERR_INVALID_ARG, "w1 and w2 must be 16-byte aligned");
+  if (!aligned(workspace, kAlign)) return fail(MDS_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const TopkLayout L = topk_layout(B, K, V, topk);
+  if (ws_bytes < L.total) return fail(MDS_ERR_WORKSPACE, "workspace too small for top-k drafting");
+  unsigned char* ws = (unsigned char*)workspace;
+  hipStream_t st = (hipStream_t)stream;
+  mds::TopkArgs a{};
+  a.B = B;
+  a.K = K;
+  a.V = V;
+  a.r = r;
+  a.topk = topk;
+  a.NC = L.NC;
+  a.base_bf16 = base_dtype == MDS_BF16;
+  a.cache_bf16 = cache_dtype == MDS_BF16;
+  a.vec_base = vec_ok(base, base_dtype, base_rs, base_ss);
+  a.vec_cache = vec_ok(cache, cache_dtype, cache_rs, cache_ss);
+  a.base = base;
+  a.base_rs = base_rs;
+  a.base_ss = base_ss;
+  a.w1 = (const uint16_t*)w1;
+  a.w2 = (const uint16_t*)w2;
+  a.anchor = anchor;
+  a.temp = temperature;
+  a.seeds = (const long long*)seeds;
+  a.cache = cache;
+  a.cache_rs = cache_rs;
+  a.cache_ss = cache_ss;
+  a.tokens = draft_tokens;
+  a.lse = draft_lse;
+  a.ckeys = (unsigned long long*)(ws + L.ckeys);
+  a.cand = (int32_t*)(ws + L.cand);
+  a.status = (uint32_t*)ws;
+  a.idx_map = ix.idx_map;
+  a.row_map = ix.idx_map ? ix.row_map : nullptr;
+  a.sample_pos = (const long long*)ix.sample_pos;
+  a.n_slots = ix.idx_map ? ix.n_slots : B;
+  a.n_rows = n_rows;
+  a.fp64 = (ix.flags & MDS_DRAFT_FP64_GUMBEL) != 0;
+  hipError_t e;
+  if (ev_begin && (e = hipEventRecord((hipEvent_t)ev_begin, st)) != hipSuccess) return hip_fail(e, "event record");
+  if ((e = mds::launch_topk_select(a, st)) != hipSuccess) return hip_fail(e, "top-k selection launch");
+  if (ev_end && (e = hipEventRecord((hipEvent_t)ev_end, st)) != hipSuccess) return hip_fail(e, "event record");
+  if ((e = mds::launch_topk_merge(a, st)) != hipSuccess) return hip_fail(e, "top-k merge launch");
+  if ((e = mds::launch_topk_chain(a, st)) != hipSuccess) return hip_fail(e, "top-k chain launch");
+  return ok();
+}
+
 }  // namespace
 
 namespace mds {
@@ -346,6 +437,36 @@ int mds_draft_workspace_bytes(int B, int K, int V, int r, size_t* out_bytes) {
   if (!out_bytes) return fail(MDS_ERR_INVALID_ARG, "out_bytes is NULL");
   *out_bytes = draft_layout(B, K, V).total;
   return ok();
+}
+
+int mds_draft_topk_workspace_bytes(int B, int K, int V, int r, int topk, size_t* out_bytes) {
+  int rc;
+  if ((rc = check_sizes(B, K, V)) || (rc = check_rank(r)) || (rc = check_topk(B, K, V, topk))) return rc;
+  if (!out_bytes) return fail(MDS_ERR_INVALID_ARG, "out_bytes is NULL");
+  *out_bytes = topk_layout(B, K, V, topk).total;
+  return ok();
+}
+
+int mds_markov_draft_loop_topk(int B, int K, int V, int r, int topk, const void* base, int base_dtype,
+                               int64_t base_req_stride, int64_t base_step_stride, const void* w1, const void* w2,
+                               const int32_t* anchor_tokens, const int32_t* idx_map, const int64_t* sample_pos,
+                               int n_slots, const float* temperature, const int64_t* seeds,
+                               const int32_t* row_mapping, int n_cache_rows, void* cache, int cache_dtype,
+                               int64_t cache_row_stride, int64_t cache_step_stride, int32_t* draft_tokens,
+                               float* draft_lse, uint32_t flags, void* workspace, size_t workspace_bytes,
+                               void* stream, void* ev_begin, void* ev_end) {
+  if (!idx_map && (row_mapping || n_slots < B || n_cache_rows < B))
+    return fail(MDS_ERR_INVALID_ARG, "without idx_map: no row_mapping, n_slots >= B and n_cache_rows >= B");
+  Indexing ix;
+  ix.idx_map = idx_map;
+  ix.row_map = row_mapping;
+  ix.sample_pos = sample_pos;
+  ix.n_slots = n_slots;
+  ix.n_rows = n_cache_rows;
+  ix.flags = flags;
+  return topk_impl(B, K, V, r, topk, base, base_dtype, base_req_stride, base_step_stride, w1, w2, anchor_tokens,
+                   temperature, seeds, cache, cache_dtype, cache_row_stride, cache_step_stride, draft_tokens,
+                   draft_lse, workspace, workspace_bytes, stream, ev_begin, ev_end, ix);
 }
 
 int mds_verify_workspace_bytes(int B, int K, int V, int has_top_p, int has_draft_lse, size_t* out_bytes) {

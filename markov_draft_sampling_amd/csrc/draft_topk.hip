@@ -1,0 +1,495 @@
+// Top-k Markov drafting (DSparkSpeculator API page, _sample_sequential_topk).
+//
+// The candidates of every (request, step) row are the k largest of that
+// step's base logits, chosen once for all steps. Each step then applies the
+// Markov bias at those columns only, through k gathered rows of w2; every
+// other entry of the row is -inf, and the row goes through the same sampler
+// and cache write as the dense loop (so verification reads it unchanged).
+//
+// Three launches on the caller's stream:
+//  1. topk_chunk_kernel, one work-group per 8192-column chunk of a row:
+//     streams the chunk's base logits, writes -inf over the same cache
+//     columns, and keeps the chunk's k largest entries.
+//  2. topk_merge_kernel, one work-group per row: the k largest of the
+//     chunks' survivors, in increasing column order.
+//  3. topk_chain_kernel, one work-group per request: the K sequential steps,
+//     each over the k candidates of its row.
+//
+// Selection order: the winner rule's total order (NaN above every number,
+// -0 == +0, the lower column first among equal values), encoded in the
+// 64-bit winner key ord(value) << 32 | ~column, so that "the k largest keys"
+// is the whole rule and every key is distinct. Key 0 means "no entry".
+#include "mds_device.h"
+#include "mds_internal.h"
+
+namespace mds {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kPerThread = kTopkChunk / kThreads;  // 32 base logits per thread
+
+// -------------------------------------------------- block radix select --
+// Block-wide (256 threads) search for the k largest of n distinct keys held
+// in LDS, most significant byte first. On return, the selected keys are
+// exactly those with (key & mask) >= prefix. Requires n >= k >= 1.
+struct SelectState {
+  unsigned long long prefix;
+  int need, done;
+};
+
+__device__ void block_select_top(const unsigned long long* keys, int n, int k, unsigned* hist, unsigned* wtot,
+                                 SelectState* st, unsigned long long& prefix, unsigned long long& mask) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  prefix = 0;
+  mask = 0;
+  int need = k;  // keys still to take among those whose masked bits equal prefix
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    hist[t] = 0u;
+    __syncthreads();
+    for (int i = t; i < n; i += kThreads) {
+      const unsigned long long key = keys[i];
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    // s = keys in digit bins >= t (suffix sum over the 256 bins)
+    const unsigned h = hist[t];
+    unsigned s = h;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const unsigned o = __shfl_down(s, off);
+      if (lane + off < 64) s += o;
+    }
+    if (lane == 0) wtot[w] = s;
+    __syncthreads();
+    for (int u = w + 1; u < kThreads / 64; ++u) s += wtot[u];
+    if (s >= (unsigned)need && s - h < (unsigned)need) {  // the bin holding the need-th largest key
+      const int rest = need - (int)(s - h);
+      st->prefix = prefix | ((unsigned long long)t << shift);
+      st->need = rest;
+      st->done = (int)h == rest;
+    }
+    __syncthreads();
+    prefix = st->prefix;
+    need = st->need;
+    mask |= 0xFFull << shift;
+    if (st->done) break;  // every key of the bin is taken
+  }
+}
+
+// ------------------------------------------------------------ loads --
+template <bool BF16>
+__device__ __forceinline__ void load4(const void* row, int c, int V, bool vec, float v[4]) {
+  if (vec && c + 3 < V) {
+    if (BF16) {
+      const u32x2 x = *(const u32x2*)((const uint16_t*)row + c);
+      v[0] = __uint_as_float(x.x << 16);
+      v[1] = __uint_as_float(x.x & 0xFFFF0000u);
+      v[2] = __uint_as_float(x.y << 16);
+      v[3] = __uint_as_float(x.y & 0xFFFF0000u);
+    } else {
+      const f32x4 x = *(const f32x4*)((const float*)row + c);
+      v[0] = x.x;
+      v[1] = x.y;
+      v[2] = x.z;
+      v[3] = x.w;
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = 0.0f;
+    if (c + i < V)
+      v[i] = BF16 ? bf16_bits_to_f32(((const uint16_t*)row)[c + i]) : ((const float*)row)[c + i];
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_neg_inf4(void* row, int c, int V, bool vec) {
+  if (vec && c + 3 < V) {
+    if (BF16)
+      *(u32x2*)((uint16_t*)row + c) = u32x2{0xFF80FF80u, 0xFF80FF80u};
+    else
+      *(f32x4*)((float*)row + c) = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (c + i < V) {
+      if (BF16)
+        ((uint16_t*)row)[c + i] = 0xFF80u;
+      else
+        ((float*)row)[c + i] = -INFINITY;
+    }
+  }
+}
+
+__device__ __forceinline__ int row_slot(const TopkArgs& a, int b, int k, uint32_t* status) {
+  return draft_slot(a.idx_map, a.row_map, a.B, a.K, a.n_slots, a.n_rows, status, b, k);
+}
+__device__ __forceinline__ int slot_cache_row(const TopkArgs& a, int b, int s) {
+  return !a.idx_map ? b : (a.row_map ? a.row_map[s] : s);
+}
+
+// ------------------------------------------------- 1. chunk selection --
+// Thread t holds columns c0 + 1024 j + 4 t + i (j < 8, i < 4). The k-th
+// largest of the 256 per-thread maxima, t0, is a lower bound of the chunk's
+// k-th largest key, and only the k threads whose maximum reaches t0 can hold
+// keys >= t0: at most 32 k survivors go to LDS for the exact selection.
+template <bool BBF16, bool CBF16>
+__global__ __launch_bounds__(kThreads) void topk_chunk_kernel(TopkArgs a) {
+  extern __shared__ unsigned long long s_keys[];  // [32 * topk]
+  __shared__ unsigned long long s_tmax[kThreads];
+  __shared__ unsigned s_hist[256];
+  __shared__ unsigned s_wtot[4];
+  __shared__ SelectState s_st;
+  __shared__ unsigned long long s_t0;
+  __shared__ int s_n, s_out;
+  const int chunk = blockIdx.x % a.NC;
+  const int row = blockIdx.x / a.NC;
+  const int b = row / a.K, k = row - b * a.K;
+  const int sl = row_slot(a, b, k, nullptr);
+  if (sl < 0) return;  // inert row: no cache write, no candidates (uniform over the block)
+  const int tid = threadIdx.x;
+  const int V = a.V;
+  const int c0 = chunk * kTopkChunk;
+  const void* brow = BBF16 ? (const void*)((const uint16_t*)a.base + b * a.base_rs + k * a.base_ss)
+                           : (const void*)((const float*)a.base + b * a.base_rs + k * a.base_ss);
+  const long long crow_off = (long long)slot_cache_row(a, b, sl) * a.cache_rs + (long long)k * a.cache_ss;
+  void* crow = CBF16 ? (void*)((uint16_t*)a.cache + crow_off) : (void*)((float*)a.cache + crow_off);
+  if (tid == 0) {
+    s_t0 = 0ull;
+    s_n = 0;
+    s_out = 0;
+  }
+  float v[kPerThread];
+#pragma unroll
+  for (int j = 0; j < kPerThread / 4; ++j) load4<BBF16>(brow, c0 + 1024 * j + 4 * tid, V, a.vec_base != 0, v + 4 * j);
+#pragma unroll
+  for (int j = 0; j < kPerThread / 4; ++j) store_neg_inf4<CBF16>(crow, c0 + 1024 * j + 4 * tid, V, a.vec_cache != 0);
+
+  unsigned long long tmax = 0ull;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    const int c = c0 + 1024 * (j >> 2) + 4 * tid + (j & 3);
+    const unsigned long long key = c < V ? win_key(v[j], (uint32_t)c) : 0ull;
+    tmax = key > tmax ? key : tmax;
+  }
+  s_tmax[tid] = tmax;
+  __syncthreads();
+  int above = 0;  // thread maxima larger than this thread's
+  for (int u = 0; u < kThreads; u += 2) {
+    const unsigned long long x0 = s_tmax[u], x1 = s_tmax[u + 1];
+    above += (x0 > tmax) + (x1 > tmax);
+  }
+  if (tmax != 0ull && above == a.topk - 1) s_t0 = tmax;  // distinct nonzero keys: one writer at most
+  __syncthreads();
+  const unsigned long long t0 = s_t0 ? s_t0 : 1ull;
+  const int cap = kPerThread * a.topk;
+  if (tmax >= t0) {
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int c = c0 + 1024 * (j >> 2) + 4 * tid + (j & 3);
+      const unsigned long long key = c < V ? win_key(v[j], (uint32_t)c) : 0ull;
+      if (key >= t0) {
+        const int i = atomicAdd(&s_n, 1);
+        if (i < cap) s_keys[i] = key;
+      }
+    }
+  }
+  __syncthreads();
+  const int n = min(s_n, cap);
+  unsigned long long* out = a.ckeys + ((size_t)row * a.NC + chunk) * a.topk;
+  if (n <= a.topk) {  // every survivor is kept; the rest of the slots say "none"
+    for (int i = tid; i < a.topk; i += kThreads) out[i] = i < n ? s_keys[i] : 0ull;
+    return;
+  }
+  unsigned long long prefix, mask;
+  block_select_top(s_keys, n, a.topk, s_hist, s_wtot, &s_st, prefix, mask);
+  for (int i = tid; i < n; i += kThreads) {
+    const unsigned long long key = s_keys[i];
+    if ((key & mask) >= prefix) {
+      const int i2 = atomicAdd(&s_out, 1);
+      if (i2 < a.topk) out[i2] = key;
+    }
+  }
+}
+
+// ------------------------------------------------------- 2. row merge --
+__global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a) {
+  __shared__ unsigned long long s_keys[kTopkMergeKeys];
+  __shared__ unsigned long long s_sel[kTopkMax];
+  __shared__ unsigned s_hist[256];
+  __shared__ unsigned s_wtot[4];
+  __shared__ SelectState s_st;
+  __shared__ int s_n;
+  const int row = blockIdx.x;
+  const int b = row / a.K, k = row - b * a.K;
+  if (row_slot(a, b, k, nullptr) < 0) return;
+  const int tid = threadIdx.x;
+  const int n = a.NC * a.topk;
+  const unsigned long long* in = a.ckeys + (size_t)row * n;
+  for (int i = tid; i < n; i += kThreads) s_keys[i] = in[i];
+  if (tid == 0) s_n = 0;
+  __syncthreads();
+  unsigned long long prefix = 0ull, mask = 0ull;  // n == topk: every key is taken
+  if (n > a.topk) block_select_top(s_keys, n, a.topk, s_hist, s_wtot, &s_st, prefix, mask);
+  for (int i = tid; i < n; i += kThreads) {
+    const unsigned long long key = s_keys[i];
+    if (key != 0ull && (key & mask) >= prefix) {
+      const int i2 = atomicAdd(&s_n, 1);
+      if (i2 < a.topk) s_sel[i2] = key;
+    }
+  }
+  __syncthreads();
+  // increasing column order: a candidate's rank is the number of lower
+  // columns (m == topk, as a row has V >= topk entries; a shortfall would
+  // leave -1, "no candidate")
+  const int m = min(s_n, a.topk);
+  if (tid < m) {
+    const uint32_t c = win_col(s_sel[tid]);
+    int rank = 0;
+    for (int u = 0; u < m; ++u) rank += win_col(s_sel[u]) < c;
+    a.cand[(size_t)row * a.topk + rank] = (int32_t)c;
+  } else if (tid < a.topk) {
+    a.cand[(size_t)row * a.topk + tid] = -1;
+  }
+}
+
+// ------------------------------------------------------ 3. the chain --
+// Winner of two (score, column) entries under the winner rule; col < 0 is
+// "no entry".
+template <typename S>
+__device__ __forceinline__ void better(S& s, int& c, S s2, int c2) {
+  bool take;
+  if (c2 < 0)
+    take = false;
+  else if (c < 0)
+    take = true;
+  else if (s2 != s2 || s != s)
+    take = (s2 != s2) && (s == s || c2 < c);
+  else
+    take = s2 > s || (s2 == s && c2 < c);
+  s = take ? s2 : s;
+  c = take ? c2 : c;
+}
+
+template <typename S>
+__device__ __forceinline__ void wave_better(S& s, int& c) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const S s2 = __shfl_xor(s, off);
+    const int c2 = __shfl_xor(c, off);
+    better(s, c, s2, c2);
+  }
+}
+
+__device__ __forceinline__ float dot8(u32x4 w, const float* e) {
+  float acc = 0.0f;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const uint32_t x = h == 0 ? w.x : (h == 1 ? w.y : (h == 2 ? w.z : w.w));
+    acc = __builtin_fmaf(__uint_as_float(x << 16), e[2 * h], acc);
+    acc = __builtin_fmaf(__uint_as_float(x & 0xFFFF0000u), e[2 * h + 1], acc);
+  }
+  return acc;
+}
+
+constexpr int kChainBatch = 8;  // 16-byte w2 chunks a thread loads ahead of the embedding
+
+template <bool BBF16, bool CBF16, bool F64>
+__global__ __launch_bounds__(kThreads) void topk_chain_kernel(TopkArgs a, int tpc) {
+  using Score = typename std::conditional<F64, double, float>::type;
+  __shared__ float s_e[512];
+  __shared__ Score s_ws[4];
+  __shared__ int s_wc[4];
+  __shared__ float s_wm[4], s_wsum[4];
+  __shared__ int s_wnan[4];
+  __shared__ int s_prev;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int r = a.r, nch = r >> 3;
+  const int ci = tid / tpc, part = tid - ci * tpc;
+  if (tid == 0) s_prev = a.anchor[b];
+  for (int k = 0; k < a.K; ++k) {
+    const int row = b * a.K + k;
+    const int sl = row_slot(a, b, k, tid == 0 ? a.status : nullptr);
+    __syncthreads();  // s_prev of the previous step is visible; s_e is free
+    if (sl < 0) {  // inert step: no sample, no cache write; the next step has no previous token
+      if (tid == 0) {
+        a.tokens[row] = -1;
+        if (a.lse) a.lse[row] = NAN;
+        s_prev = -1;
+      }
+      continue;
+    }
+    // w2 rows of the candidates and their base logits go out first
+    const int cc = ci < a.topk ? a.cand[(size_t)row * a.topk + ci] : -1;
+    const bool has = cc >= 0 && cc < a.V;
+    const int col = has ? cc : 0;
+    const uint16_t* w2row = a.w2 + (size_t)col * r;
+    u32x4 wch[kChainBatch];
+#pragma unroll
+    for (int q = 0; q < kChainBatch; ++q) {
+      const int j = part + q * tpc;
+      if (has && j < nch) wch[q] = *(const u32x4*)(w2row + 8 * j);
+    }
+    float bv = 0.0f;
+    if (has && part == 0) {
+      bv = BBF16 ? bf16_bits_to_f32(((const uint16_t*)a.base)[b * a.base_rs + k * a.base_ss + col])
+                 : ((const float*)a.base)[b * a.base_rs + k * a.base_ss + col];
+    }
+    // embedding of the previous token
+    long long tk = s_prev;
+    if (tk < 0 || tk >= a.V) {
+      if (tid == 0) set_status(a.status, kStatusBadAnchor);
+      tk = 0;
+    }
+    for (int j = tid; j < nch; j += kThreads) {
+      const u32x4 x = *(const u32x4*)(a.w1 + (size_t)tk * r + 8 * j);
+      const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        s_e[8 * j + 2 * h] = __uint_as_float(xs[h] << 16);
+        s_e[8 * j + 2 * h + 1] = __uint_as_float(xs[h] & 0xFFFF0000u);
+      }
+    }
+    __syncthreads();
+    float acc = 0.0f;
+#pragma unroll
+    for (int q = 0; q < kChainBatch; ++q) {
+      const int j = part + q * tpc;
+      if (has && j < nch) acc += dot8(wch[q], s_e + 8 * j);
+    }
+    for (int j = part + kChainBatch * tpc; has && j < nch; j += tpc)
+      acc += dot8(*(const u32x4*)(w2row + 8 * j), s_e + 8 * j);
+    for (int off = tpc >> 1; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+
+    // biased logit, cache write, score and log-sum-exp terms at the candidate
+    const float T = a.temp[sl];
+    const bool samp = T > 0.0f;
+    Score s = (Score)0;
+    int c = -1;
+    float x = -INFINITY;
+    int xnan = 0;
+    if (has && part == 0) {
+      const float z = bv + acc;
+      const long long off = (long long)slot_cache_row(a, b, sl) * a.cache_rs + (long long)k * a.cache_ss + col;
+      float cv = z;
+      if (CBF16) {
+        const uint32_t hb = f32_to_bf16_bits(z);
+        ((uint16_t*)a.cache)[off] = (uint16_t)hb;
+        cv = bf16_bits_to_f32(hb);
+      } else {
+        ((float*)a.cache)[off] = z;
+      }
+      c = col;
+      if (samp) {
+        const float invT = 1.0f / T;
+        const unsigned long long seed = (unsigned long long)a.seeds[sl];
+        const unsigned long long pos = (unsigned long long)(a.sample_pos[row] - 1);
+        const Philox4 w = philox4x32_10((uint32_t)col >> 2, (uint32_t)pos, (uint32_t)(pos >> 32), kSaltDraft,
+                                        (uint32_t)seed, (uint32_t)(seed >> 32));
+        const uint32_t sel = col & 3;
+        const uint32_t wd = sel == 0 ? w.x0 : (sel == 1 ? w.x1 : (sel == 2 ? w.x2 : w.x3));
+        if (F64)
+          s = (Score)((double)z / (double)T + gumbel64_from_word(wd));
+        else
+          s = (Score)(div_t(z, T, invT) + gumbel_from_word(wd));
+        x = div_t(cv, T, invT);
+        xnan = x != x;
+        if (xnan) x = -INFINITY;
+      } else {
+        s = (Score)z;
+      }
+    }
+    // winner, and max / NaN flag of cache / T
+    wave_better(s, c);
+    float m = wave_max_f32(x);
+    int anynan = __any(xnan) ? 1 : 0;
+    if (lane == 0) {
+      s_ws[wv] = s;
+      s_wc[wv] = c;
+      s_wm[wv] = m;
+      s_wnan[wv] = anynan;
+    }
+    __syncthreads();
+    s = s_ws[0];
+    c = s_wc[0];
+    m = s_wm[0];
+    anynan = s_wnan[0];
+    for (int u = 1; u < 4; ++u) {
+      better(s, c, s_ws[u], s_wc[u]);
+      m = fmaxf(m, s_wm[u]);
+      anynan |= s_wnan[u];
+    }
+    // an all -inf row: every column ties at -inf and the first column wins
+    const int token = (c < 0 || (s == -(Score)INFINITY)) ? 0 : c;
+    float lse = NAN;
+    if (samp && !anynan && (m == INFINITY || m == -INFINITY)) {
+      lse = m;
+    } else if (samp && !anynan) {
+      float e = (has && part == 0 && x > -INFINITY) ? __expf(x - m) : 0.0f;
+      e = wave_sum_f32(e);
+      if (lane == 0) s_wsum[wv] = e;
+      __syncthreads();
+      lse = m + __logf(s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3]);
+    }
+    if (tid == 0) {
+      a.tokens[row] = token;
+      if (a.lse) a.lse[row] = lse;
+      s_prev = token;
+    }
+  }
+}
+
+template <bool BBF16, bool CBF16>
+hipError_t launch_select_t(const TopkArgs& a, hipStream_t st) {
+  const size_t lds = topk_chunk_lds(a.topk);
+  if (lds + 4096 > 65536) {  // with the kernel's static LDS
+    const hipError_t e = hipFuncSetAttribute((const void*)topk_chunk_kernel<BBF16, CBF16>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((topk_chunk_kernel<BBF16, CBF16>), dim3(a.NC * a.B * a.K), dim3(kThreads), lds, st, a);
+  return hipGetLastError();
+}
+
+template <bool BBF16, bool CBF16, bool F64>
+hipError_t launch_chain_t(const TopkArgs& a, hipStream_t st) {
+  // threads per candidate: a power of two, at most a wave and at most the
+  // rank's 16-byte chunks
+  int kp = 1;
+  while (kp < a.topk) kp <<= 1;
+  int tpc = kThreads / kp;
+  if (tpc > 64) tpc = 64;
+  while (tpc > 1 && tpc > (a.r >> 3)) tpc >>= 1;
+  hipLaunchKernelGGL((topk_chain_kernel<BBF16, CBF16, F64>), dim3(a.B), dim3(kThreads), 0, st, a, tpc);
+  return hipGetLastError();
+}
+
+template <bool F64>
+hipError_t launch_chain_f(const TopkArgs& a, hipStream_t st) {
+  if (a.base_bf16)
+    return a.cache_bf16 ? launch_chain_t<true, true, F64>(a, st) : launch_chain_t<true, false, F64>(a, st);
+  return a.cache_bf16 ? launch_chain_t<false, true, F64>(a, st) : launch_chain_t<false, false, F64>(a, st);
+}
+
+}  // namespace
+
+size_t topk_chunk_lds(int topk) { return (size_t)kPerThread * topk * sizeof(unsigned long long); }
+
+hipError_t launch_topk_select(const TopkArgs& a, hipStream_t st) {
+  if (a.base_bf16) return a.cache_bf16 ? launch_select_t<true, true>(a, st) : launch_select_t<true, false>(a, st);
+  return a.cache_bf16 ? launch_select_t<false, true>(a, st) : launch_select_t<false, false>(a, st);
+}
+
+hipError_t launch_topk_merge(const TopkArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(topk_merge_kernel, dim3(a.B * a.K), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_chain(const TopkArgs& a, hipStream_t st) {
+  return a.fp64 ? launch_chain_f<true>(a, st) : launch_chain_f<false>(a, st);
+}
+
+}  // namespace mds

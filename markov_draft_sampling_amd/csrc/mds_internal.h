@@ -96,6 +96,39 @@ hipError_t launch_draft_resident(const DraftStepArgs& a, size_t lds_bytes, hipSt
 constexpr uint32_t kStatusBarrierTimeout = 4u;
 hipError_t launch_draft_finalize(const DraftFinalArgs& a, hipStream_t st);
 
+// ------------------------------------------------- top-k Markov drafting --
+constexpr int kTopkMax = 256;             // candidates per row, at most
+constexpr int kTopkChunk = 8192;          // base-logit columns per selection work-group
+constexpr int kTopkMergeKeys = 7168;      // chunk keys a row's merge holds on chip (chunks * k)
+
+struct TopkArgs {
+  int B, K, V, r, topk, NC;  // NC = chunks per row
+  int base_bf16, cache_bf16, vec_base, vec_cache;
+  const void* base;
+  long long base_rs, base_ss;
+  const uint16_t* w1;
+  const uint16_t* w2;
+  const int32_t* anchor;
+  const float* temp;
+  const long long* seeds;
+  void* cache;
+  long long cache_rs, cache_ss;
+  int32_t* tokens;
+  float* lse;
+  unsigned long long* ckeys;  // [B*K][NC][topk] each chunk's k largest selection keys (0 = none)
+  int32_t* cand;              // [B*K][topk] a row's candidate columns, increasing
+  uint32_t* status;
+  const int32_t* idx_map;     // as in DraftStepArgs
+  const int32_t* row_map;
+  const long long* sample_pos;  // [B][K], required
+  int n_slots, n_rows;
+  int fp64;
+};
+size_t topk_chunk_lds(int topk);
+hipError_t launch_topk_select(const TopkArgs& a, hipStream_t st);
+hipError_t launch_topk_merge(const TopkArgs& a, hipStream_t st);
+hipError_t launch_topk_chain(const TopkArgs& a, hipStream_t st);
+
 // ---------------------------------------------------------- verification --
 constexpr int kStatsChunk = 8192;  // columns per statistics block (the pages' 8192-column blocks)
 

@@ -119,14 +119,22 @@ def _midpoint_near(z32: np.ndarray) -> np.ndarray:
     return np.abs(low.astype(np.int64) - 0x8000) <= 8
 
 
-def compare_draft(wl: Workload, rows, gpu_tokens, gpu_cache, gpu_lse, rep: Report):
-    """Teacher-forced oracle on requests `rows`; compares tokens, cache and lse."""
+def compare_draft(wl: Workload, rows, gpu_tokens, gpu_cache, gpu_lse, rep: Report, **oracle_kw):
+    """Teacher-forced oracle on requests `rows`; compares tokens, cache and lse.
+
+    oracle_kw: options of the draft loop (topk, fp64_gumbel) passed to the oracle.
+    """
+    with np.errstate(invalid="ignore"):  # inf - inf where both sides hold the same infinity
+        return _compare_draft(wl, rows, gpu_tokens, gpu_cache, gpu_lse, rep, **oracle_kw)
+
+
+def _compare_draft(wl: Workload, rows, gpu_tokens, gpu_cache, gpu_lse, rep: Report, **oracle_kw):
     rows = np.asarray(rows)
     base = wl.draft_base[rows]
     teacher = gpu_tokens[rows]
     args = (base, wl.base_dtype, wl.w1, wl.w2, wl.anchor_tokens[rows], wl.anchor_pos[rows], wl.seeds[rows],
             wl.temperature[rows])
-    ref = oracle.draft_loop(*args, wl.cache_dtype, teacher=teacher)
+    ref = oracle.draft_loop(*args, wl.cache_dtype, teacher=teacher, **oracle_kw)
     # tokens
     mism = ref["tokens"] != teacher
     exc = mism & (ref["margin"] <= TOK_MARGIN)
@@ -142,12 +150,12 @@ def compare_draft(wl: Workload, rows, gpu_tokens, gpu_cache, gpu_lse, rep: Repor
     if wl.cache_dtype == "bf16":
         g = bf16_bits_to_f32(gc).astype(np.float64)
         o = bf16_bits_to_f32(ref["cache"]).astype(np.float64)
-        z32 = oracle.draft_loop(*args, "f32", teacher=teacher)["cache"]
+        z32 = oracle.draft_loop(*args, "f32", teacher=teacher, **oracle_kw)["cache"]
         near = _midpoint_near(z32)
         ulp = np.abs(o) * 2.0 ** -7
         err = np.abs(g - o)
         both_nan = np.isnan(g) & np.isnan(o)
-        bad = ~both_nan & ~(err <= CACHE_TOL)
+        bad = ~both_nan & ~(err <= CACHE_TOL) & (g != o)
         excused = bad & near & (err <= ulp * 1.01)
         bad &= ~excused
         rep.cache_excused += int(excused.sum())
@@ -156,7 +164,7 @@ def compare_draft(wl: Workload, rows, gpu_tokens, gpu_cache, gpu_lse, rep: Repor
         o = ref["cache"].astype(np.float64)
         err = np.abs(g - o)
         both_nan = np.isnan(g) & np.isnan(o)
-        bad = ~both_nan & ~(err <= CACHE_TOL)
+        bad = ~both_nan & ~(err <= CACHE_TOL) & (g != o)
     rep.cache_total += bad.size
     rep.cache_bad += int(bad.sum())
     fin = np.isfinite(err)
@@ -172,7 +180,7 @@ def compare_draft(wl: Workload, rows, gpu_tokens, gpu_cache, gpu_lse, rep: Repor
         ol = ref["lse"][samp]
         err = np.abs(gl - ol)
         both_nan = np.isnan(gl) & np.isnan(ol)
-        badl = ~both_nan & ~(err <= 1e-4 + 1e-5 * np.abs(ol))
+        badl = ~both_nan & ~(err <= 1e-4 + 1e-5 * np.abs(ol)) & (gl != ol)
         rep.lse_bad += int(badl.sum())
         if (~both_nan).any():
             e = err[~both_nan]
