@@ -26,6 +26,7 @@ Parity status per function:
 * ``top_p_keep``        pinned (brute-force threshold formulation on the pages' row families)
 * ``topk_columns``      pinned (torch.topk on distinct values; order invariants with ties, NaN, signed zeros)
 * ``draft_loop(topk=)`` pinned (k = V equals the dense loop; the dense loop on the masked base; k = 1; the law)
+* ``draft_logits``      pinned (exact fsum dot products on small shapes; unit hidden vectors pick lm_head columns)
 """
 from .philox import philox4x32_10, PHILOX_M0, PHILOX_M1, PHILOX_W0, PHILOX_W1  # noqa: F401
 from .noise import (SALT_ACCEPT, SALT_DRAFT, SALT_RESAMPLE, noise_words, uniform24, gumbel,  # noqa: F401
@@ -33,3 +34,4 @@ from .noise import (SALT_ACCEPT, SALT_DRAFT, SALT_RESAMPLE, noise_words, uniform
 from .core import argmax_rule, bf16_rne, bf16_to_f64, top_two_margin, topk_columns  # noqa: F401
 from .draft import draft_loop  # noqa: F401
 from .verify import verify, top_p_keep  # noqa: F401
+from .lm_head import draft_logits  # noqa: F401

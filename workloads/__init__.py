@@ -28,7 +28,8 @@ import functools
 
 import numpy as np
 
-__all__ = ["CONFIGS", "Workload", "make_workload", "bf16_bits", "bf16_bits_to_f32", "CFG5_BATCHES", "CFG4_BATCHES"]
+__all__ = ["CONFIGS", "Workload", "make_workload", "bf16_bits", "bf16_bits_to_f32", "CFG5_BATCHES", "CFG4_BATCHES",
+           "make_lm_head"]
 
 CFG4_BATCHES = (1, 8, 32, 128)
 CFG5_BATCHES = (1, 2, 3, 4, 5, 7, 8, 16, 31, 32, 33, 64, 96, 127, 128)
@@ -235,3 +236,21 @@ def make_custom(V: int, r: int, K: int, B: int, *, seed: int = 0, base_std: floa
                     seeds=rng.integers(0, 2**63, size=B, dtype=np.int64),
                     temperature=np.full(B, temperature, np.float32), target=target,
                     top_p=None if top_p is None else np.full(B, top_p, np.float32))
+
+
+def make_lm_head(rows: int, V: int, H: int, *, seed: int = 0, logit_std: float = 3.0):
+    """Seeded draft LM-head inputs: hidden [rows, H] and lm_head [V, H] as bf16 bit patterns.
+
+    hidden ~ N(0, 1) and lm_head ~ N(0, logit_std^2 / H), so the logits
+    hidden @ lm_head^T are ~N(0, logit_std^2) like the configs' base logits.
+    Generated in row chunks to bound host memory.
+    """
+    rng = np.random.default_rng([seed, 11, rows, V, H])
+    hidden = bf16_bits(rng.standard_normal((rows, H), dtype=np.float32))
+    lm = np.empty((V, H), np.uint16)
+    scale = np.float32(logit_std / np.sqrt(H))
+    step = max(1, (1 << 24) // H)
+    for v0 in range(0, V, step):
+        v1 = min(V, v0 + step)
+        lm[v0:v1] = bf16_bits(rng.standard_normal((v1 - v0, H), dtype=np.float32) * scale)
+    return hidden, lm
