@@ -54,6 +54,11 @@ def topk_bytes(B, K, V, r, topk, s_base=4, s_cache=4):
     return select, select + merge + chain
 
 
+def lm_head_bytes(M, V, H, s_out=4):
+    """Draft LM head: lm_head and hidden read once, the base logits written."""
+    return V * H * 2 + M * H * 2 + M * V * s_out
+
+
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "markov_draft_sampling_amd", "csrc")
 
@@ -76,9 +81,10 @@ def recorded_traffic(profile: str, sources) -> float | None:
     return float(fields["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(wl, n_req: int, repeats: int = 2, **draft_kw):
+def cpu_baseline(wl, n_req: int, repeats: int = 2, lm=None, **draft_kw):
     """The oracle, as it stands, on the first n_req requests of the workload
-    (draft_kw: the draft loop's options, topk or fp64_gumbel)."""
+    (draft_kw: the draft loop's options, topk or fp64_gumbel; lm: (hidden,
+    lm_head) bf16 bits, whose LM head then gives the base logits)."""
     import numpy as np
     import oracle
     try:
@@ -91,7 +97,10 @@ def cpu_baseline(wl, n_req: int, repeats: int = 2, **draft_kw):
     tgt = wl.target.reshape(wl.B, K + 1, wl.V)[rows].reshape(n_req * (K + 1), wl.V)
     t0 = time.perf_counter()
     for _ in range(repeats):
-        d = oracle.draft_loop(wl.draft_base[rows], wl.base_dtype, wl.w1, wl.w2, wl.anchor_tokens[rows],
+        base = wl.draft_base[rows]
+        if lm is not None:
+            base = oracle.draft_logits(lm[0][: n_req * K], lm[1]).reshape(n_req, K, wl.V)
+        d = oracle.draft_loop(base, wl.base_dtype, wl.w1, wl.w2, wl.anchor_tokens[rows],
                               wl.anchor_pos[rows], wl.seeds[rows], wl.temperature[rows], wl.cache_dtype, **draft_kw)
         oracle.verify(tgt, d["cache"], wl.cache_dtype, d["tokens"], wl.temperature[rows],
                       None if wl.top_p is None else wl.top_p[rows], wl.seeds[rows], wl.anchor_pos[rows])
@@ -99,7 +108,8 @@ def cpu_baseline(wl, n_req: int, repeats: int = 2, **draft_kw):
     if ctx is not None:
         ctx.unregister() if hasattr(ctx, "unregister") else None
     return {"value": n_req * K / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_req} of the {wl.B} requests (all {K} draft steps + verification), run {repeats} times, "
+            "sample": f"{n_req} of the {wl.B} requests ({'LM head, ' if lm is not None else ''}all {K} draft steps "
+                      f"+ verification), run {repeats} times, "
                       f"float64 NumPy, BLAS limited to 1 thread; {dt:.1f} s per run"}
 
 
@@ -112,10 +122,12 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=32, help="requests the CPU oracle baseline runs on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="do not flush caches between timed steps")
-    ap.add_argument("--variant", choices=("plain", "indexed", "fp64", "topk"), default="plain",
+    ap.add_argument("--variant", choices=("plain", "indexed", "fp64", "topk", "lmhead"), default="plain",
                     help="plain: batch-indexed draft + verify; indexed: the same work through request-state slots, "
                          "a row mapping and per-step sample positions; fp64: the float64 Gumbel option; topk: "
-                         "top-k Markov drafting (--topk candidates per row)")
+                         "top-k Markov drafting (--topk candidates per row); lmhead: the draft LM head "
+                         "(hidden [B*K, --hidden] x lm_head [V, --hidden]) computes the base logits, then plain")
+    ap.add_argument("--hidden", type=int, default=4096, help="hidden size of --variant lmhead")
     ap.add_argument("--topk", type=int, default=64, help="candidates per row of --variant topk")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB elementwise copy (reference dispatch for counter scaling)")
@@ -156,6 +168,13 @@ def main():
     ws_v = mds.new_workspace(mds.verify_workspace_bytes(B, K, V, False, True), dev)
     flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)  # 512 MiB, read to evict caches
     stream = torch.cuda.current_stream(dev)
+    if a.variant == "lmhead":
+        t_gen = time.perf_counter()
+        hid_np, lm_np = workloads.make_lm_head(B * K, V, a.hidden, seed=1)
+        hidden = torch.from_numpy(hid_np.view(np.int16)).view(torch.bfloat16).to(dev)
+        lm_head = torch.from_numpy(lm_np.view(np.int16)).view(torch.bfloat16).to(dev)
+        print(f"# LM head inputs H={a.hidden} generated in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr,
+              flush=True)
     spos = (apos[:, None] + 1 + torch.arange(K, device=dev)[None, :]).contiguous()
     if a.variant == "indexed":
         # request b lives in slot perm[b] of 2B slots; slot s owns cache row rowmap[s]
@@ -173,6 +192,13 @@ def main():
         s_temp, s_seed = torch.from_numpy(s_temp).to(dev), torch.from_numpy(s_seed).to(dev)
 
     def step(events=None):
+        if a.variant == "lmhead":
+            mds.draft_lm_head(hidden, lm_head, base, K, events=events)
+            if events is not None:
+                launches.append(1)
+            mds.markov_draft_loop(base, w1, w2, anchor, apos, temp, seeds, cache, toks, lse, workspace=ws_d)
+            mds.rejection_verify(target, cache, toks, temp, seeds, apos, out, nacc, draft_lse=lse, workspace=ws_v)
+            return
         if a.variant == "plain":
             if events is None:
                 mds.markov_draft_loop(base, w1, w2, anchor, apos, temp, seeds, cache, toks, lse, workspace=ws_d)
@@ -238,6 +264,9 @@ def main():
     bytes_per_launch = draft_b / n_launch
     if a.variant == "topk":
         bytes_per_launch, draft_b = topk_bytes(B, K, V, r, a.topk)
+    if a.variant == "lmhead":
+        bytes_per_launch = lm_head_bytes(B * K, V, a.hidden)
+        draft_b += bytes_per_launch
     achieved = bytes_per_launch / (kern_avg_ms * 1e-3) / 1e9
     step_gbps = (draft_b + verify_b) / (ms * 1e-3) / 1e9
     acc_len = float((nacc.float() + 1).mean().item())
@@ -250,7 +279,11 @@ def main():
     if a.variant == "topk":
         traffic = recorded_traffic("topk_chunk_kernel_hbm_traffic_V200064_B32.md",
                                    ("draft_topk.hip", "mds_device.h", "mds_internal.h"))
-    if B != 32 or a.variant not in ("plain", "topk") or (a.variant == "topk" and a.topk != 64):
+    if a.variant == "lmhead":
+        traffic = recorded_traffic("lm_head_kernel_hbm_traffic_V200064_B32.md",
+                                   ("lm_head.hip", "mds_device.h", "mds_internal.h"))
+    if (B != 32 or a.variant not in ("plain", "topk", "lmhead") or (a.variant == "topk" and a.topk != 64)
+            or (a.variant == "lmhead" and a.hidden != 4096)):
         traffic = None
     status = mds.workspace_status(ws_d) | mds.workspace_status(ws_v)
 
@@ -270,20 +303,26 @@ def main():
         "config": {"workload": f"Markov draft loop + rejection verify, V={V} r={r} K={K} B={B}, fp32 base/target/"
                                f"cache, bf16 w1/w2, T=1" + {"plain": "", "indexed": ", request-state slots + row "
                                "mapping", "fp64": ", float64 Gumbel",
-                               "topk": f", top-k Markov drafting k={a.topk}"}[a.variant],
+                               "topk": f", top-k Markov drafting k={a.topk}",
+                               "lmhead": f", base logits from the draft LM head (H={a.hidden}, bf16)"}[a.variant],
                    "V": V, "r": r, "K": K, "B": B, "variant": a.variant,
                    **({"topk": a.topk} if a.variant == "topk" else {}),
+                   **({"hidden": a.hidden} if a.variant == "lmhead" else {}),
                    "cache_flushed_between_steps": not a.no_flush},
         "hbm": {"algorithmic_bytes_per_step": draft_b + verify_b, "achieved_GBps": step_gbps,
                 "peak_GBps": HBM_PEAK_GBPS, "frac": step_gbps / HBM_PEAK_GBPS},
         "roofline": {"kernel": ("topk_chunk_kernel (base logits streamed once, -inf cache rows, chunk top-k)"
                                 if a.variant == "topk" else
+                                "lm_head_kernel (draft LM head, bf16 MFMA, lm_head streamed once)"
+                                if a.variant == "lmhead" else
                                 "draft_resident_kernel (all K Markov steps, w2 held on chip)" if n_launch == 1 else
                                 "draft_wave_kernel (one Markov step, w2 streamed)"),
                      "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "bytes_per_launch": bytes_per_launch, "avg_launch_us": kern_avg_ms * 1e3,
-                     "launches": int(n_launch * a.steps)},
+                     "launches": int(n_launch * a.steps),
+                     **({"mfma_TFLOPs": 2.0 * B * K * V * a.hidden / (kern_avg_ms * 1e-3) / 1e12,
+                         "mfma_peak_TFLOPs": 2500.0} if a.variant == "lmhead" else {})},
         "warm": {"ms_per_step": warm_ms, "value": tokens / (warm_ms * 1e-3)},
         "step_ms_p10_p50_p90": [float(np.percentile(step_ms, q)) for q in (10, 50, 90)],
         "draft_kernels_ms": float(np.mean(draft_span_ms)),
@@ -303,7 +342,11 @@ def main():
         res["copy_calibration_bytes"] = {"read": src.numel() * 4, "write": dst.numel() * 4}
     if not a.no_cpu_baseline:
         kw = {"topk": a.topk} if a.variant == "topk" else ({"fp64_gumbel": True} if a.variant == "fp64" else {})
-        res["cpu_baseline"] = cpu_baseline(wl, min(a.cpu_sample, B), **kw)
+        if a.variant == "lmhead":
+            # the LM head dominates the oracle's time: at most 16 requests, once
+            res["cpu_baseline"] = cpu_baseline(wl, min(a.cpu_sample, 16), repeats=1, lm=(hid_np, lm_np))
+        else:
+            res["cpu_baseline"] = cpu_baseline(wl, min(a.cpu_sample, B), **kw)
     print(json.dumps(res), flush=True)
 
 

@@ -289,6 +289,29 @@ int mds_markov_draft_loop_topk(int B, int K, int V, int r, int topk,
                                void* ev_begin, void* ev_end);
 
 /*
+ * mds_draft_lm_head - the draft model's LM head ahead of the loop
+ * (DSparkSpeculator API page, _sample_sequential: compute_draft_logits on the
+ * gathered hidden states, ordered (request, step)).
+ *   out[b, k, v] = sum_h hidden[b*K + k, h] * lm_head[v, h]
+ * bf16 inputs, float32 accumulation (any order), rounded to out_dtype (bf16:
+ * round to nearest even). The output is the base-logit layout the draft loop
+ * reads: row (b, k) at out + b*out_req_stride + k*out_step_stride (elements).
+ * Arguments:
+ *   B, K, V      as for the draft loop (B*K rows)
+ *   H            hidden size, a multiple of 256 (else MDS_ERR_UNSUPPORTED)
+ *   hidden       bf16 [B*K, H], row stride hidden_row_stride >= H elements, a
+ *                multiple of 8; 16-byte aligned
+ *   lm_head      bf16 [V, H] contiguous, 16-byte aligned
+ *   out          MDS_F32 or MDS_BF16, rows as above (must not overlap)
+ *   ev_begin / ev_end  hipEvent_t (as void*) or NULL, recorded around the launch
+ * One kernel launch on `stream`; lm_head is read once from HBM while
+ * B*K <= 256 (each further 256 rows read it again). No workspace.
+ */
+int mds_draft_lm_head(int B, int K, int V, int H, const void* hidden, int64_t hidden_row_stride,
+                      const void* lm_head, void* out, int out_dtype, int64_t out_req_stride,
+                      int64_t out_step_stride, void* stream, void* ev_begin, void* ev_end);
+
+/*
  * mds_rejection_verify_indexed - mds_rejection_verify with request-state
  * indexing: request b uses state slot s = idx_map[b] (temperature[s],
  * seeds[s], top_p[s], arrays of n_slots) and draft-logits cache rows

@@ -62,6 +62,7 @@ _SIGS = {
     "mds_markov_draft_loop_topk": ([_c_int] * 5 + [_vp, _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _c_int, _vp,
                                                    _vp, _vp, _c_int, _vp, _c_int, _c_i64, _c_i64, _vp, _vp,
                                                    ctypes.c_uint32, _vp, _c_sz, _vp, _vp, _vp], _c_int),
+    "mds_draft_lm_head": ([_c_int] * 4 + [_vp, _c_i64, _vp, _vp, _c_int, _c_i64, _c_i64, _vp, _vp, _vp], _c_int),
     "mds_rejection_verify_indexed": ([_c_int] * 3 + [_vp, _c_i64, _vp, _c_int, _c_i64, _c_i64, _c_int, _vp, _vp, _vp,
                                                      _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp],
                                      _c_int),
@@ -365,6 +366,35 @@ def markov_draft_loop_topk(base, w1, w2, anchor_tokens, idx_map, sample_pos, tem
         workspace.numel(), _stream(stream, base.device), ev[0], ev[1])
     _check(rc, "markov_draft_loop_topk")
     return workspace
+
+
+def draft_lm_head(hidden, lm_head, out, K, stream=None, events=None):
+    """Base draft logits from the draft LM head (mds_draft_lm_head).
+
+    hidden bf16 [B*K, H] (row b*K + k, unit column stride), lm_head bf16
+    [V, H] contiguous, out float32 or bf16 [B, >=K, V] with unit column
+    stride (rows k < K are written). events: optional (begin, end)
+    torch.cuda.Event pair recorded around the launch.
+    """
+    import torch
+    V, H = lm_head.shape
+    _need(hidden.is_cuda and hidden.dtype == torch.bfloat16 and hidden.dim() == 2 and hidden.shape[1] == H
+          and hidden.stride(1) == 1 and hidden.shape[0] % K == 0, "hidden must be bf16 [B*K, H] with unit column stride")
+    B = hidden.shape[0] // K
+    _need(lm_head.dtype == torch.bfloat16 and lm_head.is_contiguous(), "lm_head must be contiguous bf16 [V, H]")
+    _need(out.dim() == 3 and out.shape[0] == B and out.shape[1] >= K and out.shape[2] == V and out.stride(2) == 1,
+          "out must be [B, >=K, V] with unit column stride")
+    ev = (None, None)
+    if events is not None:
+        st = stream if stream is not None else torch.cuda.current_stream(hidden.device)
+        for e in events:  # torch creates the underlying HIP event on its first record
+            if not e.cuda_event:
+                e.record(st)
+        ev = (_vp(events[0].cuda_event), _vp(events[1].cuda_event))
+    rc = _lib().mds_draft_lm_head(B, K, V, H, _ptr(hidden), hidden.stride(0), _ptr(lm_head), _ptr(out),
+                                  _dtype_code(out), out.stride(0), out.stride(1), _stream(stream, hidden.device),
+                                  ev[0], ev[1])
+    _check(rc, "draft_lm_head")
 
 
 def rejection_verify_indexed(target, cache, draft_tokens, idx_map, temperature, seeds, anchor_pos, out_tokens,

@@ -469,6 +469,41 @@ int mds_markov_draft_loop_topk(int B, int K, int V, int r, int topk, const void*
                    draft_lse, workspace, workspace_bytes, stream, ev_begin, ev_end, ix);
 }
 
+int mds_draft_lm_head(int B, int K, int V, int H, const void* hidden, int64_t hidden_row_stride, const void* lm_head,
+                      void* out, int out_dtype, int64_t out_req_stride, int64_t out_step_stride, void* stream,
+                      void* ev_begin, void* ev_end) {
+  int rc;
+  if ((rc = check_sizes(B, K, V))) return rc;
+  if (H < 256 || H > 65536 || H % 256) return fail(MDS_ERR_UNSUPPORTED, "H must be a multiple of 256 in [256, 65536]");
+  if (!hidden || !lm_head || !out) return fail(MDS_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (out_dtype != MDS_F32 && out_dtype != MDS_BF16) return fail(MDS_ERR_INVALID_ARG, "out dtype must be MDS_F32 or MDS_BF16");
+  if (hidden_row_stride < H || hidden_row_stride % 8)
+    return fail(MDS_ERR_INVALID_ARG, "hidden_row_stride must be >= H and a multiple of 8");
+  if (!aligned(hidden, 16) || !aligned(lm_head, 16))
+    return fail(MDS_ERR_INVALID_ARG, "hidden and lm_head must be 16-byte aligned");
+  if (!rows_disjoint(B, K, V, out_req_stride, out_step_stride))
+    return fail(MDS_ERR_INVALID_ARG, "out strides make rows overlap or are shorter than V");
+  mds::LmHeadArgs a{};
+  a.M = B * K;
+  a.K = K;
+  a.V = V;
+  a.H = H;
+  a.hidden = (const uint16_t*)hidden;
+  a.hidden_rs = hidden_row_stride;
+  a.lm_head = (const uint16_t*)lm_head;
+  a.out = out;
+  a.out_rs = out_req_stride;
+  a.out_ss = out_step_stride;
+  a.out_bf16 = out_dtype == MDS_BF16;
+  a.vec_out = vec_ok(out, out_dtype, out_req_stride, out_step_stride);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  if (ev_begin && (e = hipEventRecord((hipEvent_t)ev_begin, st)) != hipSuccess) return hip_fail(e, "event record");
+  if ((e = mds::launch_lm_head(a, st)) != hipSuccess) return hip_fail(e, "LM head launch");
+  if (ev_end && (e = hipEventRecord((hipEvent_t)ev_end, st)) != hipSuccess) return hip_fail(e, "event record");
+  return ok();
+}
+
 int mds_verify_workspace_bytes(int B, int K, int V, int has_top_p, int has_draft_lse, size_t* out_bytes) {
   int rc;
   if ((rc = check_sizes(B, K, V))) return rc;

@@ -125,6 +125,18 @@ struct TopkArgs {
   int fp64;
 };
 size_t topk_chunk_lds(int topk);
+
+// ------------------------------------------------------ draft LM head --
+struct LmHeadArgs {
+  int M, K, V, H;             // rows M = B*K (row m = b*K + k), vocabulary, hidden size (a multiple of 256)
+  const uint16_t* hidden;     // [M][H] bf16, row stride hidden_rs elements
+  long long hidden_rs;
+  const uint16_t* lm_head;    // [V][H] bf16, contiguous
+  void* out;                  // row (b, k) at b*out_rs + k*out_ss elements, float32 or bf16
+  long long out_rs, out_ss;
+  int out_bf16, vec_out;
+};
+hipError_t launch_lm_head(const LmHeadArgs& a, hipStream_t st);
 hipError_t launch_topk_select(const TopkArgs& a, hipStream_t st);
 hipError_t launch_topk_merge(const TopkArgs& a, hipStream_t st);
 hipError_t launch_topk_chain(const TopkArgs& a, hipStream_t st);
