@@ -137,9 +137,13 @@ __device__ __forceinline__ void store_col4(void* p, long long off, int n, bool v
 }
 
 // RK = r / 32 (MFMA k-steps per tile), RMT = register-resident tiles per wave
-template <int RK, int RMT>
+// (a multiple of kDepth, so the base-row ring index stays static across the
+// register tiles and the LDS tiles that follow them).
+template <int RK, int RMT, bool BBF16, bool CBF16>
 __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void draft_resident_kernel(
     DraftStepArgs a) {
+  static_assert(RMT % kDepth == 0, "register tiles per wave must be a multiple of the ring depth");
+  static_assert(kNB == 32, "the projection is written for two 16-request MFMA tiles");
   constexpr int NT = kNB / 16;
   constexpr int R = RK * 32;
   constexpr int CPR = R / 8;  // 16-byte chunks per w2 row
@@ -189,14 +193,13 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
   }
 
   // tiles of this wave: register tiles j < R_w, then LDS tiles wave, wave+4, ...
+  // (LDS tiles exist only when every wave holds RMT register tiles)
   int R_w = 0;
 #pragma unroll
   for (int j = 0; j < RMT; ++j) R_w += (wave + 4 * j < n_reg) ? 1 : 0;
   const int L_w = n_lds > wave ? (n_lds - wave + 3) / 4 : 0;
   const int T_w = R_w + L_w;
-  auto tile_col = [&](int t) -> int {  // first column of this wave's t-th tile
-    return t < R_w ? (mt_begin + wave + 4 * t) * 16 : (mt_begin + n_reg + wave + 4 * (t - R_w)) * 16;
-  };
+  const int last = T_w > 0 ? T_w - 1 : 0;
 
   const int BT = (B + kNB - 1) / kNB;
   for (int k = 0; k < a.K; ++k) {
@@ -232,14 +235,11 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         *(u32x4*)(s_e + row * RS + ch * 8) = v;
       }
       __syncthreads();
-
-      // embedding operands (B operand: 16 requests x 32 ranks per MFMA) are read
-      // from LDS at every tile; the runtime-zero offset keeps the compiler from
-      // hoisting them into 64 more registers next to the resident w2
+      // embedding operands (16 requests x 32 ranks per MFMA) are read from
+      // LDS at every tile, all of a tile's reads ahead of its MFMAs; the
+      // runtime-zero offset keeps the compiler from hoisting them into 64
+      // more registers next to the resident w2
       const uint16_t* ebase = s_e + lrow * RS + lgrp * 8;
-      auto bfrag = [&](int s, int nt, int t) -> bf16x8 {
-        return *(const bf16x8*)(ebase + nt * 16 * RS + s * 32 + a.zero * t);
-      };
 
       // per-lane request parameters (rows nt*16 + lrow of the tile)
       bool rv[NT];
@@ -269,25 +269,72 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         qs[nt] = 0.0f;
         qnan[nt] = false;
       }
+      bool all_fast = a.vec_base && a.vec_cache, all_t1 = true;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        all_fast &= rv[nt] && Tv[nt] > 0.0f;
+        all_t1 &= Tv[nt] == 1.0f;
+      }
+      const bool fast_req = __all(all_fast);
+      const bool t1 = __all(all_t1);
 
-      // base rows of the next kDepth-1 tiles stay in flight in a register ring
-      // (the tile loop is unrolled by kDepth so every slot has a static index)
-      float ring[kDepth][NT][4];
+      auto tile_col = [&](int t) -> int {  // first column of this wave's t-th tile
+        return t < R_w ? (mt_begin + wave + 4 * t) * 16 : (mt_begin + n_reg + wave + 4 * (t - R_w)) * 16;
+      };
+      // base rows of this wave's tiles: a ring of kDepth tiles, kDepth - 1
+      // ahead; the last tiles are requested again at the end (cache hits),
+      // so every load is unconditional and in order
       auto load_base = [&](int t, float (&dst)[NT][4]) {
         const int c = tile_col(t) + lgrp * 4;
-        const int n = V - c >= 4 ? 4 : (V - c > 0 ? V - c : 0);
+        if (fast_req && c + 4 <= V) {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          if (rv[nt] && n > 0) {
-            if (a.base_bf16)
-              load_col4<true>(a.base, rbase[nt] + c, n, a.vec_base, dst[nt]);
-            else
-              load_col4<false>(a.base, rbase[nt] + c, n, a.vec_base, dst[nt]);
+          for (int nt = 0; nt < NT; ++nt) load_col4<BBF16>(a.base, rbase[nt] + c, 4, true, dst[nt]);
+        } else {
+          const int n = V - c >= 4 ? 4 : (V - c > 0 ? V - c : 0);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[nt][i] = 0.0f;
+            if (rv[nt] && n > 0) load_col4<BBF16>(a.base, rbase[nt] + c, n, a.vec_base, dst[nt]);
           }
         }
       };
+      // epilogue of one tile from the accumulator layout: lane holds columns
+      // c .. c+3 of request 16 nt + lrow
       auto epilogue = [&](int t, const floatx4 (&acc)[NT], const float (&bz)[NT][4]) {
         const int c = tile_col(t) + lgrp * 4;
+        if (fast_req && tile_col(t) + 16 <= V) {
+          // straight-line form: every request of the tile exists and samples,
+          // full tile, vector stores; a NaN among the q values rides the sum
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            float z[4], cv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) z[i] = bz[nt][i] + acc[nt][i];
+            store_col4<CBF16>(a.cache, rcache[nt] + c, 4, true, z, cv);
+            const Philox4 w = philox4x32_10((uint32_t)(c >> 2), pk0[nt], pk1[nt], kSaltDraft, sk0[nt], sk1[nt]);
+            const uint32_t wd[4] = {w.x0, w.x1, w.x2, w.x3};
+            float x[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float y = t1 ? z[i] : div_t(z[i], Tv[nt], invT[nt]);
+              x[i] = CBF16 ? (t1 ? cv[i] : div_t(cv[i], Tv[nt], invT[nt])) : y;
+              const float sv = y + gumbel_from_word(wd[i]);
+              const bool take = (sv > bv[nt]) || ((sv != sv) && (bv[nt] == bv[nt])) || (bi[nt] < 0);
+              bv[nt] = take ? sv : bv[nt];
+              bi[nt] = take ? c + i : bi[nt];
+            }
+            const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));  // NaN-ignoring max
+            const float mn = fmaxf(qm[nt], mx);
+            const float sub = mn == -INFINITY ? 0.0f : mn;
+            float s_acc = qs[nt] * fast_exp(qm[nt] - sub);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s_acc += fast_exp(x[i] - sub);
+            qs[nt] = s_acc;
+            qm[nt] = mn;
+          }
+          return;
+        }
         const int n = V - c >= 4 ? 4 : (V - c > 0 ? V - c : 0);
         if (n == 0) return;
 #pragma unroll
@@ -296,10 +343,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
           float z[4], cv[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) z[i] = bz[nt][i] + acc[nt][i];
-          if (a.cache_bf16)
-            store_col4<true>(a.cache, rcache[nt] + c, n, a.vec_cache, z, cv);
-          else
-            store_col4<false>(a.cache, rcache[nt] + c, n, a.vec_cache, z, cv);
+          store_col4<CBF16>(a.cache, rcache[nt] + c, n, a.vec_cache, z, cv);
           if (Tv[nt] > 0.0f) {
             const Philox4 w = philox4x32_10((uint32_t)(c >> 2), pk0[nt], pk1[nt], kSaltDraft, sk0[nt], sk1[nt]);
             const uint32_t wd[4] = {w.x0, w.x1, w.x2, w.x3};
@@ -329,6 +373,10 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
           }
         }
       };
+
+      auto bfrag = [&](int sidx, int nt, int t) -> bf16x8 {
+        return *(const bf16x8*)(ebase + nt * 16 * RS + sidx * 32 + a.zero * t);
+      };
       auto project = [&](int t, floatx4 (&acc)[NT]) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -339,10 +387,25 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
 #define MDS_REG_TILE(J)                                                                                  \
   case J:                                                                                                \
     if constexpr (J < RMT) {                                                                             \
-      _Pragma("unroll") for (int s = 0; s < RK; ++s) {                                                   \
-        _Pragma("unroll") for (int nt = 0; nt < NT; ++nt) acc[nt] =                                      \
-            __builtin_amdgcn_mfma_f32_16x16x32_bf16(wr[J][s], bfrag(s, nt, t), acc[nt], 0, 0, 0);        \
+      bf16x8 e0 = bfrag(0, 0, t), e1 = bfrag(0, 1, t);                                                   \
+      _Pragma("unroll") for (int sidx = 0; sidx < RK; ++sidx) {                                          \
+        bf16x8 n0 = e0, n1 = e1;                                                                         \
+        if (sidx + 1 < RK) {                                                                             \
+          n0 = bfrag(sidx + 1, 0, t);                                                                    \
+          n1 = bfrag(sidx + 1, 1, t);                                                                    \
+        }                                                                                                \
+        acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wr[J][sidx], e0, acc[0], 0, 0, 0);              \
+        acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wr[J][sidx], e1, acc[1], 0, 0, 0);              \
+        e0 = n0;                                                                                         \
+        e1 = n1;                                                                                         \
       }                                                                                                  \
+      /* one slice of embedding reads ahead of the MFMAs that use them */                                \
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                                 \
+      _Pragma("unroll") for (int sidx = 0; sidx + 1 < RK; ++sidx) {                                      \
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                               \
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                               \
+      }                                                                                                  \
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                                 \
     }                                                                                                    \
     break;
             MDS_REG_TILE(0) MDS_REG_TILE(1) MDS_REG_TILE(2) MDS_REG_TILE(3) MDS_REG_TILE(4) MDS_REG_TILE(5)
@@ -356,26 +419,44 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
           }
         } else {
           const int L = wave + 4 * (t - R_w);
+          const uint16_t* wrow = s_w + (L * 16 + lrow) * R;
+          bf16x8 f = *(const bf16x8*)(wrow + ((lgrp ^ (lrow & XMASK)) * 8));
+          bf16x8 e0 = bfrag(0, 0, t), e1 = bfrag(0, 1, t);
 #pragma unroll
-          for (int s = 0; s < RK; ++s) {
-            const int ch = s * 4 + lgrp;
-            const bf16x8 afr = *(const bf16x8*)(s_w + (L * 16 + lrow) * R + ((ch ^ (lrow & XMASK)) * 8));
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-              acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfrag(s, nt, t), acc[nt], 0, 0, 0);
+          for (int sidx = 0; sidx < RK; ++sidx) {
+            bf16x8 nf = f, n0 = e0, n1 = e1;
+            if (sidx + 1 < RK) {
+              const int ch = (sidx + 1) * 4 + lgrp;
+              nf = *(const bf16x8*)(wrow + ((ch ^ (lrow & XMASK)) * 8));
+              n0 = bfrag(sidx + 1, 0, t);
+              n1 = bfrag(sidx + 1, 1, t);
+            }
+            acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f, e0, acc[0], 0, 0, 0);
+            acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f, e1, acc[1], 0, 0, 0);
+            f = nf;
+            e0 = n0;
+            e1 = n1;
           }
+          // one slice of w2 and embedding reads ahead of the MFMAs that use them
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+          for (int sidx = 0; sidx + 1 < RK; ++sidx) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         }
       };
 
+      float ring[kDepth][NT][4];
 #pragma unroll
-      for (int u = 0; u < kDepth - 1; ++u)
-        if (u < T_w) load_base(u, ring[u]);
+      for (int u = 0; u < kDepth - 1; ++u) load_base(min(u, last), ring[u]);
       for (int t0 = 0; t0 < T_w; t0 += kDepth) {
 #pragma unroll
         for (int u = 0; u < kDepth; ++u) {
           const int t = t0 + u;
           if (t < T_w) {
-            if (t + kDepth - 1 < T_w) load_base(t + kDepth - 1, ring[(u + kDepth - 1) % kDepth]);
+            load_base(min(t + kDepth - 1, last), ring[(u + kDepth - 1) % kDepth]);
             floatx4 acc[NT];
             project(t, acc);
             epilogue(t, acc, ring[u]);
@@ -422,19 +503,30 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
   }
 }
 
-template <int RK, int RMT>
-hipError_t launch_res(const DraftStepArgs& a, size_t lds, hipStream_t st) {
+template <int RK, int RMT, bool BBF16, bool CBF16>
+hipError_t launch_res_t(const DraftStepArgs& a, size_t lds, hipStream_t st) {
   if (lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute((const void*)draft_resident_kernel<RK, RMT>,
+    const hipError_t e = hipFuncSetAttribute((const void*)draft_resident_kernel<RK, RMT, BBF16, CBF16>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((draft_resident_kernel<RK, RMT>), dim3(a.G), dim3(kThreads), lds, st, a);
+  hipLaunchKernelGGL((draft_resident_kernel<RK, RMT, BBF16, CBF16>), dim3(a.G), dim3(kThreads), lds, st, a);
   return hipGetLastError();
 }
 
-// register tiles per wave for rank r: 64 / RK tiles x RK k-steps x 4 registers = 256 registers
-int res_rmt(int r) { return 64 / (r / 32); }
+template <int RK, int RMT>
+hipError_t launch_res(const DraftStepArgs& a, size_t lds, hipStream_t st) {
+  if (a.base_bf16)
+    return a.cache_bf16 ? launch_res_t<RK, RMT, true, true>(a, lds, st) : launch_res_t<RK, RMT, true, false>(a, lds, st);
+  return a.cache_bf16 ? launch_res_t<RK, RMT, false, true>(a, lds, st) : launch_res_t<RK, RMT, false, false>(a, lds, st);
+}
+
+// register tiles per wave for rank r: about 256 registers of w2 per lane
+// (RMT tiles x RK k-steps x 4), RMT a multiple of the ring depth
+int res_rmt(int r) {
+  const int rmt = 64 / (r / 32);
+  return rmt - rmt % kDepth;
+}
 
 }  // namespace
 
@@ -459,7 +551,7 @@ hipError_t launch_draft_resident(const DraftStepArgs& a, size_t lds, hipStream_t
   switch (a.r) {
     case 64: return launch_res<2, 32>(a, lds, st);
     case 128: return launch_res<4, 16>(a, lds, st);
-    case 192: return launch_res<6, 10>(a, lds, st);
+    case 192: return launch_res<6, 8>(a, lds, st);
     case 256: return launch_res<8, 8>(a, lds, st);
     default: return hipErrorNotSupported;
   }
