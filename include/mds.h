@@ -180,7 +180,8 @@ int mds_markov_draft_loop(int B, int K, int V, int r,
  *                         draft_lse != NULL) bytes, 256-byte aligned, zero-filled
  *                         before its first use. Bytes [256, 256 + 512 KiB) hold one
  *                         arrival counter per request that every call leaves at
- *                         zero; the caller must not write the workspace between calls.
+ *                         zero; the caller must not write the workspace between calls
+ *                         (nor use the same memory as a draft-loop workspace).
  */
 int mds_rejection_verify(int B, int K, int V,
                          const float* target, int64_t target_row_stride,

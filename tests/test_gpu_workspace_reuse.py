@@ -1,0 +1,50 @@
+"""Back-to-back draft calls of different shapes on one workspace (the
+workspace layout depends on B and K, so one call's partials can land where
+the next call keeps its winner keys and barrier counters): each call matches
+the oracle, and repeating a call repeats its tokens exactly."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import workloads
+from parity import Report, cache_to_numpy, compare_draft, dev_tensors
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(params=["stream", "auto"])
+def draft_path(request, monkeypatch):
+    monkeypatch.setenv("MDS_DRAFT_PATH", request.param)
+    return request.param
+
+
+def _draft(wl, ws):
+    import torch
+    import markov_draft_sampling_amd as mds
+    d = dev_tensors(wl)
+    mds.markov_draft_loop(d["base"], d["w1"], d["w2"], d["anchor_tokens"], d["anchor_pos"], d["temperature"],
+                          d["seeds"], d["cache"], d["draft_tokens"], d["draft_lse"], workspace=ws)
+    torch.cuda.synchronize()
+    assert mds.workspace_status(ws) == 0
+    return d["draft_tokens"].cpu().numpy(), cache_to_numpy(d["cache"], wl.cache_dtype), d["draft_lse"].cpu().numpy()
+
+
+def test_calls_on_one_workspace(draft_path):
+    import torch
+    import markov_draft_sampling_amd as mds
+    wa = workloads.make_workload(2, B=8)
+    wb = workloads.make_custom(9001, 128, 3, 3, seed=12, temperature=0.8)
+    ws = mds.new_workspace(max(mds.draft_workspace_bytes(wa.B, wa.K, wa.V, wa.r),
+                               mds.draft_workspace_bytes(wb.B, wb.K, wb.V, wb.r)), torch.device("cuda"))
+    first = None
+    for wl in (wa, wb, wa):
+        toks, cache, lse = _draft(wl, ws)
+        rep = Report()
+        compare_draft(wl, np.arange(wl.B), toks, cache, lse, rep)
+        assert rep.ok(), rep.notes[:3]
+        if wl is wa:
+            if first is None:
+                first = toks
+            else:
+                np.testing.assert_array_equal(toks, first)
