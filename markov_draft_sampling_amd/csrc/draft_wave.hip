@@ -31,7 +31,10 @@ namespace {
 constexpr int kRKMax = 8;  // rank slices of 32 (r <= 256)
 
 // F64: the fp64 Gumbel option (scores and the running winner in float64).
-template <int NB, bool BBF16, bool CBF16, bool F64>
+// FL: compile the fixed-count fast loop; it raises the register count to one
+// wave per SIMD, so it is used when the grid has one work-group per CU (one
+// batch tile) and left out otherwise.
+template <int NB, bool BBF16, bool CBF16, bool F64, bool FL>
 __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
   using Score = typename std::conditional<F64, double, float>::type;
   constexpr int NT = NB / 16;
@@ -95,9 +98,30 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
   auto load_a = [&](int t, u32x4 (&A)[kRKMax]) {
     const int v = t * 16 + lr;
     const uint16_t* p = a.w2 + (size_t)(v < V ? v : V - 1) * r + lg * 8;
+    // all kRKMax slices, past the rank clamped to its last slice (same
+    // lines, no extra traffic): a fixed number of loads per tile lets the
+    // compiler wait for exactly the tile in use, not for the one in flight
 #pragma unroll
-    for (int s = 0; s < kRKMax; ++s)
-      if (s < RK) A[s] = *(const u32x4*)(p + s * 32);
+    for (int s = 0; s < kRKMax; ++s) A[s] = *(const u32x4*)(p + (s < RK ? s : RK - 1) * 32);
+  };
+  auto load_base_vec = [&](int t, float (&bz)[NT][4]) {
+    const int c = t * 16 + lg * 4;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      if (BBF16) {
+        const u32x2 w = *(const u32x2*)((const uint16_t*)a.base + rbase[nt] + c);
+        bz[nt][0] = bf16_bits_to_f32(w.x & 0xFFFFu);
+        bz[nt][1] = bf16_bits_to_f32(w.x >> 16);
+        bz[nt][2] = bf16_bits_to_f32(w.y & 0xFFFFu);
+        bz[nt][3] = bf16_bits_to_f32(w.y >> 16);
+      } else {
+        const f32x4 w = *(const f32x4*)((const float*)a.base + rbase[nt] + c);
+        bz[nt][0] = w.x;
+        bz[nt][1] = w.y;
+        bz[nt][2] = w.z;
+        bz[nt][3] = w.w;
+      }
+    }
   };
   auto load_base = [&](int t, float (&bz)[NT][4]) {
     const int c = t * 16 + lg * 4;
@@ -197,11 +221,112 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
   const bool fast_req = a.vec_cache && __all(all_sampled && all_valid);
   const bool t1 = __all(all_t1);
 
-  for (int t = t_first; t < mt_end; t += 4) {
-    const bool more = t + 4 < mt_end;
-    if (more) {
-      load_a(t + 4, An);
-      load_base(t + 4, bzn);
+  // Fast loop: the full tiles of a work-group whose requests all exist and
+  // sample, with vector base loads and cache stores. Its body has a fixed
+  // number of memory operations (the next tile's loads, then this tile's
+  // stores), so the wait for the next tile leaves this tile's stores in
+  // flight; the remaining tiles (a partial last tile, other work-groups) take
+  // the general loop below.
+  int t_gen = t_first;
+  if (FL && fast_req && a.vec_base) {
+    const int full_end = mt_end < V / 16 ? mt_end : V / 16;  // tiles [mt_begin, full_end) lie inside V
+    auto run_fast = [&](auto t1_tag) {
+      constexpr bool T1 = decltype(t1_tag)::value;
+      int t = t_first;
+      if (t < full_end) {
+        const int t_lastf = t_first + ((full_end - 1 - t_first) / 4) * 4;
+        for (; t < full_end; t += 4) {
+          const int tn = t + 4 < full_end ? t + 4 : t_lastf;  // the last tile again at the end: cache hits
+          load_a(tn, An);
+          load_base_vec(tn, bzn);
+          floatx4 acc[NT];
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) acc[nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int s = 0; s < kRKMax; ++s) {
+            if (s < RK) {
+              const bf16x8 afr = __builtin_bit_cast(bf16x8, A[s]);
+#pragma unroll
+              for (int nt = 0; nt < NT; ++nt) {
+                const bf16x8 bfr = *(const bf16x8*)(s_e + (nt * 16 + lr) * rs + s * 32 + lg * 8);
+                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr, acc[nt], 0, 0, 0);
+              }
+            }
+          }
+          const int c = t * 16 + lg * 4;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            float z[4], cv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) z[i] = bz[nt][i] + acc[nt][i];
+            if (CBF16) {
+              uint32_t h[4];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                h[i] = f32_to_bf16_bits(z[i]);
+                cv[i] = bf16_bits_to_f32(h[i]);
+              }
+              u32x2 w;
+              w.x = h[0] | (h[1] << 16);
+              w.y = h[2] | (h[3] << 16);
+              *(u32x2*)((uint16_t*)a.cache + rcache[nt] + c) = w;
+            } else {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) cv[i] = z[i];
+              *(f32x4*)((float*)a.cache + rcache[nt] + c) = f32x4{z[0], z[1], z[2], z[3]};
+            }
+            const Philox4 w = philox4x32_10((uint32_t)(c >> 2), pk0[nt], pk1[nt], kSaltDraft, sk0[nt], sk1[nt]);
+            const uint32_t wd[4] = {w.x0, w.x1, w.x2, w.x3};
+            float y[4], x[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              y[i] = T1 ? z[i] : div_t(z[i], Tv[nt], invT[nt]);
+              x[i] = CBF16 ? (T1 ? cv[i] : div_t(cv[i], Tv[nt], invT[nt])) : y[i];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              Score sv;
+              if (F64)
+                sv = (T1 ? (double)z[i] : (double)z[i] / (double)Tv[nt]) + gumbel64_from_word(wd[i]);
+              else
+                sv = y[i] + gumbel_from_word(wd[i]);
+              const bool take = (sv > bv[nt]) || ((sv != sv) && (bv[nt] == bv[nt]));
+              bv[nt] = take ? sv : bv[nt];
+              bi[nt] = take ? c + i : bi[nt];
+            }
+            const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));  // NaN-ignoring max
+            const float mn = fmaxf(qm[nt], mx);
+            const float sub = mn == -INFINITY ? 0.0f : mn;
+            float s_acc = qs[nt] * fast_exp(qm[nt] - sub);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s_acc += fast_exp(x[i] - sub);
+            qs[nt] = s_acc;
+            qm[nt] = mn;
+          }
+#pragma unroll
+          for (int s = 0; s < kRKMax; ++s) A[s] = An[s];
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) bz[nt][i] = bzn[nt][i];
+        }
+      }
+      return t;
+    };
+    t_gen = t1 ? run_fast(std::integral_constant<bool, true>()) : run_fast(std::integral_constant<bool, false>());
+    if (t_gen < mt_end) {  // the partial last tile: its operands again, for the general loop
+      load_a(t_gen, A);
+      load_base(t_gen, bz);
+    }
+  }
+
+  // the wave's last tile: the prefetch past it requests that tile again
+  const int t_last = t_gen < mt_end ? t_gen + ((mt_end - 1 - t_gen) / 4) * 4 : t_gen;
+  for (int t = t_gen; t < mt_end; t += 4) {
+    {
+      const int tn = t + 4 < mt_end ? t + 4 : t_last;
+      load_a(tn, An);
+      load_base(tn, bzn);
     }
     // bias of this tile: D[column][request] for the NT request tiles
     floatx4 acc[NT];
@@ -350,14 +475,12 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
       }
     }
     }
-    if (more) {
 #pragma unroll
-      for (int s = 0; s < kRKMax; ++s) A[s] = An[s];
+    for (int s = 0; s < kRKMax; ++s) A[s] = An[s];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) bz[nt][i] = bzn[nt][i];
-    }
+      for (int i = 0; i < 4; ++i) bz[nt][i] = bzn[nt][i];
   }
 
   // merge the 4 lanes of each request row (lanes lr, lr + 16, lr + 32, lr + 48)
@@ -399,8 +522,12 @@ template <int NB, bool BBF16, bool CBF16, bool F64>
 hipError_t launch_wave(const DraftStepArgs& a, int bt, hipStream_t st) {
   DraftStepArgs b = a;
   b.BT = bt;
-  hipLaunchKernelGGL((draft_wave_kernel<NB, BBF16, CBF16, F64>), dim3(a.G * bt), dim3(256), draft_wave_lds(NB, a.r),
-                     st, b);
+  if (bt == 1)
+    hipLaunchKernelGGL((draft_wave_kernel<NB, BBF16, CBF16, F64, true>), dim3(a.G), dim3(256), draft_wave_lds(NB, a.r),
+                       st, b);
+  else
+    hipLaunchKernelGGL((draft_wave_kernel<NB, BBF16, CBF16, F64, false>), dim3(a.G * bt), dim3(256),
+                       draft_wave_lds(NB, a.r), st, b);
   return hipGetLastError();
 }
 
