@@ -15,8 +15,10 @@ writing leaves no dirty lines whose write-back would compete with the step.
 Each step is timed
 with HIP events on the stream the kernels run on, and the flush is outside
 the events. The same steps run back to back without flushes are reported as
-`warm`. The fused Markov-step kernel is additionally timed per launch (events
-around each of its K launches) for the roofline entry.
+`warm`. For the roofline entry the steps run once more, the library
+recording events around the launches of the dominant kernel (the fused
+Markov-step kernel, or the variant's); those records sit between kernels, so
+this pass is not the timed one.
 
 Prints one JSON line. One GPU only: --gpus N with N > 1 exits with an error.
 """
@@ -234,18 +236,27 @@ def main():
     starts, ends = [ev() for _ in range(a.steps)], [ev() for _ in range(a.steps)]
     kev = [(ev(), ev()) for _ in range(a.steps)]
     launches = []
+    # the timed steps: nothing but the step between the events
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(a.steps):
         if not a.no_flush:
             flush.sum()
         starts[i].record(stream)
-        step(kev[i])
+        step()
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
-    draft_span_ms = np.array([b.elapsed_time(e) for b, e in kev])  # all Markov-step kernel launches of a call
+    # the same steps again, the library recording events around the dominant
+    # kernel's launches (those records sit between kernels, so these steps
+    # are not the timed ones)
+    for i in range(a.steps):
+        if not a.no_flush:
+            flush.sum()
+        step(kev[i])
+    torch.cuda.synchronize()
+    draft_span_ms = np.array([b.elapsed_time(e) for b, e in kev])  # all launches of the dominant kernel in a call
     n_launch = launches[-1]
 
     # back to back, caches warm
