@@ -230,6 +230,14 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
   int t_gen = t_first;
   if (FL && fast_req && a.vec_base) {
     const int full_end = mt_end < V / 16 ? mt_end : V / 16;  // tiles [mt_begin, full_end) lie inside V
+    // the embedding operands are the same for every tile: read once, kept in
+    // registers for the whole loop (one wave per SIMD leaves room)
+    bf16x8 Er[NT][kRKMax];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int s = 0; s < kRKMax; ++s)
+        Er[nt][s] = *(const bf16x8*)(s_e + (nt * 16 + lr) * rs + (s < RK ? s : 0) * 32 + lg * 8);
     auto run_fast = [&](auto t1_tag) {
       constexpr bool T1 = decltype(t1_tag)::value;
       int t = t_first;
@@ -247,10 +255,7 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
             if (s < RK) {
               const bf16x8 afr = __builtin_bit_cast(bf16x8, A[s]);
 #pragma unroll
-              for (int nt = 0; nt < NT; ++nt) {
-                const bf16x8 bfr = *(const bf16x8*)(s_e + (nt * 16 + lr) * rs + s * 32 + lg * 8);
-                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr, acc[nt], 0, 0, 0);
-              }
+              for (int nt = 0; nt < NT; ++nt) acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, Er[nt][s], acc[nt], 0, 0, 0);
             }
           }
           const int c = t * 16 + lg * 4;
