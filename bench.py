@@ -136,7 +136,7 @@ def main():
     a = ap.parse_args()
     if a.gpus != 1:
         print("bench.py runs on one GPU only: the path is measured on a single MI355X "
-              "(no multi-GPU code is part of this build)", file=sys.stderr)
+              "(the library has no multi-GPU code)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -147,7 +147,7 @@ def main():
     assert torch.cuda.is_available(), "no GPU"
     dev = torch.device("cuda:0")
     t_gen = time.perf_counter()
-    wl = workloads.make_workload(4, B=a.batch)
+    wl = workloads.make_workload("headline_v200064", B=a.batch)
     B, K, V, r = wl.B, wl.K, wl.V, wl.r
     print(f"# workload V={V} r={r} K={K} B={B} generated in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr,
           flush=True)

@@ -46,7 +46,7 @@ extern "C" {
 /* return codes */
 #define MDS_OK 0
 #define MDS_ERR_INVALID_ARG (-1)      /* a size, stride, pointer or dtype is invalid */
-#define MDS_ERR_UNSUPPORTED (-2)      /* valid but not supported by this build (e.g. r not a multiple of 32) */
+#define MDS_ERR_UNSUPPORTED (-2)      /* valid but not supported by this library (e.g. r not a multiple of 32) */
 #define MDS_ERR_WORKSPACE (-3)        /* workspace smaller than the matching *_workspace_bytes() */
 #define MDS_ERR_HIP (-4)              /* a HIP runtime call or kernel launch failed */
 

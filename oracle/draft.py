@@ -9,7 +9,7 @@ feed the sample back as the previous token) and ``_sample_logits`` (the draw
 for predicted position P is keyed by P-1, temperature is applied, and the
 biased logits are stored into the draft-logits cache at column = step).
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
 
 * the Markov embedding of token x is row x of a bf16 matrix w1[V, r], with no
   scale or normalisation, and the bias is w2[V, r] @ embedding (PR #65007,

@@ -6,7 +6,7 @@ step) row, gathered in (request, step) order, goes through the draft model's
 ``compute_draft_logits`` to give that row's base draft logits over the draft
 vocabulary, before the Markov loop starts.
 
-Readings (listed in the design doc): the draft LM head is a plain linear map with
+Readings where the pages are silent: the draft LM head is a plain linear map with
 no bias, scale or soft cap (the pages name no logits processor on this path),
 logits = hidden @ lm_head^T with hidden [rows, H] and lm_head [V, H] in bf16;
 the products of bf16 values are exact in float64 and the sum is kept in

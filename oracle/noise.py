@@ -5,7 +5,7 @@ Part 1 and its review thread on constants): the noise of a draw is a pure
 function of the request's seed, of the position *before* the sampled token
 (P-1 for a token at position P) and of the column, and draft noise carries a
 salt of 1<<30 so that it never collides with the noise of target sampling.
-What they leave open and this build fixes:
+What they leave open, and the choice made here:
 
 * counter = (column >> 2, low 32 bits of the position key, high 32 bits,
   salt), key = (low 32 bits of the seed, high 32 bits); column c reads output

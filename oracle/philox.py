@@ -2,8 +2,8 @@
 
 The pages key the draft noise by (seed, position-1, column) through a counter
 hash they name but do not define (PR #65007, Part 1: the noise keys of the
-replicated loop; API page, ``_sample_logits``). This build defines that hash
-as Philox4x32 with 10 rounds from Salmon, Moraes, Dror and Shaw, "Parallel
+replicated loop; API page, ``_sample_logits``). The hash used here is
+Philox4x32 with 10 rounds from Salmon, Moraes, Dror and Shaw, "Parallel
 random numbers: as easy as 1, 2, 3" (SC'11): each round multiplies words 0
 and 2 by two fixed odd constants, keeps both 32-bit halves of each product,
 and mixes the high halves with words 1 and 3 and the round key; the key is

@@ -14,7 +14,7 @@ probability min(1, p_k(x) / q_k(x)); the first rejected step draws its
 replacement from the normalised residual max(0, p_k - q_k); when every draft
 is accepted a bonus token is drawn from p_K.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
 
 * the accept test is p >= u * q with u the column-0 uniform of the accept
   stream at key P0+k, taken in float32 (the kernel's precision);

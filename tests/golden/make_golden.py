@@ -20,7 +20,7 @@ import workloads  # noqa: E402
 
 
 def compute():
-    wl = workloads.make_workload(1)
+    wl = workloads.make_workload("tiny_v4096")
     d = oracle.draft_loop(wl.draft_base, wl.base_dtype, wl.w1, wl.w2, wl.anchor_tokens, wl.anchor_pos, wl.seeds,
                           wl.temperature, wl.cache_dtype)
     v = oracle.verify(wl.target, d["cache"], wl.cache_dtype, d["tokens"], wl.temperature, wl.top_p, wl.seeds,

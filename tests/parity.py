@@ -1,6 +1,6 @@
 """Test helpers: run the HIP path on a workload and compare it with the oracle.
 
-Parity rules (the margins come from the task's parity contract):
+Parity rules:
 * draft token (b, k): must equal the oracle's, unless the oracle's top-two
   float32 scores at that step differ by at most 1e-3 (excused);
 * accept count / emitted tokens of a request: must equal the oracle's, unless

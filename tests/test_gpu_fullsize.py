@@ -43,12 +43,12 @@ def _check(wl, rows, label):
 
 @pytest.mark.parametrize("B,rows", [(32, [0, 7, 19, 31]), (1, [0]), (128, [0, 64, 127])])
 def test_headline_workload(draft_path, B, rows):
-    wl = workloads.make_workload(4, B=B)
+    wl = workloads.make_workload("headline_v200064", B=B)
     _check(wl, rows, f"V=200064 B={B} {draft_path}")
 
 
 def test_bf16_top_p_workload(draft_path):
-    wl = workloads.make_workload(3)
+    wl = workloads.make_workload("zipf_top_p_v151936")
     _check(wl, [0, 13, 31], f"bf16 top-p V=151936 B=32 {draft_path}")
 
 
@@ -57,7 +57,7 @@ def test_resident_kernel_engages_on_the_headline_workload(monkeypatch):
     import markov_draft_sampling_amd as mds
     from parity import dev_tensors
     monkeypatch.setenv("MDS_DRAFT_PATH", "auto")
-    wl = workloads.make_workload(4, B=8)
+    wl = workloads.make_workload("headline_v200064", B=8)
     d = dev_tensors(wl)
     ws = mds.new_workspace(mds.draft_workspace_bytes(wl.B, wl.K, wl.V, wl.r))
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -133,11 +133,11 @@ def test_indexed_verify_matches_oracle(top_p):
     assert gn[5] <= 2 and (go[5, gn[5] + 1:] == -1).all()
 
 
-@pytest.mark.parametrize("cfg", [2, 5])
-def test_plain_verify_with_placeholder_drafts(cfg):
+@pytest.mark.parametrize("wname", ["boosted_v32000", "odd_vocab_v50017"])
+def test_plain_verify_with_placeholder_drafts(wname):
     import torch
     import markov_draft_sampling_amd as mds
-    wl = workloads.make_workload(cfg, B=8)
+    wl = workloads.make_workload(wname, B=8)
     d = run_gpu(wl, verify=False)
     toks = d["draft_tokens"].cpu().numpy()
     cut = np.array([wl.K, 0, 1, 2, wl.K - 1, 3, 0, 2])[: wl.B]

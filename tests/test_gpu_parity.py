@@ -26,28 +26,28 @@ def _assert(rep: Report, label: str):
     assert rep.ok(), rep.notes[:5]
 
 
-def test_tiny_config():
-    wl = workloads.make_workload(1)
+def test_tiny_workload():
+    wl = workloads.make_workload("tiny_v4096")
     _assert(full_parity(wl), "tiny")
 
 
 def test_tiny_config_matches_golden():
     import json, os
-    wl = workloads.make_workload(1)
+    wl = workloads.make_workload("tiny_v4096")
     d = run_gpu(wl)
     want = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "tiny_v4096_oracle.json")))
     assert d["draft_tokens"].cpu().tolist() == want["draft_tokens"]
     assert d["out_tokens"].cpu().tolist() == want["out_tokens"]
 
 
-def test_boosted_config():
-    wl = workloads.make_workload(2)
+def test_boosted_workload():
+    wl = workloads.make_workload("boosted_v32000")
     _assert(full_parity(wl), "V=32000 r=128 K=5 B=8")
 
 
 @pytest.mark.parametrize("B", [1, 4, 8, 33])
-def test_edge_config(B):
-    wl = workloads.make_workload(5, B=B)
+def test_odd_vocab_workload(B):
+    wl = workloads.make_workload("odd_vocab_v50017", B=B)
     _assert(full_parity(wl), f"edge V=50017 B={B}")
 
 
@@ -55,7 +55,7 @@ def test_edge_config_planted_ties_and_nan_are_exact():
     # exact ties and NaN columns are decided by the rule alone (no margin):
     # the first NaN column wins its step; in greedy requests with planted ties
     # the first tie column wins every other step and every target row
-    wl = workloads.make_workload(5, B=16)
+    wl = workloads.make_workload("odd_vocab_v50017", B=16)
     d = run_gpu(wl)
     toks = d["draft_tokens"].cpu().numpy()
     out = d["out_tokens"].cpu().numpy()
@@ -87,12 +87,12 @@ def test_custom_shapes(V, r, K, B, bd, cd):
 
 
 def test_padded_rows_take_vector_path_on_odd_vocab():
-    wl = workloads.make_workload(5, B=8)
+    wl = workloads.make_workload("odd_vocab_v50017", B=8)
     _assert(full_parity(wl, pad_to=64), "edge V=50017 rows padded to 64")
 
 
 def test_verify_recomputes_draft_lse_when_not_given():
-    wl = workloads.make_workload(2)
+    wl = workloads.make_workload("boosted_v32000")
     _assert(full_parity(wl, with_lse=False), "V=32000 without draft lse")
 
 
@@ -132,7 +132,7 @@ def test_bad_anchor_sets_sticky_status():
 def test_non_default_stream_and_graph_replay():
     import markov_draft_sampling_amd as mds
     import torch
-    wl = workloads.make_workload(2, B=4)
+    wl = workloads.make_workload("boosted_v32000", B=4)
     d = dev_tensors(wl)
     ws_d = mds.new_workspace(mds.draft_workspace_bytes(4, wl.K, wl.V, wl.r))
     ws_v = mds.new_workspace(mds.verify_workspace_bytes(4, wl.K, wl.V, False, True))

@@ -58,9 +58,10 @@ def _check(wl, d, topk, rows=None, fp64=False, verify=False):
     return toks, ref
 
 
-@pytest.mark.parametrize("cfg,topk", [(1, 1), (1, 7), (1, 256), (2, 64), (5, 33), (3, 64)])
-def test_topk_matches_oracle(cfg, topk):
-    wl = workloads.make_workload(cfg, B=None if cfg == 1 else 6)
+@pytest.mark.parametrize("wname,topk", [("tiny_v4096", 1), ("tiny_v4096", 7), ("tiny_v4096", 256),
+                                         ("boosted_v32000", 64), ("odd_vocab_v50017", 33), ("zipf_top_p_v151936", 64)])
+def test_topk_matches_oracle(wname, topk):
+    wl = workloads.make_workload(wname, B=None if wname == "tiny_v4096" else 6)
     d = _run(wl, topk, verify=True)
     _check(wl, d, topk, verify=True)
 
@@ -96,7 +97,7 @@ def test_topk_ties_nan_and_inf_rows():
 
 
 def test_topk_fp64_gumbel():
-    wl = workloads.make_workload(2, B=6)
+    wl = workloads.make_workload("boosted_v32000", B=6)
     d = _run(wl, 50, fp64=True)
     _check(wl, d, 50, fp64=True)
 
@@ -146,7 +147,7 @@ def test_topk_indexed_with_padding():
 
 
 def test_topk_headline_rows():
-    wl = workloads.make_workload(4, B=32)
+    wl = workloads.make_workload("headline_v200064", B=32)
     d = _run(wl, 64, verify=True)
     _check(wl, d, 64, rows=[0, 13, 31], verify=True)
 

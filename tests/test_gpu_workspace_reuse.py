@@ -33,7 +33,7 @@ def _draft(wl, ws):
 def test_calls_on_one_workspace(draft_path):
     import torch
     import markov_draft_sampling_amd as mds
-    wa = workloads.make_workload(2, B=8)
+    wa = workloads.make_workload("boosted_v32000", B=8)
     wb = workloads.make_custom(9001, 128, 3, 3, seed=12, temperature=0.8)
     ws = mds.new_workspace(max(mds.draft_workspace_bytes(wa.B, wa.K, wa.V, wa.r),
                                mds.draft_workspace_bytes(wb.B, wb.K, wb.V, wb.r)), torch.device("cuda"))

@@ -3,23 +3,23 @@ the planted features the edge workload is meant to exercise."""
 import numpy as np
 import pytest
 
-from workloads import make_workload, make_custom, CONFIGS, bf16_bits_to_f32
+from workloads import make_workload, make_custom, WORKLOADS, bf16_bits_to_f32
 
 
 def test_reproducible_and_prefix_consistent():
-    a = make_workload(2, B=3)
-    b = make_workload(2, B=8)
+    a = make_workload("boosted_v32000", B=3)
+    b = make_workload("boosted_v32000", B=8)
     for f in ("base", "anchor_tokens", "anchor_pos", "seeds", "temperature"):
         assert np.array_equal(getattr(a, f), getattr(b, f)[:3]), f
     assert np.array_equal(a.target, b.target[: 3 * (a.K + 1)])
-    c = make_workload(2, B=3)
+    c = make_workload("boosted_v32000", B=3)
     assert np.array_equal(a.base, c.base) and np.array_equal(a.w2, c.w2)
 
 
-@pytest.mark.parametrize("cfg", [1, 2])
-def test_shapes_and_distributions(cfg):
-    wl = make_workload(cfg)
-    spec = CONFIGS[cfg]
+@pytest.mark.parametrize("wname", ["tiny_v4096", "boosted_v32000"])
+def test_shapes_and_distributions(wname):
+    wl = make_workload(wname)
+    spec = WORKLOADS[wname]
     assert wl.base.shape == (wl.B, wl.K + 1, wl.V)
     assert wl.target.shape == (wl.B * (wl.K + 1), wl.V)
     assert wl.w1.shape == wl.w2.shape == (wl.V, wl.r)
@@ -30,16 +30,16 @@ def test_shapes_and_distributions(cfg):
     assert np.all((wl.anchor_tokens >= 0) & (wl.anchor_tokens < wl.V))
 
 
-def test_cfg2_boost_and_temperatures():
-    wl = make_workload(2)
+def test_boosted_workload_boost_and_temperatures():
+    wl = make_workload("boosted_v32000")
     assert np.all((wl.temperature >= 0.6) & (wl.temperature <= 1.2))
     # 5% of the columns of each request sit ~6 above the rest, in all K+1 rows
     m = wl.base[0].mean(0)  # boosted columns average ~6 over the request's K+1 rows
     assert 0.04 < (m > 3).mean() < 0.07
 
 
-def test_cfg5_planted_features():
-    wl = make_workload(5, B=16)
+def test_odd_vocab_workload_planted_features():
+    wl = make_workload("odd_vocab_v50017", B=16)
     assert wl.V == 50017 and wl.r == 192
     assert (wl.temperature == 0).sum() == 4
     assert 3 in wl.tie_requests

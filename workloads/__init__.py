@@ -28,16 +28,16 @@ import functools
 
 import numpy as np
 
-__all__ = ["CONFIGS", "Workload", "make_workload", "bf16_bits", "bf16_bits_to_f32", "CFG5_BATCHES", "CFG4_BATCHES",
-           "make_lm_head"]
+__all__ = ["WORKLOADS", "Workload", "make_workload", "bf16_bits", "bf16_bits_to_f32", "HEADLINE_BATCHES",
+           "ODD_VOCAB_BATCHES", "make_lm_head"]
 
-CFG4_BATCHES = (1, 8, 32, 128)
-CFG5_BATCHES = (1, 2, 3, 4, 5, 7, 8, 16, 31, 32, 33, 64, 96, 127, 128)
+HEADLINE_BATCHES = (1, 8, 32, 128)
+ODD_VOCAB_BATCHES = (1, 2, 3, 4, 5, 7, 8, 16, 31, 32, 33, 64, 96, 127, 128)
 
 
 @dataclasses.dataclass(frozen=True)
-class ConfigSpec:
-    name: str
+class WorkloadSpec:
+    desc: str
     V: int
     r: int
     K: int
@@ -47,23 +47,29 @@ class ConfigSpec:
     base_std: float
     w_std: float
     target_std: float
-    master: int
+    master: int  # seed material of the generators
     top_p: float | None = None
+    boost: bool = False  # 5% of the columns of each request raised by 6
+    zipf: bool = False  # Zipf-shaped offsets (rank^-1.1 scaled to +10) on the base logits
+    temp: str = "one"  # "one", "fixed" (T = 1, seed 0, position 100), "u0.6-1.2", "u0.7-1.0", "greedy_quarter"
+    planted: bool = False  # exact ties between blocks, NaN columns, zero w2 rows
 
 
-CONFIGS: dict[int, ConfigSpec] = {
-    1: ConfigSpec("tiny V=4096 r=64 K=3 B=1", 4096, 64, 3, 1, "f32", "f32", 3.0, 0.05, 0.5, 0),
-    2: ConfigSpec("V=32000 r=128 K=5 B=8 boosted", 32000, 128, 5, 8, "f32", "f32", 3.0, 0.02, 1.0, 2),
-    3: ConfigSpec("V=151936 r=256 K=7 B=32 bf16 zipf top-p", 151936, 256, 7, 32, "bf16", "bf16", 4.0, 0.02, 0.8, 3,
-                  top_p=0.95),
-    4: ConfigSpec("V=200064 r=256 K=7 fp32", 200064, 256, 7, 32, "f32", "f32", 3.0, 0.02, 1.0, 4),
-    5: ConfigSpec("edge V=50017 r=192 K=7", 50017, 192, 7, 32, "f32", "f32", 3.0, 0.05, 0.5, 5),
+WORKLOADS: dict[str, WorkloadSpec] = {
+    "tiny_v4096": WorkloadSpec("tiny V=4096 r=64 K=3 B=1", 4096, 64, 3, 1, "f32", "f32", 3.0, 0.05, 0.5, 0,
+                               temp="fixed"),
+    "boosted_v32000": WorkloadSpec("V=32000 r=128 K=5 B=8 boosted", 32000, 128, 5, 8, "f32", "f32", 3.0, 0.02, 1.0,
+                                   2, boost=True, temp="u0.6-1.2"),
+    "zipf_top_p_v151936": WorkloadSpec("V=151936 r=256 K=7 B=32 bf16 zipf top-p", 151936, 256, 7, 32, "bf16", "bf16",
+                                       4.0, 0.02, 0.8, 3, top_p=0.95, zipf=True, temp="u0.7-1.0"),
+    "headline_v200064": WorkloadSpec("V=200064 r=256 K=7 fp32", 200064, 256, 7, 32, "f32", "f32", 3.0, 0.02, 1.0, 4),
+    "odd_vocab_v50017": WorkloadSpec("odd vocabulary V=50017 r=192 K=7", 50017, 192, 7, 32, "f32", "f32", 3.0, 0.05,
+                                     0.5, 5, temp="greedy_quarter", planted=True),
 }
 
 
 @dataclasses.dataclass
 class Workload:
-    cfg: int
     name: str
     V: int
     r: int
@@ -104,13 +110,13 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
 
 
 @functools.lru_cache(maxsize=4)
-def _weights(cfg: int):
-    spec = CONFIGS[cfg]
+def _weights(wname: str):
+    spec = WORKLOADS[wname]
     rng = np.random.default_rng([spec.master, 0])
     w1 = rng.standard_normal((spec.V, spec.r), dtype=np.float32) * np.float32(spec.w_std)
     w2 = rng.standard_normal((spec.V, spec.r), dtype=np.float32) * np.float32(spec.w_std)
     tie_cols: tuple = ()
-    if cfg == 5:
+    if spec.planted:
         # Four columns in distinct 1024-column blocks plus a second column in
         # the first one's block; their w2 rows are zero, so the Markov bias
         # there is exactly 0 whatever the previous token.
@@ -123,8 +129,8 @@ def _weights(cfg: int):
 
 
 @functools.lru_cache(maxsize=2)
-def _zipf_offsets(cfg: int) -> np.ndarray:
-    spec = CONFIGS[cfg]
+def _zipf_offsets(wname: str) -> np.ndarray:
+    spec = WORKLOADS[wname]
     rng = np.random.default_rng([spec.master, 2])
     perm = rng.permutation(spec.V)
     off = np.empty(spec.V, dtype=np.float32)
@@ -132,28 +138,28 @@ def _zipf_offsets(cfg: int) -> np.ndarray:
     return off
 
 
-def _request(cfg: int, b: int):
+def _request(wname: str, b: int):
     """Per-request draws: base rows, target rows, temperature, seed, position, anchor."""
-    spec = CONFIGS[cfg]
+    spec = WORKLOADS[wname]
     V, K = spec.V, spec.K
     rng = np.random.default_rng([spec.master, 1, b])
     base = rng.standard_normal((K + 1, V), dtype=np.float32) * np.float32(spec.base_std)
-    if cfg == 2:
+    if spec.boost:
         boosted = rng.choice(V, size=V // 20, replace=False)
         base[:, boosted] += np.float32(6.0)
-    if cfg == 3:
-        base += _zipf_offsets(cfg)[None, :]
+    if spec.zipf:
+        base += _zipf_offsets(wname)[None, :]
     noise = rng.standard_normal((K + 1, V), dtype=np.float32) * np.float32(spec.target_std)
-    if cfg == 1:
+    if spec.temp == "fixed":
         temp, seed, pos = 1.0, 0, 100
     else:
         seed = int(rng.integers(0, 2**63, dtype=np.int64))
         pos = int(rng.integers(1, 2**20))
-        if cfg == 2:
+        if spec.temp == "u0.6-1.2":
             temp = float(rng.uniform(0.6, 1.2))
-        elif cfg == 3:
+        elif spec.temp == "u0.7-1.0":
             temp = float(rng.uniform(0.7, 1.0))
-        elif cfg == 5:
+        elif spec.temp == "greedy_quarter":
             # a quarter of the requests are greedy (b = 3, 7, 11, ...), so
             # every batch of four or more holds one
             temp = 0.0 if b % 4 == 3 else 1.0
@@ -163,14 +169,14 @@ def _request(cfg: int, b: int):
     return base, noise, np.float32(temp), seed, pos, anchor, rng
 
 
-def make_workload(cfg: int, B: int | None = None) -> Workload:
-    """Build workload ``cfg`` (1..5) at batch ``B`` (default: the config's own)."""
-    spec = CONFIGS[cfg]
+def make_workload(wname: str, B: int | None = None) -> Workload:
+    """Build the named workload (a key of WORKLOADS) at batch ``B`` (default: its own)."""
+    spec = WORKLOADS[wname]
     B = spec.B if B is None else int(B)
     if B < 1:
         raise ValueError("B must be >= 1")
     V, K = spec.V, spec.K
-    w1, w2, tie_cols = _weights(cfg)
+    w1, w2, tie_cols = _weights(wname)
     base_bits = spec.base_dtype == "bf16"
     base = np.empty((B, K + 1, V), dtype=np.uint16 if base_bits else np.float32)
     target = np.empty((B * (K + 1), V), dtype=np.float32)
@@ -181,7 +187,7 @@ def make_workload(cfg: int, B: int | None = None) -> Workload:
     nan_rows = []
     tie_requests = []
     for b in range(B):
-        rb, noise, t, s, p, a, rng = _request(cfg, b)
+        rb, noise, t, s, p, a, rng = _request(wname, b)
         if base_bits:
             bits = bf16_bits(rb)
             base[b] = bits
@@ -191,7 +197,7 @@ def make_workload(cfg: int, B: int | None = None) -> Workload:
             rb_f = rb
         target[b * (K + 1):(b + 1) * (K + 1)] = rb_f + noise
         temps[b], seeds[b], pos[b], anchors[b] = t, s, p, a
-        if cfg == 5:
+        if spec.planted:
             # exact ties in every other greedy request: the tie columns carry
             # the row maximum + 5 in every base row and every target row
             if t == 0.0 and (b // 4) % 2 == 0:
@@ -208,7 +214,7 @@ def make_workload(cfg: int, B: int | None = None) -> Workload:
                     base[b, k, cols] = np.nan
                     nan_rows.append((b, k, tuple(int(c) for c in cols)))
     top_p = None if spec.top_p is None else np.full(B, spec.top_p, np.float32)
-    return Workload(cfg=cfg, name=spec.name, V=V, r=spec.r, K=K, B=B, base_dtype=spec.base_dtype,
+    return Workload(name=wname, V=V, r=spec.r, K=K, B=B, base_dtype=spec.base_dtype,
                     cache_dtype=spec.cache_dtype, base=base, w1=w1, w2=w2, anchor_tokens=anchors,
                     anchor_pos=pos, seeds=seeds, temperature=temps, target=target, top_p=top_p,
                     nan_rows=nan_rows, tie_cols=tie_cols, tie_requests=tuple(tie_requests))
@@ -229,7 +235,7 @@ def make_custom(V: int, r: int, K: int, B: int, *, seed: int = 0, base_std: floa
         base = rb
     target = (rb + rng.standard_normal((B, K + 1, V), dtype=np.float32) * np.float32(target_std)).reshape(
         B * (K + 1), V)
-    return Workload(cfg=0, name=f"custom V={V} r={r} K={K} B={B}", V=V, r=r, K=K, B=B, base_dtype=base_dtype,
+    return Workload(name=f"custom V={V} r={r} K={K} B={B}", V=V, r=r, K=K, B=B, base_dtype=base_dtype,
                     cache_dtype=cache_dtype, base=base, w1=w1, w2=w2,
                     anchor_tokens=rng.integers(0, V, size=B).astype(np.int32),
                     anchor_pos=rng.integers(1, 2**20, size=B).astype(np.int64),
@@ -242,7 +248,7 @@ def make_lm_head(rows: int, V: int, H: int, *, seed: int = 0, logit_std: float =
     """Seeded draft LM-head inputs: hidden [rows, H] and lm_head [V, H] as bf16 bit patterns.
 
     hidden ~ N(0, 1) and lm_head ~ N(0, logit_std^2 / H), so the logits
-    hidden @ lm_head^T are ~N(0, logit_std^2) like the configs' base logits.
+    hidden @ lm_head^T are ~N(0, logit_std^2) like the workloads' base logits.
     Generated in row chunks to bound host memory.
     """
     rng = np.random.default_rng([seed, 11, rows, V, H])
