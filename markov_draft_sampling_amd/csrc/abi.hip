@@ -53,7 +53,7 @@ bool vec_ok(const void* p, int dtype, long long rs, long long ss) {
   return aligned(p, dtype == MDS_BF16 ? 8 : 16) && rs % 4 == 0 && ss % 4 == 0;
 }
 
-// Draft workspace: [status | keys K*B u64 | barrier words K+1 u32 | per-slab
+// Draft workspace: [status | keys K*B u64, one per 128-byte line | barrier words K+1 u32 | per-slab
 // (max, sum exp) partials K*B*kDraftMaxSlabs]. Sized without the device so the
 // query needs no GPU.
 struct DraftLayout {
@@ -65,7 +65,7 @@ DraftLayout draft_layout(int B, int K, int V) {
   DraftLayout L;
   L.nMT = (V + 15) / 16;
   L.keys = kAlign;
-  L.bar = L.keys + up((size_t)K * B * 8);
+  L.bar = L.keys + up((size_t)K * B * 8 * mds::kKeyStride);
   L.qpart = L.bar + up((size_t)(K + 1) * 4);
   L.total = L.qpart + up((size_t)K * B * mds::kDraftMaxSlabs * sizeof(float2));
   return L;

@@ -258,7 +258,7 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftStepArgs a) {
     const int b = b0 + i;
     int prev = -1;  // rows that are not served get a zero embedding
     if (draft_slot(a, b) >= 0) {
-      long long t = (k == 0) ? (long long)a.anchor[b] : (long long)(int32_t)win_col(a.keys[(size_t)(k - 1) * a.B + b]);
+      long long t = (k == 0) ? (long long)a.anchor[b] : (long long)(int32_t)win_col(a.keys[key_index(k - 1, a.B, b)]);
       if (t < 0 || t >= V) {
         set_status(a.status, kStatusBadAnchor);
         t = 0;
@@ -390,14 +390,14 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftStepArgs a) {
     const int b = b0 + i;
     if (draft_slot(a, b) < 0) continue;  // no winner and no partial for rows that are not served
     const unsigned long long key = s_key[i];
-    if (key) atomicMax(&a.keys[(size_t)k * a.B + b], key);
+    if (key) atomicMax(&a.keys[key_index(k, a.B, b)], key);
     a.qpart[((size_t)k * a.B + b) * a.G + g] = make_float2(s_qm[i], s_qs[i]);
   }
 }
 
 __global__ __launch_bounds__(256) void draft_init_kernel(unsigned long long* keys, int n, unsigned* bar, int nbar) {
   const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) keys[i] = 0ull;
+  if (i < n) keys[(size_t)i * kKeyStride] = 0ull;
   if (i < nbar) bar[i] = 0u;
 }
 
@@ -409,7 +409,7 @@ __global__ __launch_bounds__(256) void draft_finalize_kernel(DraftFinalArgs a) {
   if (row >= a.B * a.K) return;
   const int b = row / a.K, k = row - b * a.K;
   // inert rows keep key 0, i.e. token -1
-  if (lane == 0) a.tokens[row] = key_col(a.keys[(size_t)k * a.B + b], a.fp64 != 0);
+  if (lane == 0) a.tokens[row] = key_col(a.keys[key_index(k, a.B, b)], a.fp64 != 0);
   if (!a.lse) return;
   const int sl = draft_slot(a.idx_map, a.row_map, a.B, a.K, a.n_slots, a.n_rows, nullptr, b, k);
   if (sl < 0) {

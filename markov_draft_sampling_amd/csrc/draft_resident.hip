@@ -216,7 +216,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
             t = a.anchor[b];
           } else {
             const unsigned long long key =
-                __hip_atomic_load(&a.keys[(size_t)(k - 1) * B + b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_load(&a.keys[key_index(k - 1, B, b)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             t = (long long)win_col(key);
           }
           if (t < 0 || t >= V) {
@@ -494,7 +494,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
             lse_merge(m, s, s_qm[w * kNB + tid], s_qs[w * kNB + tid]);
           }
           // the returned value makes the wave wait until the atomic is performed
-          const unsigned long long prev = key ? atomicMax(&a.keys[(size_t)k * B + b], key) : 0ull;
+          const unsigned long long prev = key ? atomicMax(&a.keys[key_index(k, B, b)], key) : 0ull;
           s_flag[1] = (int)(prev >> 63);
           a.qpart[((size_t)k * B + b) * G + g] = make_float2(m, s);
         }

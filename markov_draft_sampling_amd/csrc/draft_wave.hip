@@ -29,6 +29,7 @@ namespace mds {
 namespace {
 
 constexpr int kRKMax = 8;  // rank slices of 32 (r <= 256)
+constexpr int kRing = 2;   // ring entries (tiles in flight + the tile in use) per wave in the fast loop
 
 // F64: the fp64 Gumbel option (scores and the running winner in float64).
 // FL: compile the fixed-count fast loop; it raises the register count to one
@@ -104,6 +105,13 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
 #pragma unroll
     for (int s = 0; s < kRKMax; ++s) A[s] = *(const u32x4*)(p + (s < RK ? s : RK - 1) * 32);
   };
+  // rank r = 32 kRKMax: every slice is real, the offsets are constants
+  auto load_a_full = [&](int t, u32x4 (&A)[kRKMax]) {
+    const int v = t * 16 + lr;
+    const uint16_t* p = a.w2 + (size_t)(v < V ? v : V - 1) * r + lg * 8;
+#pragma unroll
+    for (int s = 0; s < kRKMax; ++s) A[s] = *(const u32x4*)(p + s * 32);
+  };
   auto load_base_vec = [&](int t, float (&bz)[NT][4]) {
     const int c = t * 16 + lg * 4;
 #pragma unroll
@@ -172,7 +180,7 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
     int prev = -1;  // rows that are not served get a zero embedding
     if (draft_slot(a, b) >= 0) {
       // the previous step's winner (key 0, i.e. -1, when that step was inert)
-      long long tk = (k == 0) ? (long long)a.anchor[b] : (long long)key_col(a.keys[(size_t)(k - 1) * a.B + b], F64);
+      long long tk = (k == 0) ? (long long)a.anchor[b] : (long long)key_col(a.keys[key_index(k - 1, a.B, b)], F64);
       if (tk < 0 || tk >= V) {
         set_status(a.status, kStatusBadAnchor);
         tk = 0;
@@ -238,87 +246,133 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
 #pragma unroll
       for (int s = 0; s < kRKMax; ++s)
         Er[nt][s] = *(const bf16x8*)(s_e + (nt * 16 + lr) * rs + (s < RK ? s : 0) * 32 + lg * 8);
-    auto run_fast = [&](auto t1_tag) {
+    // One full tile of the fast loop: bias by MFMA from the ring entry's w2
+    // rows, then the branch-free epilogue. `live` is 1 for every tile the
+    // loop computes; the accumulation of q statistics multiplies by it.
+    auto fast_tile = [&](auto t1_tag, auto full_tag, int t, const u32x4 (&Ab)[kRKMax], const float (&bzb)[NT][4]) {
       constexpr bool T1 = decltype(t1_tag)::value;
+      constexpr bool FULL = decltype(full_tag)::value;
+      floatx4 acc[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int s = 0; s < kRKMax; ++s) {
+        if (FULL || s < RK) {
+          const bf16x8 afr = __builtin_bit_cast(bf16x8, Ab[s]);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, Er[nt][s], acc[nt], 0, 0, 0);
+        }
+      }
+      const int c = t * 16 + lg * 4;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        float z[4], cv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[i] = bzb[nt][i] + acc[nt][i];
+        if (CBF16) {
+          uint32_t h[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            h[i] = f32_to_bf16_bits(z[i]);
+            cv[i] = bf16_bits_to_f32(h[i]);
+          }
+          u32x2 w;
+          w.x = h[0] | (h[1] << 16);
+          w.y = h[2] | (h[3] << 16);
+          *(u32x2*)((uint16_t*)a.cache + rcache[nt] + c) = w;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) cv[i] = z[i];
+          *(f32x4*)((float*)a.cache + rcache[nt] + c) = f32x4{z[0], z[1], z[2], z[3]};
+        }
+        const Philox4 w = philox4x32_10((uint32_t)(c >> 2), pk0[nt], pk1[nt], kSaltDraft, sk0[nt], sk1[nt]);
+        const uint32_t wd[4] = {w.x0, w.x1, w.x2, w.x3};
+        float y[4], x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          y[i] = T1 ? z[i] : div_t(z[i], Tv[nt], invT[nt]);
+          x[i] = CBF16 ? (T1 ? cv[i] : div_t(cv[i], Tv[nt], invT[nt])) : y[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          Score sv;
+          if (F64)
+            sv = (T1 ? (double)z[i] : (double)z[i] / (double)Tv[nt]) + gumbel64_from_word(wd[i]);
+          else
+            sv = y[i] + gumbel_from_word(wd[i]);
+          // the winner rule as one mask: a held NaN stays; otherwise a NaN
+          // or a strictly larger score replaces it
+          const bool take = (bv[nt] == bv[nt]) & !(sv <= bv[nt]);
+          bv[nt] = take ? sv : bv[nt];
+          bi[nt] = take ? c + i : bi[nt];
+        }
+        const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));  // NaN-ignoring max
+        const float mn = fmaxf(qm[nt], mx);
+        const float sub = mn == -INFINITY ? 0.0f : mn;
+        float s_acc = qs[nt] * fast_exp(qm[nt] - sub);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s_acc += fast_exp(x[i] - sub);
+        qs[nt] = s_acc;
+        qm[nt] = mn;
+      }
+    };
+    // The loop keeps kRing tiles in flight per wave: ring entry i holds tile
+    // t + 4 i. Entries are refilled right after their tile is computed, with
+    // the tile kRing steps ahead, so a load has kRing - 1 tiles of compute
+    // to arrive. The loop is unrolled over the ring (no register copies,
+    // which would wait for the loads) and runs whole turns only; the last
+    // partial turn computes the entries already loaded.
+    auto run_fast = [&](auto t1_tag, auto full_tag) {
+      constexpr bool FULL = decltype(full_tag)::value;
+      auto load = [&](int tt, u32x4 (&Ab)[kRKMax]) {
+        if (FULL)
+          load_a_full(tt, Ab);
+        else
+          load_a(tt, Ab);
+      };
       int t = t_first;
       if (t < full_end) {
         const int t_lastf = t_first + ((full_end - 1 - t_first) / 4) * 4;
-        for (; t < full_end; t += 4) {
-          const int tn = t + 4 < full_end ? t + 4 : t_lastf;  // the last tile again at the end: cache hits
-          load_a(tn, An);
-          load_base_vec(tn, bzn);
-          floatx4 acc[NT];
+        const int n_tiles = (t_lastf - t_first) / 4 + 1;
+        const int n_turns = n_tiles / kRing;
+        u32x4 Ar[kRing][kRKMax];
+        float bzr[kRing][NT][4];
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) acc[nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int s = 0; s < kRKMax; ++s) Ar[0][s] = A[s];
 #pragma unroll
-          for (int s = 0; s < kRKMax; ++s) {
-            if (s < RK) {
-              const bf16x8 afr = __builtin_bit_cast(bf16x8, A[s]);
+        for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-              for (int nt = 0; nt < NT; ++nt) acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, Er[nt][s], acc[nt], 0, 0, 0);
-            }
-          }
-          const int c = t * 16 + lg * 4;
+          for (int i = 0; i < 4; ++i) bzr[0][nt][i] = bz[nt][i];
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            float z[4], cv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) z[i] = bz[nt][i] + acc[nt][i];
-            if (CBF16) {
-              uint32_t h[4];
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                h[i] = f32_to_bf16_bits(z[i]);
-                cv[i] = bf16_bits_to_f32(h[i]);
-              }
-              u32x2 w;
-              w.x = h[0] | (h[1] << 16);
-              w.y = h[2] | (h[3] << 16);
-              *(u32x2*)((uint16_t*)a.cache + rcache[nt] + c) = w;
-            } else {
-#pragma unroll
-              for (int i = 0; i < 4; ++i) cv[i] = z[i];
-              *(f32x4*)((float*)a.cache + rcache[nt] + c) = f32x4{z[0], z[1], z[2], z[3]};
-            }
-            const Philox4 w = philox4x32_10((uint32_t)(c >> 2), pk0[nt], pk1[nt], kSaltDraft, sk0[nt], sk1[nt]);
-            const uint32_t wd[4] = {w.x0, w.x1, w.x2, w.x3};
-            float y[4], x[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              y[i] = T1 ? z[i] : div_t(z[i], Tv[nt], invT[nt]);
-              x[i] = CBF16 ? (T1 ? cv[i] : div_t(cv[i], Tv[nt], invT[nt])) : y[i];
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              Score sv;
-              if (F64)
-                sv = (T1 ? (double)z[i] : (double)z[i] / (double)Tv[nt]) + gumbel64_from_word(wd[i]);
-              else
-                sv = y[i] + gumbel_from_word(wd[i]);
-              const bool take = (sv > bv[nt]) || ((sv != sv) && (bv[nt] == bv[nt]));
-              bv[nt] = take ? sv : bv[nt];
-              bi[nt] = take ? c + i : bi[nt];
-            }
-            const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));  // NaN-ignoring max
-            const float mn = fmaxf(qm[nt], mx);
-            const float sub = mn == -INFINITY ? 0.0f : mn;
-            float s_acc = qs[nt] * fast_exp(qm[nt] - sub);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) s_acc += fast_exp(x[i] - sub);
-            qs[nt] = s_acc;
-            qm[nt] = mn;
-          }
-#pragma unroll
-          for (int s = 0; s < kRKMax; ++s) A[s] = An[s];
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) bz[nt][i] = bzn[nt][i];
+        for (int e = 1; e < kRing; ++e) {
+          const int te = t + 4 * e <= t_lastf ? t + 4 * e : t_lastf;  // past the last tile: that tile again (cache hits)
+          load(te, Ar[e]);
+          load_base_vec(te, bzr[e]);
         }
+        for (int turn = 0; turn < n_turns; ++turn) {
+#pragma unroll
+          for (int e = 0; e < kRing; ++e) {
+            fast_tile(t1_tag, full_tag, t + 4 * e, Ar[e], bzr[e]);
+            const int tn = t + 4 * (e + kRing) <= t_lastf ? t + 4 * (e + kRing) : t_lastf;
+            load(tn, Ar[e]);
+            load_base_vec(tn, bzr[e]);
+          }
+          t += 4 * kRing;
+        }
+        const int rest = n_tiles - n_turns * kRing;
+#pragma unroll
+        for (int e = 0; e < kRing - 1; ++e)
+          if (e < rest) fast_tile(t1_tag, full_tag, t + 4 * e, Ar[e], bzr[e]);
+        t += 4 * rest;
       }
       return t;
     };
-    t_gen = t1 ? run_fast(std::integral_constant<bool, true>()) : run_fast(std::integral_constant<bool, false>());
+    using True = std::integral_constant<bool, true>;
+    using False = std::integral_constant<bool, false>;
+    if (RK == kRKMax)
+      t_gen = t1 ? run_fast(True(), True()) : run_fast(False(), True());
+    else
+      t_gen = t1 ? run_fast(True(), False()) : run_fast(False(), False());
     if (t_gen < mt_end) {  // the partial last tile: its operands again, for the general loop
       load_a(t_gen, A);
       load_base(t_gen, bz);
@@ -390,7 +444,7 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
             sv = (T1 ? (double)z[i] : (double)z[i] / (double)Tv[nt]) + gumbel64_from_word(wd[i]);
           else
             sv = y[i] + gumbel_from_word(wd[i]);
-          const bool take = (sv > bv[nt]) || ((sv != sv) && (bv[nt] == bv[nt]));
+          const bool take = (bv[nt] == bv[nt]) & !(sv <= bv[nt]);
           bv[nt] = take ? sv : bv[nt];
           bi[nt] = take ? c + i : bi[nt];
         }
@@ -518,7 +572,7 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
       key = k2 > key ? k2 : key;
       lse_merge(m, s, s_qm[w * NB + i], s_qs[w * NB + i]);
     }
-    if (key) atomicMax(&a.keys[(size_t)k * a.B + b], key);
+    if (key) atomicMax(&a.keys[key_index(k, a.B, b)], key);
     a.qpart[((size_t)k * a.B + b) * a.G + g] = make_float2(m, s);
   }
 }

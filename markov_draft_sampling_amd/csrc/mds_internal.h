@@ -10,6 +10,12 @@ namespace mds {
 // ------------------------------------------------------------ draft loop --
 constexpr int kDraftMaxSlabs = 1024;    // column slabs (work-groups) per batch tile and step
 constexpr int kDraftMinTilesPerSlab = 8;  // 16-column tiles per slab, at least
+// Winner keys sit one 128-byte line apart: every work-group of a step merges
+// into every request's key, and atomics on keys sharing a line serialise.
+constexpr int kKeyStride = 16;  // u64 words from one (step, request) key to the next
+__host__ __device__ __forceinline__ size_t key_index(int k, int B, int b) {
+  return ((size_t)k * B + b) * kKeyStride;
+}
 
 struct DraftStepArgs {
   int B, K, V, r, k, G, nMT, BT;
@@ -24,7 +30,7 @@ struct DraftStepArgs {
   const long long* seeds;
   void* cache;
   long long cache_rs, cache_ss;
-  unsigned long long* keys;  // [K][B] winner keys
+  unsigned long long* keys;  // [K][B] winner keys at key_index(k, B, b)
   float2* qpart;             // [K][B][G] (max, sum exp) of cache / T per slab
   uint32_t* status;
   unsigned* bar;             // [K] grid-barrier arrival counters (resident kernel)
