@@ -166,6 +166,8 @@ struct ReqLds {
   int acc[kMaxK];
   int x[kMaxK];             // draft tokens (sampled requests: clamped into [0, V))
   float tx[kMaxK], cx[kMaxK];  // target and cache logits at the draft tokens
+  unsigned long long seed;     // the request's seed and anchor position, loaded ahead by the caller
+  long long pos0;
 };
 
 // Draft token k of request b (state slot s) and the target / cache logits at
@@ -303,8 +305,8 @@ __device__ void decide(const VerifyArgs& a, int b, int sl, ReqLds& L) {
       if (!a.topp || kept(a.topp[row], tx, x)) logp = div_t(tx, T, invT) - L.m[k] - L.lz[k];
       const float p = expf(logp);
       const float q = expf(div_t(L.cx[k], T, invT) - L.lq[k]);
-      const unsigned long long sd = (unsigned long long)a.seeds[sl];
-      const unsigned long long pk = (unsigned long long)(a.anchor_pos[b] + k);
+      const unsigned long long sd = L.seed;
+      const unsigned long long pk = (unsigned long long)(L.pos0 + k);
       const Philox4 w = philox4x32_10(0u, (uint32_t)pk, (uint32_t)(pk >> 32), kSaltAccept, (uint32_t)sd,
                                       (uint32_t)(sd >> 32));
       const float u = uniform24(w.x0);
@@ -342,32 +344,57 @@ __device__ void decide(const VerifyArgs& a, int b, int sl, ReqLds& L) {
   }
 }
 
-// Run by wave 0 of the last work-group of request b: combine every partial of
-// the request, write the row statistics and, without top-p, decide. Resets
-// the request's counter.
-__device__ void combine_request(const VerifyArgs& a, int b, int sl, ReqLds& L, unsigned long long* stage) {
+// Combine every partial of request b, write the row statistics and, without
+// top-p, decide. Run by one wave: either wave 0 of the statistics pass's last
+// work-group of the request (counted: it resets the request's arrival
+// counter, and block 0 of each target row published the logits at the draft
+// tokens), or a work-group of its own after the whole pass (the partials are
+// then plain stores of the finished pass, and the logits are read here).
+__device__ void combine_request(const VerifyArgs& a, int b, int sl, ReqLds& L, unsigned long long* stage,
+                                bool counted) {
   const int K = a.K, NC = a.NC;
   const int lane = threadIdx.x & 63;
   if (sl < 0) {  // padding request: nothing was published
-    if (lane == 0) atomicExch(a.cnt + verify_counter_index(b), 0u);
+    if (counted && lane == 0) atomicExch(a.cnt + verify_counter_index(b), 0u);
     if (a.decide) finish_padding(a, b);
     return;
   }
-  const bool greedy = !(a.temp[sl] > 0.0f);
-  // the draft tokens, and the logits at them that block 0 of each target row
-  // published, load together with the partials
+  // every load that depends on nothing else goes out first: temperature,
+  // draft tokens, draft normalisers, seed and position; then (sampled
+  // requests, no publication) the logits at the draft tokens, in flight
+  // together with the partials
+  const float T = a.temp[sl];
+  int x0 = 0;
+  float lq0 = 0.0f;
   if (lane < K) {
-    const int x = a.draft[b * K + lane];
+    x0 = a.draft[b * K + lane];
+    if (a.draft_lse) lq0 = a.draft_lse[b * K + lane];
+  }
+  if (a.decide && lane == 0) {  // only the decision reads them (the top-p debug entry passes neither)
+    L.seed = (unsigned long long)a.seeds[sl];
+    L.pos0 = a.anchor_pos[b];
+  }
+  const bool greedy = !(T > 0.0f);
+  int xp = 0;
+  float txp = 0.0f, cxp = 0.0f;
+  if (lane < K) {
     if (greedy) {
-      L.x[lane] = x;
-    } else {
+      L.x[lane] = x0;
+    } else if (counted) {
       const unsigned long long w = __hip_atomic_load(a.tq + b * K + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      L.x[lane] = (x == -1) ? -1 : ((x < 0 || x >= a.V) ? 0 : x);
+      L.x[lane] = (x0 == -1) ? -1 : ((x0 < 0 || x0 >= a.V) ? 0 : x0);
       L.tx[lane] = unpack_m(w);
       L.cx[lane] = unpack_s(w);
+    } else {
+      draft_point(a, b, sl, lane, xp, txp, cxp);
     }
   }
   wave_combine(a.tpart + (size_t)b * (K + 1), (size_t)a.B * (K + 1), K + 1, NC, greedy, stage, L.m, L.lz, L.key);
+  if (!counted && !greedy && lane < K) {
+    L.x[lane] = xp;
+    L.tx[lane] = txp;
+    L.cx[lane] = cxp;
+  }
   if (lane <= K) {
     const float s = L.lz[lane];
     const float lz = (s != s) ? NAN : __logf(s);
@@ -383,20 +410,22 @@ __device__ void combine_request(const VerifyArgs& a, int b, int sl, ReqLds& L, u
       a.qlse[b * K + lane] = lq;
     }
   } else if (lane < K) {
-    const float lq = greedy ? 0.0f : a.draft_lse[b * K + lane];
+    const float lq = greedy ? 0.0f : lq0;
     L.lq[lane] = lq;
     a.qlse[b * K + lane] = lq;
   }
-  if (lane == 0) atomicExch(a.cnt + verify_counter_index(b), 0u);
+  if (counted && lane == 0) atomicExch(a.cnt + verify_counter_index(b), 0u);
   wave_lds_sync();
   if (a.decide) decide(a, b, sl, L);
 }
 
 // Grid (NC, rows) with rows = B(K+1) target rows, then B*K cache rows when
 // draft_lse is null; rows are split over y and z (y at most 32768).
+// LAST: the request's last-arriving work-group combines (and decides);
+// otherwise the partials are plain stores and combine_kernel follows, which
+// keeps the combining code, and its registers, out of this streaming pass.
+template <bool LAST>
 __global__ __launch_bounds__(kThreads) void stats_kernel(VerifyArgs a) {
-  __shared__ ReqLds L;
-  __shared__ unsigned long long stage[kStage];
   const int chunk = blockIdx.x;
   const int row = (int)blockIdx.z * (int)gridDim.y + (int)blockIdx.y;
   const int K = a.K, V = a.V, NC = a.NC;
@@ -444,6 +473,12 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(VerifyArgs a) {
   // waves 1..3 are done; wave 0 publishes and, if it is the request's last
   // arrival, combines
   if (threadIdx.x >= 64) return;
+  if (!LAST) {
+    if (threadIdx.x == 0 && slot) *slot = word;
+    return;
+  }
+  __shared__ ReqLds L;
+  __shared__ unsigned long long stage[kStage];
   int last = 0;
   if (threadIdx.x == 0) {
     if (slot) {
@@ -466,7 +501,15 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(VerifyArgs a) {
   }
   last = __shfl(last, 0);
   if (!last) return;
-  combine_request(a, b, sl, L, stage);
+  combine_request(a, b, sl, L, stage, true);
+}
+
+// After a statistics pass without arrival counting: one wave per request.
+__global__ __launch_bounds__(64) void combine_kernel(VerifyArgs a) {
+  __shared__ ReqLds L;
+  __shared__ unsigned long long stage[kStage];
+  const int b = blockIdx.x;
+  combine_request(a, b, verify_slot(a, b), L, stage, false);
 }
 
 // With top-p: one wave per request after the top-p kernel.
@@ -478,6 +521,10 @@ __global__ __launch_bounds__(64) void decide_kernel(VerifyArgs a) {
   if (sl < 0) {
     finish_padding(a, b);
     return;
+  }
+  if (j == 0) {
+    L.seed = (unsigned long long)a.seeds[sl];
+    L.pos0 = a.anchor_pos[b];
   }
   if (j <= K) {
     const RowStat rs = a.rowstat[b * (K + 1) + j];
@@ -692,11 +739,19 @@ __global__ void debug_gumbel_kernel(int n, const uint32_t* words, float* g) {
 
 }  // namespace
 
-hipError_t launch_verify_stats(const VerifyArgs& a, hipStream_t st) {
+hipError_t launch_verify_stats(const VerifyArgs& a, bool last_arrival, hipStream_t st) {
   const int rows = a.B * (a.K + 1) + (a.qpart ? a.B * a.K : 0);
   const int gy = rows < 32768 ? rows : 32768;
   const int gz = (rows + gy - 1) / gy;
-  hipLaunchKernelGGL(stats_kernel, dim3(a.NC, gy, gz), dim3(kThreads), 0, st, a);
+  if (last_arrival)
+    hipLaunchKernelGGL(stats_kernel<true>, dim3(a.NC, gy, gz), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(stats_kernel<false>, dim3(a.NC, gy, gz), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const VerifyArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(combine_kernel, dim3(a.B), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 
