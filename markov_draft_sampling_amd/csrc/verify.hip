@@ -2,30 +2,33 @@
 //
 // PR #65007 (Part 2) describes the stock rejection sampler as per-block
 // kernels over 8192-column statistics blocks whose partials per-request
-// kernels combine, plus residual-mass and resample kernels. Here two
-// launches do the whole pass when there is no top-p:
-//   stats_kernel     one work-group per (row, 8192-column block) streams the
-//                    target rows (and the draft cache rows when the draft
-//                    loop gave no log-normalisers): (max, sum exp) of
-//                    logit / T for sampled requests, the winner key of the
-//                    raw logits for greedy ones (PR #63554, Notes: greedy
+// kernels combine, plus residual-mass and resample kernels. Here, without
+// top-p, three launches do the whole pass:
+//   stats_kernel<false>  one work-group per (row, kStatsChunk-column block)
+//                    streams the target rows (and the draft cache rows when
+//                    the draft loop gave no log-normalisers): (max, sum exp)
+//                    of logit / T for sampled requests, the winner key of
+//                    the raw logits for greedy ones (PR #63554, Notes: greedy
 //                    verification compares with the target argmax and never
-//                    reads the draft cache). The last work-group of a request
-//                    to finish combines its partials and runs the K accept
-//                    tests p(x) >= u * q(x);
+//                    reads the draft cache), one plain partial store per
+//                    block;
+//   combine_kernel   one wave per request combines the partials and runs the
+//                    K accept tests p(x) >= u * q(x);
 //   residual_kernel  one work-group per (request, 2048-column block) draws
 //                    over its block with Gumbel-max from the normalised
 //                    residual max(0, p - q) of the first rejected row, or
 //                    from p for the bonus token; the last one of a request
 //                    writes the output tokens.
-// With top-p the statistics pass only combines rows; the top-p kernel and a
-// small decide_kernel (one work-group per request) sit in between.
+// With top-p, stats_kernel<true>'s last-arriving work-group per request
+// combines, top_p_kernel (topp.hip) finds the kept sets, decide_kernel runs
+// the accept tests, then the residual pass.
 //
-// Cross-work-group hand-off inside a launch: partials and winner keys are
-// published with device-scope atomic read-modify-writes whose completion the
-// publishing thread waits for before it bumps the request's arrival counter;
-// the last arrival reads them back with read-modify-writes as well. Every
-// counter returns to zero before the call ends.
+// Cross-work-group hand-off inside a launch (the counting statistics pass and
+// the residual pass): partials and winner keys are published with
+// device-scope atomic read-modify-writes whose completion the publishing
+// thread waits for before it bumps the request's arrival counter; the last
+// arrival reads them back with read-modify-writes as well. Every counter
+// returns to zero before the call ends.
 #include "mds_device.h"
 #include "mds_internal.h"
 
@@ -34,7 +37,7 @@ namespace mds {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPerThread = kStatsChunk / kThreads;  // 32 columns: c0 + 1024 i + 4 tid + e
+constexpr int kPerThread = kStatsChunk / kThreads;  // columns c0 + 1024 i + 4 tid + e
 constexpr int kMaxK = 32;
 
 __device__ __forceinline__ float load_f32_or_bf16(const void* p, long long off, int bf16) {
@@ -53,9 +56,9 @@ __device__ __forceinline__ float unpack_m(unsigned long long p) { return __uint_
 __device__ __forceinline__ float unpack_s(unsigned long long p) { return __uint_as_float((uint32_t)(p >> 32)); }
 __device__ __forceinline__ unsigned long long rmw_read(unsigned long long* p) { return atomicAdd(p, 0ull); }
 
-// The 32 values of one 8192-column block that this thread owns. When the
-// whole block exists and vector access is allowed (a block-uniform test) all
-// eight loads are issued before any value is used.
+// The kPerThread values of one statistics block that this thread owns. When
+// the whole block exists and vector access is allowed (a block-uniform test)
+// all its loads are issued before any value is used.
 template <bool BF16>
 __device__ __forceinline__ void load_block(const void* rowp, int V, int c0, bool vec, float pad,
                                            float (&v)[kPerThread]) {
