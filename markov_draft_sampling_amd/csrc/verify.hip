@@ -350,9 +350,9 @@ __device__ void decide(const VerifyArgs& a, int b, int sl, ReqLds& L) {
 // Combine every partial of request b, write the row statistics and, without
 // top-p, decide. Run by one wave: either wave 0 of the statistics pass's last
 // work-group of the request (counted: it resets the request's arrival
-// counter, and block 0 of each target row published the logits at the draft
-// tokens), or a work-group of its own after the whole pass (the partials are
-// then plain stores of the finished pass, and the logits are read here).
+// counter), or a work-group of its own after the whole pass (the partials are
+// then plain stores of the finished pass). Either way block 0 of each target
+// row has recorded the target and cache logits at the draft tokens.
 __device__ void combine_request(const VerifyArgs& a, int b, int sl, ReqLds& L, unsigned long long* stage,
                                 bool counted) {
   const int K = a.K, NC = a.NC;
@@ -362,10 +362,9 @@ __device__ void combine_request(const VerifyArgs& a, int b, int sl, ReqLds& L, u
     if (a.decide) finish_padding(a, b);
     return;
   }
-  // every load that depends on nothing else goes out first: temperature,
-  // draft tokens, draft normalisers, seed and position; then (sampled
-  // requests, no publication) the logits at the draft tokens, in flight
-  // together with the partials
+  // every load goes out together: temperature, draft tokens, draft
+  // normalisers, seed and position, the logits at the draft tokens (recorded
+  // by block 0 of each target row) and the partials
   const float T = a.temp[sl];
   int x0 = 0;
   float lq0 = 0.0f;
@@ -378,26 +377,17 @@ __device__ void combine_request(const VerifyArgs& a, int b, int sl, ReqLds& L, u
     L.pos0 = a.anchor_pos[b];
   }
   const bool greedy = !(T > 0.0f);
-  int xp = 0;
-  float txp = 0.0f, cxp = 0.0f;
   if (lane < K) {
     if (greedy) {
       L.x[lane] = x0;
-    } else if (counted) {
+    } else {
       const unsigned long long w = __hip_atomic_load(a.tq + b * K + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       L.x[lane] = (x0 == -1) ? -1 : ((x0 < 0 || x0 >= a.V) ? 0 : x0);
       L.tx[lane] = unpack_m(w);
       L.cx[lane] = unpack_s(w);
-    } else {
-      draft_point(a, b, sl, lane, xp, txp, cxp);
     }
   }
   wave_combine(a.tpart + (size_t)b * (K + 1), (size_t)a.B * (K + 1), K + 1, NC, greedy, stage, L.m, L.lz, L.key);
-  if (!counted && !greedy && lane < K) {
-    L.x[lane] = xp;
-    L.tx[lane] = txp;
-    L.cx[lane] = cxp;
-  }
   if (lane <= K) {
     const float s = L.lz[lane];
     const float lz = (s != s) ? NAN : __logf(s);
@@ -477,7 +467,18 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(VerifyArgs a) {
   // arrival, combines
   if (threadIdx.x >= 64) return;
   if (!LAST) {
-    if (threadIdx.x == 0 && slot) *slot = word;
+    if (threadIdx.x == 0) {
+      if (slot) *slot = word;
+      // block 0 of target row k < K of a sampled request also records the
+      // target and cache logits at draft token k, for the accept test
+      const int k = row - b * (K + 1);
+      if (is_target && chunk == 0 && k < K && sl >= 0 && a.temp[sl] > 0.0f) {
+        int x;
+        float tx, cx;
+        draft_point(a, b, sl, k, x, tx, cx);
+        a.tq[b * K + k] = pack_ms(tx, cx);
+      }
+    }
     return;
   }
   __shared__ ReqLds L;
