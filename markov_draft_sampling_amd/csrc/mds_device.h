@@ -61,11 +61,12 @@ __device__ __forceinline__ float uniform24(uint32_t w) {
 
 // Standard Gumbel -log(-log u) with hardware base-2 logs:
 // -ln(-ln u) = -ln(ln 2) - ln 2 * log2(-log2 u).
-__device__ __forceinline__ float gumbel_from_word(uint32_t w) {
-  const float u = uniform24(w);
-  const float e2 = -__builtin_amdgcn_logf(u);  // -log2(u) > 0, u in (0, 1) normal
+// E2 = -log2(u) > 0 of the word's uniform (u in (0, 1), normal)
+__device__ __forceinline__ float neg_log2_uniform(uint32_t w) { return -__builtin_amdgcn_logf(uniform24(w)); }
+__device__ __forceinline__ float gumbel_from_e2(float e2) {
   return __builtin_fmaf(-0x1.62e430p-1f, __builtin_amdgcn_logf(e2), 0x1.774f2ap-2f);
 }
+__device__ __forceinline__ float gumbel_from_word(uint32_t w) { return gumbel_from_e2(neg_log2_uniform(w)); }
 
 // ---------------------------------------------------------- winner keys --
 // Total order of the winner rule: NaN above every value, -0 == +0, and on

@@ -660,6 +660,11 @@ __global__ __launch_bounds__(kThreads) void residual_kernel(VerifyArgs a) {
   }
   float bv = -INFINITY;
   int bi = -1;
+  // residual draw: the thread's winner of log r + g = log(r / (ln 2 * E2)),
+  // E2 = -log2 u, found by comparing r / E2 across its columns (cross-
+  // multiplied, strict: the lower column keeps a tie); its score then takes
+  // the same float operations as in the bonus draw
+  float rb = 0.0f, eb = 1.0f;
 #pragma unroll
   for (int i = 0; i < kPer / 4; ++i) {
     const int c = tc + i * 1024;
@@ -669,22 +674,23 @@ __global__ __launch_bounds__(kThreads) void residual_kernel(VerifyArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if (c + e < V) {
-        const float g = gumbel_from_word(wd[e]);
         const float logp = draw_logp(d, tv[4 * i + e], c + e);
         if (resid) {
           const int q = 4 * i + e;
           const float cq = CBF16 ? bf16_bits_to_f32((q & 1) ? (cw[q >> 1] >> 16) : (cw[q >> 1] & 0xFFFFu)) : cv[q];
           const float rv = __expf(logp) - __expf(div_t(cq, d.T, d.invT) - d.LQ);
-          const float sr = fmaxf(__logf(rv), -0x1.fffffep+127f) + g;
-          const bool take = rv > 0.0f && (sr > bv || bi < 0);
-          bv = take ? sr : bv;
+          const float e2 = neg_log2_uniform(wd[e]);
+          const bool take = rv > 0.0f && (bi < 0 || rv * eb > rb * e2);
+          rb = take ? rv : rb;
+          eb = take ? e2 : eb;
           bi = take ? c + e : bi;
         } else {
-          win_update(bv, bi, logp + g, c + e);
+          win_update(bv, bi, logp + gumbel_from_word(wd[e]), c + e);
         }
       }
     }
   }
+  if (resid && bi >= 0) bv = fmaxf(__logf(rb), -0x1.fffffep+127f) + gumbel_from_e2(eb);
   const unsigned long long key = block_max_key(bi >= 0 ? win_key(bv, (uint32_t)bi) : 0ull);
   // waves 1..3 are done; wave 0 publishes and, if last, finishes the request
   if (threadIdx.x >= 64) return;
