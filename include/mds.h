@@ -118,7 +118,11 @@ int mds_verify_workspace_bytes(int B, int K, int V, int has_top_p, int has_draft
  *                         cache[b,k,v] / T_b, the normaliser of the draft distribution
  *                         q_k that verification needs (NaN if the row holds NaN,
  *                         unspecified for greedy requests)
- *   workspace             >= mds_draft_workspace_bytes(B, K, V, r) bytes, 256-byte aligned
+ *   workspace             >= mds_draft_workspace_bytes(B, K, V, r) bytes, 256-byte aligned,
+ *                         zeroed when allocated; the library keeps part of it at zero
+ *                         between calls (so a call needs no clearing launch), so the
+ *                         caller must not write it between calls (it may be shared
+ *                         with top-k drafting calls)
  *   stream                hipStream_t as void*
  *
  * Kernels: when w2 fits in the chip's registers and LDS (V*r*2 bytes within
@@ -270,7 +274,9 @@ int mds_draft_topk_workspace_bytes(int B, int K, int V, int r, int topk, size_t*
  *   flags       MDS_DRAFT_FP64_GUMBEL: float64 variates and scores, winner
  *               taken exactly over the float64 scores;
  *   workspace   >= mds_draft_topk_workspace_bytes(B, K, V, r, topk) bytes,
- *               256-byte aligned, status word zeroed before first use;
+ *               256-byte aligned, zeroed when allocated and not written by the
+ *               caller between calls (it may be shared with the dense draft
+ *               calls, whose zero-kept region it leaves untouched);
  *   ev_begin / ev_end  hipEvent_t (as void*) or NULL: recorded around the
  *               candidate-selection launch (the kernel that streams the base
  *               logits and writes the -inf cache rows).

@@ -53,19 +53,30 @@ bool vec_ok(const void* p, int dtype, long long rs, long long ss) {
   return aligned(p, dtype == MDS_BF16 ? 8 : 16) && rs % 4 == 0 && ss % 4 == 0;
 }
 
-// Draft workspace: [status | keys K*B u64, one per 128-byte line | barrier words K+1 u32 | per-slab
-// (max, sum exp) partials K*B*kDraftMaxSlabs]. Sized without the device so the
-// query needs no GPU.
+// Draft workspace: [status | kFixedKeys winner keys, one per 128-byte line,
+// kept at zero between calls | the call's keys when K*B > kFixedKeys |
+// barrier words K+1 u32 | per-slab (max, sum exp) partials
+// K*B*kDraftMaxSlabs]. Sized without the device so the query needs no GPU.
 struct DraftLayout {
   int nMT;
+  bool fixed_keys;  // the keys sit in the zero-kept region
   size_t keys, bar, qpart, total;
 };
+
+size_t fixed_keys_bytes() { return up((size_t)mds::kFixedKeys * 8 * mds::kKeyStride); }
 
 DraftLayout draft_layout(int B, int K, int V) {
   DraftLayout L;
   L.nMT = (V + 15) / 16;
-  L.keys = kAlign;
-  L.bar = L.keys + up((size_t)K * B * 8 * mds::kKeyStride);
+  size_t o = kAlign + fixed_keys_bytes();
+  L.fixed_keys = (size_t)K * B <= (size_t)mds::kFixedKeys;
+  if (L.fixed_keys) {
+    L.keys = kAlign;
+  } else {
+    L.keys = o;
+    o += up((size_t)K * B * 8 * mds::kKeyStride);
+  }
+  L.bar = o;
   L.qpart = L.bar + up((size_t)(K + 1) * 4);
   L.total = L.qpart + up((size_t)K * B * mds::kDraftMaxSlabs * sizeof(float2));
   return L;
@@ -221,7 +232,12 @@ int draft_impl(int B, int K, int V, int r, const void* base, int base_dtype, int
   const bool wave_kernel = !resident && r <= 256;
   a.G = resident ? cus : (wave_kernel ? mds::draft_wave_slabs(V, cus) : mds::draft_slabs(V, cus));
   a.n_lds_tiles = n_lds;
-  if ((e = mds::launch_draft_init(a.keys, K * B, a.bar, K + 1, st)) != hipSuccess) return hip_fail(e, "draft init launch");
+  // keys in the zero-kept region need no clearing; the persistent kernel's
+  // barrier counters always do
+  if (!L.fixed_keys || resident) {
+    if ((e = mds::launch_draft_init(a.keys, K * B, a.bar, K + 1, st)) != hipSuccess)
+      return hip_fail(e, "draft init launch");
+  }
   if (ev_begin && (e = hipEventRecord((hipEvent_t)ev_begin, st)) != hipSuccess) return hip_fail(e, "event record");
   if (resident) {
     if ((e = mds::launch_draft_resident(a, res_lds, st)) != hipSuccess) return hip_fail(e, "resident draft launch");
@@ -300,8 +316,9 @@ int verify_impl(int B, int K, int V, const float* target, int64_t target_row_str
   return ok();
 }
 
-// Top-k drafting workspace: [status | chunk keys B*K*NC*topk u64 | candidate
-// columns B*K*topk int32]
+// Top-k drafting workspace: [status | the draft workspace's zero-kept key
+// region, untouched (so either kind of call may share a workspace) | chunk
+// keys B*K*NC*topk u64 | candidate columns B*K*topk int32]
 struct TopkLayout {
   int NC;
   size_t ckeys, cand, total;
@@ -310,7 +327,7 @@ struct TopkLayout {
 TopkLayout topk_layout(int B, int K, int V, int topk) {
   TopkLayout L;
   L.NC = (V + mds::kTopkChunk - 1) / mds::kTopkChunk;
-  L.ckeys = kAlign;
+  L.ckeys = kAlign + fixed_keys_bytes();
   L.cand = L.ckeys + up((size_t)B * K * L.NC * topk * 8);
   L.total = L.cand + up((size_t)B * K * topk * 4);
   return L;

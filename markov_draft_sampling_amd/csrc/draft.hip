@@ -408,8 +408,13 @@ __global__ __launch_bounds__(256) void draft_finalize_kernel(DraftFinalArgs a) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= a.B * a.K) return;
   const int b = row / a.K, k = row - b * a.K;
-  // inert rows keep key 0, i.e. token -1
-  if (lane == 0) a.tokens[row] = key_col(a.keys[key_index(k, a.B, b)], a.fp64 != 0);
+  // inert rows keep key 0, i.e. token -1; the key is left cleared for the
+  // next call on this workspace
+  if (lane == 0) {
+    unsigned long long* kp = a.keys + key_index(k, a.B, b);
+    a.tokens[row] = key_col(*kp, a.fp64 != 0);
+    *kp = 0ull;
+  }
   if (!a.lse) return;
   const int sl = draft_slot(a.idx_map, a.row_map, a.B, a.K, a.n_slots, a.n_rows, nullptr, b, k);
   if (sl < 0) {

@@ -16,6 +16,13 @@ constexpr int kKeyStride = 16;  // u64 words from one (step, request) key to the
 __host__ __device__ __forceinline__ size_t key_index(int k, int B, int b) {
   return ((size_t)k * B + b) * kKeyStride;
 }
+// Every draft and top-k workspace starts with a region of kFixedKeys winner
+// keys that each call leaves at zero (the finalize pass clears the keys it
+// reads, and nothing else writes there), so a streaming call with
+// K * B <= kFixedKeys needs no clearing launch whatever the workspace held
+// before; larger calls, and the persistent kernel (whose barrier counters
+// need clearing too), keep theirs elsewhere and clear them first.
+constexpr int kFixedKeys = 4096;
 
 struct DraftStepArgs {
   int B, K, V, r, k, G, nMT, BT;
@@ -47,7 +54,7 @@ struct DraftStepArgs {
 
 struct DraftFinalArgs {
   int B, K, G;
-  const unsigned long long* keys;
+  unsigned long long* keys;  // read, then cleared
   const float2* qpart;
   const float* temp;
   int32_t* tokens;
