@@ -421,6 +421,7 @@ __global__ __launch_bounds__(256) void draft_finalize_kernel(DraftFinalArgs a) {
     if (lane == 0) a.lse[row] = NAN;
     return;
   }
+  const float T = a.temp[sl];  // in flight with the partials
   float m = -INFINITY, s = 0.0f;
   const float2* qp = a.qpart + ((size_t)k * a.B + b) * a.G;
   for (int i = lane; i < a.G; i += 64) {
@@ -430,7 +431,7 @@ __global__ __launch_bounds__(256) void draft_finalize_kernel(DraftFinalArgs a) {
   wave_lse_merge(m, s);
   if (lane == 0) {
     float out;
-    if (!(a.temp[sl] > 0.0f) || s != s)
+    if (!(T > 0.0f) || s != s)
       out = NAN;
     else
       out = m + __logf(s);
