@@ -122,7 +122,8 @@ int mds_verify_workspace_bytes(int B, int K, int V, int has_top_p, int has_draft
  *                         zeroed when allocated; the library keeps part of it at zero
  *                         between calls (so a call needs no clearing launch), so the
  *                         caller must not write it between calls (it may be shared
- *                         with top-k drafting calls)
+ *                         with top-k drafting calls); after a call that returned
+ *                         MDS_ERR_HIP_LAUNCH, zero it again before the next call
  *   stream                hipStream_t as void*
  *
  * Kernels: when w2 fits in the chip's registers and LDS (V*r*2 bytes within
