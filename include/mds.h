@@ -123,7 +123,7 @@ int mds_verify_workspace_bytes(int B, int K, int V, int has_top_p, int has_draft
  *                         between calls (so a call needs no clearing launch), so the
  *                         caller must not write it between calls (it may be shared
  *                         with top-k drafting calls); after a call that returned
- *                         MDS_ERR_HIP_LAUNCH, zero it again before the next call
+ *                         MDS_ERR_HIP, zero it again before the next call
  *   stream                hipStream_t as void*
  *
  * Kernels: when w2 fits in the chip's registers and LDS (V*r*2 bytes within
