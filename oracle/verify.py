@@ -24,6 +24,12 @@ Readings where the pages are silent:
 * a residual with zero total mass (p == q, or a draft row holding NaN, which
   makes every q NaN) falls back to sampling from p;
 * top_p >= 1 disables top-p for a request;
+* a row with no finite logit (every entry -inf: all columns masked) has no
+  softmax; its distribution is taken to be the one-hot at column 0, the
+  column the winner rule gives such a row (the first of equal maxima). This
+  holds for a target row (p, and so its top-p kept set {0}) and for a draft
+  cache row (q); the pages' top-p tests name such rows without stating the
+  result;
 * a draft token of -1 is a placeholder (PR #65007, Tests: rejection sampling
   with -1 placeholder drafts): the request's drafts end there, so the draw
   after the accepted run is taken from p of that row, as when all K drafts
@@ -42,7 +48,13 @@ from .noise import SALT_RESAMPLE, accept_uniform, gumbel_row
 
 
 def _softmax(x64: np.ndarray) -> np.ndarray:
+    """softmax of a row of finite values, -inf (masked columns) and +inf-free;
+    a row with no finite value gives the one-hot at column 0 (see above)."""
     m = np.max(x64)
+    if m == -np.inf:
+        p = np.zeros(x64.shape, np.float64)
+        p[0] = 1.0
+        return p
     e = np.exp(x64 - m)
     return e / e.sum()
 
@@ -55,7 +67,8 @@ def top_p_keep(t_row, T: float, p: float):
     cumulative probability is >= p, and the row maximum is always kept.
     near_boundary is True when the cumulative mass at the cut (or one column
     before it) lies within 1e-6 of p: there a float32 implementation may keep
-    a different set (the pages' own test excludes such rows).
+    a different set (the pages' own test excludes such rows). A row with no
+    finite logit keeps {0}: its distribution is the one-hot at column 0.
     """
     t = np.asarray(t_row, dtype=np.float64)
     V = t.size

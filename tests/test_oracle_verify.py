@@ -224,3 +224,63 @@ def test_whole_pipeline_first_token_follows_target(T):
     sel = v["num_accepted"] >= 1
     assert sel.sum() > 2000
     assert _chi2_ok(np.bincount(v["out_tokens"][sel, 1], minlength=V), p1)
+
+
+# Rows with no finite logit (every column masked, -inf): the winner rule gives
+# such a row column 0, and its distribution is read as the one-hot there.
+
+def test_no_finite_target_row_keeps_column_zero_under_top_p():
+    z = np.full(37, -np.inf, np.float32)
+    for p in (0.01, 0.5, 0.95, 1 - 1e-7):
+        keep, _ = top_p_keep(z, np.float32(0.8), np.float32(p))
+        assert keep[0] and keep.sum() == 1
+
+
+def test_no_finite_target_rows_emit_column_zero():
+    # every target row masked: p is the one-hot at 0. A draft of 0 is always
+    # accepted (p(0) = 1 >= u q(0)), any other draft with q > 0 always rejected,
+    # and the final token (residual or bonus) is 0 in both cases.
+    z = np.full(8, -np.inf, np.float32)
+    c0 = np.array([0.3, -1.0, 2.0, 0.1, -0.5, 1.2, 0.0, -2.0], np.float32)
+    rng = np.random.default_rng(3)
+    B = 200
+    seeds = rng.integers(0, 2**63, B, dtype=np.int64)
+    pos = rng.integers(0, 2**40, B)
+    draft = rng.integers(0, 8, B)
+    res = _verify_one_step(z, z, c0, draft, 1.0, seeds, pos)
+    n = res["num_accepted"]
+    assert np.array_equal(n, (draft == 0).astype(np.int32))
+    out = res["out_tokens"]
+    for b in range(B):
+        assert out[b, n[b]] == 0
+        assert not np.isnan(res["accept_margin"][b])
+
+
+def test_no_finite_draft_row_accepts_with_target_probability():
+    # a masked cache row makes q the one-hot at 0 (draft token 0): accept iff
+    # p(0) >= u, i.e. with probability p(0); a rejection resamples from
+    # max(0, p - q), which is p without column 0
+    t0 = np.array([0.5, 1.0, -0.5, 0.2, 1.5, -1.0, 0.0, 0.3], np.float32)
+    z = np.full(8, -np.inf, np.float32)
+    T = 1.0
+    B = 20000
+    rng = np.random.default_rng(4)
+    seeds = rng.integers(0, 2**63, B, dtype=np.int64)
+    res = _verify_one_step(t0, t0, z, np.zeros(B, np.int64), T, seeds, rng.integers(0, 2**40, B))
+    p = special.softmax(t0.astype(np.float64) / T)
+    acc = res["num_accepted"].mean()
+    assert abs(acc - p[0]) <= 5 * np.sqrt(p[0] * (1 - p[0]) / B)
+    first = res["out_tokens"][:, 0]
+    # overall the first emitted token still follows p
+    assert _chi2_ok(np.bincount(first, minlength=8), p)
+    rej = res["num_accepted"] == 0
+    assert np.all(first[rej] != 0)
+
+
+def test_no_finite_rows_on_both_sides():
+    # p and q both the one-hot at 0: the draft 0 is accepted; a bonus from the
+    # masked last row is 0 again
+    z = np.full(8, -np.inf, np.float32)
+    res = _verify_one_step(z, z, z, np.zeros(5, np.int64), 0.7, np.arange(5), np.arange(5) * 11)
+    assert np.all(res["num_accepted"] == 1)
+    assert np.all(res["out_tokens"] == 0)
