@@ -109,7 +109,8 @@ def cpu_baseline(wl, n_req: int, repeats: int = 2, lm=None, **draft_kw):
     dt = (time.perf_counter() - t0) / repeats
     if ctx is not None:
         ctx.unregister() if hasattr(ctx, "unregister") else None
-    return {"value": n_req * K / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+    return {"value": n_req * K / dt, "unit": "tokens/s", "cores": 1, "host_cpu_count": os.cpu_count(),
+            "blas_threads": 1, "kind": "oracle",
             "sample": f"{n_req} of the {wl.B} requests ({'LM head, ' if lm is not None else ''}all {K} draft steps "
                       f"+ verification), run {repeats} times, "
                       f"float64 NumPy, BLAS limited to 1 thread; {dt:.1f} s per run"}
@@ -281,12 +282,8 @@ def main():
     achieved = bytes_per_launch / (kern_avg_ms * 1e-3) / 1e9
     step_gbps = (draft_b + verify_b) / (ms * 1e-3) / 1e9
     acc_len = float((nacc.float() + 1).mean().item())
-    if n_launch == 1:
-        traffic = recorded_traffic("draft_resident_kernel_hbm_traffic_V200064_B32.md",
-                                   ("draft_resident.hip", "mds_device.h", "mds_internal.h"))
-    else:
-        traffic = recorded_traffic("draft_wave_kernel_hbm_traffic_V200064_B32.md",
-                                   ("draft_wave.hip", "mds_device.h", "mds_internal.h"))
+    traffic = recorded_traffic("draft_wave_kernel_hbm_traffic_V200064_B32.md",
+                               ("draft_wave.hip", "mds_device.h", "mds_internal.h"))
     if a.variant == "topk":
         traffic = recorded_traffic("topk_chunk_kernel_hbm_traffic_V200064_B32.md",
                                    ("draft_topk.hip", "mds_device.h", "mds_internal.h"))
@@ -326,7 +323,6 @@ def main():
                                 if a.variant == "topk" else
                                 "lm_head_kernel (draft LM head, bf16 MFMA, lm_head streamed once)"
                                 if a.variant == "lmhead" else
-                                "draft_resident_kernel (all K Markov steps, w2 held on chip)" if n_launch == 1 else
                                 "draft_wave_kernel (one Markov step, w2 streamed)"),
                      "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,

@@ -27,7 +27,12 @@
  *     word (the first 4 bytes of the workspace, see MDS_STATUS_*). The
  *     library never clears that word: the caller zeroes the workspace once
  *     when allocating it and reads the word after a synchronisation.
- *   - Logits must be finite or NaN; +-inf inputs are outside the contract.
+ *   - Logits (base, target, cache) are finite, -inf (a masked column) or NaN;
+ *     +inf is outside the contract (NaN in target rows too). A row with no
+ *     finite logit (all -inf) is a legal input: its winner is column 0 (the
+ *     first of equal maxima), and verification takes its distribution (p of
+ *     a target row, with top-p its kept set {0}; q of a draft cache row) to
+ *     be the one-hot at column 0.
  *   - Outputs must not alias inputs; the cache must not alias base or target.
  *   - Calls that share a workspace must be ordered (same stream).
  */
@@ -41,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MDS_ABI_VERSION 1
+#define MDS_ABI_VERSION 2
 
 /* return codes */
 #define MDS_OK 0
@@ -57,8 +62,7 @@ extern "C" {
 /* sticky status bits (workspace word 0) */
 #define MDS_STATUS_BAD_ANCHOR 1u      /* an anchor token was outside [0, V); token 0 was used */
 #define MDS_STATUS_BAD_DRAFT 2u       /* a draft token given to verification was outside [0, V); token 0 was used */
-#define MDS_STATUS_BARRIER_TIMEOUT 4u /* the resident draft kernel gave up waiting at a step barrier; the
-                                         draft outputs of that call are invalid */
+/* bit 4u is reserved (unused) */
 #define MDS_STATUS_BAD_INDEX 8u       /* an indexed call met a state slot >= n_slots or a cache row outside
                                          [0, n_cache_rows); that row was treated as padding */
 
@@ -106,7 +110,8 @@ int mds_verify_workspace_bytes(int B, int K, int V, int has_top_p, int has_draft
  *   B, K, V, r            batch, draft steps, vocabulary, Markov rank (host ints)
  *   base, base_dtype      base draft logits, MDS_F32 or MDS_BF16; element (b, k, v) at
  *                         b*base_req_stride + k*base_step_stride + v
- *   w1, w2                bf16 [V, r] row-major (row stride r), 4-byte aligned
+ *   w1, w2                bf16 [V, r] row-major (row stride r), 16-byte aligned
+ *                         (else MDS_ERR_INVALID_ARG)
  *   anchor_tokens         int32 [B]   previous token of step 0
  *   anchor_pos            int64 [B]   position P0 of the anchor token
  *   temperature           float [B]   > 0 sampled request, == 0 greedy request
@@ -126,15 +131,10 @@ int mds_verify_workspace_bytes(int B, int K, int V, int has_top_p, int has_draft
  *                         MDS_ERR_HIP, zero it again before the next call
  *   stream                hipStream_t as void*
  *
- * Kernels: when w2 fits in the chip's registers and LDS (V*r*2 bytes within
- * about 392 KiB per CU, r in {64, 128, 192, 256}) one persistent launch runs
- * all K steps with w2 read from memory once; it needs every CU of the device
- * free for the duration of the call (one work-group per CU, grid barriers
- * between steps with a bounded wait, see MDS_STATUS_BARRIER_TIMEOUT).
- * Otherwise one launch per step streams w2 each time. The environment
- * variable MDS_DRAFT_PATH selects: "stream" (the default) one streaming
- * launch per step, "auto" the resident kernel when w2 fits, "resident"
- * requires it (MDS_ERR_UNSUPPORTED if it does not fit).
+ * Kernels: one launch per step (each streams w2 once; rank <= 256 and larger
+ * ranks use different step kernels), then one launch that writes the tokens
+ * and draft_lse; a call with K*B > 4096 also clears its winner keys first.
+ * The kernel sequence depends only on the arguments, never on global state.
  */
 int mds_markov_draft_loop(int B, int K, int V, int r,
                           const void* base, int base_dtype, int64_t base_req_stride, int64_t base_step_stride,
@@ -183,9 +183,10 @@ int mds_markov_draft_loop(int B, int K, int V, int r,
  *   top_p                 float [B] or NULL (off); a value >= 1 turns it off for that request
  *   workspace             >= mds_verify_workspace_bytes(B, K, V, top_p != NULL,
  *                         draft_lse != NULL) bytes, 256-byte aligned, zero-filled
- *                         before its first use. Bytes [256, 256 + 512 KiB) hold one
- *                         arrival counter per request that every call leaves at
- *                         zero; the caller must not write the workspace between calls
+ *                         before its first use. Bytes [256, 256 + 1 MiB) hold one
+ *                         arrival counter and one winner key per request (see
+ *                         mds_verify_slot_offsets) that every call leaves at zero;
+ *                         the caller must not write the workspace between calls
  *                         (nor use the same memory as a draft-loop workspace).
  */
 int mds_rejection_verify(int B, int K, int V,
@@ -226,8 +227,7 @@ int mds_rejection_verify(int B, int K, int V,
  * z/T + g in float64; the winner is the first NaN, else the first maximum of
  * the float64 scores at a resolution of 2^-28 relative (candidates closer
  * than that go to the lower column); needs r <= 256.
- * Always runs the streaming kernels (MDS_DRAFT_PATH=resident returns
- * MDS_ERR_UNSUPPORTED). Workspace and errors as for mds_markov_draft_loop.
+ * Workspace and errors as for mds_markov_draft_loop.
  * ev_begin / ev_end (hipEvent_t as void*, or NULL) are recorded on `stream`
  * around the Markov step launches and *n_step_launches (if not NULL) gets
  * their count, as in mds_markov_draft_loop_timed.
@@ -345,8 +345,7 @@ int mds_rejection_verify_indexed(int B, int K, int V,
  * mds_markov_draft_loop_timed - mds_markov_draft_loop that also records
  * ev_begin just before the first and ev_end just after the last launch of the
  * Markov step kernel on `stream` (the init and finalize kernels stay outside),
- * and writes to *n_step_launches how many launches that span held: 1 when
- * the resident kernel ran all K steps, K for the streaming kernel.
+ * and writes to *n_step_launches how many launches that span held (K).
  * ev_begin, ev_end: hipEvent_t (as void*) created by the caller;
  * n_step_launches: host pointer, nullable.
  */
@@ -382,6 +381,16 @@ int mds_debug_noise(int n, const int32_t* cols, int64_t seed, int64_t pos_key, u
 int mds_debug_top_p(int rows, int V, const float* target, int64_t row_stride, const float* temperature,
                     const float* top_p, uint32_t* tau, int32_t* cut, float* log_z, int32_t* on,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mds_verify_slot_offsets - layout hook (pure host function, no GPU needed):
+ * byte offsets, from the start of a verification workspace, of request b's
+ * 32-bit arrival counter and of its 64-bit final-draw winner key, for
+ * 0 <= b < 65535 (else MDS_ERR_INVALID_ARG). Both lie in the fixed block
+ * [256, 256 + 1 MiB) whatever B, K or V a call uses; no two requests share a
+ * counter or a key, and no key overlaps a counter.
+ */
+int mds_verify_slot_offsets(int b, size_t* counter_offset, size_t* key_offset);
 
 /*
  * mds_debug_gumbel - test hook: the float32 Gumbel variate the kernels derive

@@ -17,13 +17,13 @@ import os
 
 __all__ = [
     "F32", "BF16", "MdsError", "library_path", "abi_version", "draft_workspace_bytes", "verify_workspace_bytes",
-    "new_workspace", "workspace_status", "markov_draft_loop", "markov_draft_loop_timed", "rejection_verify",
-    "debug_noise", "debug_gumbel", "debug_top_p", "STATUS_BAD_ANCHOR", "STATUS_BAD_DRAFT", "STATUS_BARRIER_TIMEOUT", "SALT_DRAFT", "SALT_ACCEPT",
+    "new_workspace", "workspace_status", "verify_slot_offsets", "markov_draft_loop", "markov_draft_loop_timed", "rejection_verify",
+    "debug_noise", "debug_gumbel", "debug_top_p", "STATUS_BAD_ANCHOR", "STATUS_BAD_DRAFT", "STATUS_BAD_INDEX", "SALT_DRAFT", "SALT_ACCEPT",
     "SALT_RESAMPLE",
 ]
 
 F32, BF16 = 0, 1
-STATUS_BAD_ANCHOR, STATUS_BAD_DRAFT, STATUS_BARRIER_TIMEOUT, STATUS_BAD_INDEX = 1, 2, 4, 8
+STATUS_BAD_ANCHOR, STATUS_BAD_DRAFT, STATUS_BAD_INDEX = 1, 2, 8
 SALT_DRAFT, SALT_ACCEPT, SALT_RESAMPLE = 1 << 30, 1, 2
 DRAFT_FP64_GUMBEL = 1
 
@@ -68,6 +68,7 @@ _SIGS = {
                                      _c_int),
     "mds_debug_noise": ([_c_int, _vp, _c_i64, _c_i64, ctypes.c_uint32, _vp, _vp, _vp], _c_int),
     "mds_debug_gumbel": ([_c_int, _vp, _vp, _vp], _c_int),
+    "mds_verify_slot_offsets": ([_c_int, ctypes.POINTER(_c_sz), ctypes.POINTER(_c_sz)], _c_int),
     "mds_debug_top_p": ([_c_int, _c_int, _vp, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp], _c_int),
 }
 
@@ -109,6 +110,14 @@ def verify_workspace_bytes(B: int, K: int, V: int, has_top_p: bool, has_draft_ls
     _check(_lib().mds_verify_workspace_bytes(B, K, V, int(has_top_p), int(has_draft_lse), ctypes.byref(out)),
            "verify_workspace_bytes")
     return out.value
+
+
+def verify_slot_offsets(b: int) -> tuple[int, int]:
+    """Byte offsets of request b's arrival counter and final-draw key in a
+    verification workspace (host only)."""
+    c, k = _c_sz(), _c_sz()
+    _check(_lib().mds_verify_slot_offsets(b, ctypes.byref(c), ctypes.byref(k)), "verify_slot_offsets")
+    return c.value, k.value
 
 
 def new_workspace(nbytes: int, device=None):
@@ -197,8 +206,8 @@ def markov_draft_loop(base, w1, w2, anchor_tokens, anchor_pos, temperature, seed
 def markov_draft_loop_timed(base, w1, w2, anchor_tokens, anchor_pos, temperature, seeds, cache, draft_tokens,
                             draft_lse, workspace, ev_begin, ev_end, stream=None) -> int:
     """markov_draft_loop recording ev_begin / ev_end (torch.cuda.Event with
-    timing) around the Markov step kernel launch(es); returns how many
-    launches that span held (1 resident kernel, or K streaming launches)."""
+    timing) around the Markov step kernel launches; returns how many
+    launches that span held (K)."""
     import torch
     args = _draft_args(base, w1, w2, anchor_tokens, anchor_pos, temperature, seeds, cache, draft_tokens, draft_lse,
                        workspace)

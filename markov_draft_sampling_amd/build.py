@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmds.so")
-SOURCES = ("abi.hip", "draft.hip", "draft_wave.hip", "draft_topk.hip", "lm_head.hip", "draft_resident.hip", "verify.hip", "topp.hip")
+SOURCES = ("abi.hip", "draft.hip", "draft_wave.hip", "draft_topk.hip", "lm_head.hip", "verify.hip", "topp.hip")
 ARCH = "gfx950"
 
 FLAGS = [

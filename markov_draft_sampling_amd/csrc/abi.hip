@@ -1,8 +1,6 @@
 // extern "C" entry points of libmds.so: argument validation on the host,
 // workspace layout, and the kernel sequence on the caller's stream. See
 // include/mds.h for the contract of each call.
-#include <cstdlib>
-#include <cstring>
 #include <string>
 
 #include "../../include/mds.h"
@@ -27,8 +25,11 @@ size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+constexpr int kMaxBatch = 65535;
+static_assert(kMaxBatch < mds::kVerifyMaxB, "the verify counter block must hold every request of a call");
+
 int check_sizes(int B, int K, int V) {
-  if (B < 1 || B > 65535) return fail(MDS_ERR_INVALID_ARG, "B must be in [1, 65535]");
+  if (B < 1 || B > kMaxBatch) return fail(MDS_ERR_INVALID_ARG, "B must be in [1, 65535]");
   if (K < 1 || K > 32) return fail(MDS_ERR_INVALID_ARG, "K must be in [1, 32]");
   if (V < 2 || V >= (1 << 24)) return fail(MDS_ERR_INVALID_ARG, "V must be in [2, 2^24)");
   return MDS_OK;
@@ -55,12 +56,12 @@ bool vec_ok(const void* p, int dtype, long long rs, long long ss) {
 
 // Draft workspace: [status | kFixedKeys winner keys, one per 128-byte line,
 // kept at zero between calls | the call's keys when K*B > kFixedKeys |
-// barrier words K+1 u32 | per-slab (max, sum exp) partials
-// K*B*kDraftMaxSlabs]. Sized without the device so the query needs no GPU.
+// per-slab (max, sum exp) partials K*B*kDraftMaxSlabs]. Sized without the
+// device so the query needs no GPU.
 struct DraftLayout {
   int nMT;
   bool fixed_keys;  // the keys sit in the zero-kept region
-  size_t keys, bar, qpart, total;
+  size_t keys, qpart, total;
 };
 
 size_t fixed_keys_bytes() { return up((size_t)mds::kFixedKeys * 8 * mds::kKeyStride); }
@@ -76,21 +77,9 @@ DraftLayout draft_layout(int B, int K, int V) {
     L.keys = o;
     o += up((size_t)K * B * 8 * mds::kKeyStride);
   }
-  L.bar = o;
-  L.qpart = L.bar + up((size_t)(K + 1) * 4);
+  L.qpart = o;
   L.total = L.qpart + up((size_t)K * B * mds::kDraftMaxSlabs * sizeof(float2));
   return L;
-}
-
-// Which draft kernel runs: MDS_DRAFT_PATH = "stream" (default) streams w2 at
-// every step; "resident" requires the persistent kernel that keeps w2 on chip;
-// "auto" uses the resident kernel when w2 fits.
-int draft_path_choice() {
-  const char* e = getenv("MDS_DRAFT_PATH");
-  if (!e || !*e || !strcmp(e, "stream")) return 1;
-  if (!strcmp(e, "auto")) return 0;
-  if (!strcmp(e, "resident")) return 2;
-  return -1;
 }
 
 struct VerifyLayout {
@@ -206,50 +195,30 @@ int draft_impl(int B, int K, int V, int r, const void* base, int base_dtype, int
   a.keys = (unsigned long long*)(ws + L.keys);
   a.qpart = (float2*)(ws + L.qpart);
   a.status = (uint32_t*)ws;
-  a.bar = (unsigned*)(ws + L.bar);
-  a.abort_flag = a.bar + K;
   a.idx_map = ix.idx_map;
   a.row_map = ix.idx_map ? ix.row_map : nullptr;
   a.sample_pos = (const long long*)ix.sample_pos;
   a.n_slots = ix.idx_map ? ix.n_slots : B;
   a.n_rows = n_rows;
   a.fp64 = fp64;
-  const int choice = draft_path_choice();
-  if (choice < 0) return fail(MDS_ERR_INVALID_ARG, "MDS_DRAFT_PATH must be auto, stream or resident");
-  const bool indexed = ix.idx_map || ix.sample_pos || fp64;
-  if (choice == 2 && indexed)
-    return fail(MDS_ERR_UNSUPPORTED, "the resident draft kernel takes neither request-state indexing nor fp64 noise");
-  int dev = 0, cus = 0, lds_max = 0;
+  int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
   if (e != hipSuccess) return hip_fail(e, "device query");
-  int n_lds = 0;
-  size_t res_lds = 0;
-  const bool resident = choice != 1 && !indexed && cus <= mds::kDraftMaxSlabs &&
-                        mds::draft_resident_plan(V, r, cus, (size_t)lds_max, &n_lds, &res_lds) == hipSuccess;
-  if (choice == 2 && !resident) return fail(MDS_ERR_UNSUPPORTED, "w2 does not fit on chip for the resident kernel");
-  const bool wave_kernel = !resident && r <= 256;
-  a.G = resident ? cus : (wave_kernel ? mds::draft_wave_slabs(V, cus) : mds::draft_slabs(V, cus));
-  a.n_lds_tiles = n_lds;
-  // keys in the zero-kept region need no clearing; the persistent kernel's
-  // barrier counters always do
-  if (!L.fixed_keys || resident) {
-    if ((e = mds::launch_draft_init(a.keys, K * B, a.bar, K + 1, st)) != hipSuccess)
-      return hip_fail(e, "draft init launch");
+  const bool wave_kernel = r <= 256;
+  a.G = wave_kernel ? mds::draft_wave_slabs(V, cus) : mds::draft_slabs(V, cus);
+  // keys in the zero-kept region need no clearing
+  if (!L.fixed_keys) {
+    if ((e = mds::launch_draft_init(a.keys, K * B, st)) != hipSuccess) return hip_fail(e, "draft init launch");
   }
   if (ev_begin && (e = hipEventRecord((hipEvent_t)ev_begin, st)) != hipSuccess) return hip_fail(e, "event record");
-  if (resident) {
-    if ((e = mds::launch_draft_resident(a, res_lds, st)) != hipSuccess) return hip_fail(e, "resident draft launch");
-  } else {
-    for (int k = 0; k < K; ++k) {
-      a.k = k;
-      e = wave_kernel ? mds::launch_draft_wave(a, st) : mds::launch_draft_step(a, st);
-      if (e != hipSuccess) return hip_fail(e, "draft step launch");
-    }
+  for (int k = 0; k < K; ++k) {
+    a.k = k;
+    e = wave_kernel ? mds::launch_draft_wave(a, st) : mds::launch_draft_step(a, st);
+    if (e != hipSuccess) return hip_fail(e, "draft step launch");
   }
   if (ev_end && (e = hipEventRecord((hipEvent_t)ev_end, st)) != hipSuccess) return hip_fail(e, "event record");
-  if (n_launches) *n_launches = resident ? 1 : K;
+  if (n_launches) *n_launches = K;
   mds::DraftFinalArgs f{B, K, a.G, a.keys, a.qpart, temperature, draft_tokens, draft_lse,
                         a.idx_map, a.row_map, a.n_slots, a.n_rows, a.fp64};
   if ((e = mds::launch_draft_finalize(f, st)) != hipSuccess) return hip_fail(e, "draft finalize launch");
@@ -647,6 +616,14 @@ int mds_debug_top_p(int rows, int V, const float* target, int64_t row_stride, co
   if ((e = mds::launch_top_p(a, st)) != hipSuccess) return hip_fail(e, "top-p launch");
   if ((e = mds::launch_debug_top_p_out(rows, a.topp, tau, cut, log_z, on, st)) != hipSuccess)
     return hip_fail(e, "top-p output launch");
+  return ok();
+}
+
+int mds_verify_slot_offsets(int b, size_t* counter_offset, size_t* key_offset) {
+  if (b < 0 || b >= kMaxBatch) return fail(MDS_ERR_INVALID_ARG, "b must be in [0, 65535)");
+  if (!counter_offset || !key_offset) return fail(MDS_ERR_INVALID_ARG, "a required pointer is NULL");
+  *counter_offset = mds::kVerifyCounterOffset + (size_t)mds::verify_counter_index(b) * 4;
+  *key_offset = mds::kVerifyCounterOffset + (size_t)mds::verify_key_index(b) * 8;
   return ok();
 }
 

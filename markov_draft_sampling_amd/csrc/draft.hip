@@ -395,10 +395,9 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftStepArgs a) {
   }
 }
 
-__global__ __launch_bounds__(256) void draft_init_kernel(unsigned long long* keys, int n, unsigned* bar, int nbar) {
+__global__ __launch_bounds__(256) void draft_init_kernel(unsigned long long* keys, int n) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < n) keys[(size_t)i * kKeyStride] = 0ull;
-  if (i < nbar) bar[i] = 0u;
 }
 
 // Draft tokens from the winner keys, and log-sum-exp of cache / T per row
@@ -473,9 +472,8 @@ int draft_nb(int B, int r) {
   return B <= 16 ? 16 : 32;
 }
 
-hipError_t launch_draft_init(unsigned long long* keys, int n, unsigned* bar, int nbar, hipStream_t st) {
-  const int m = n > nbar ? n : nbar;
-  hipLaunchKernelGGL(draft_init_kernel, dim3((m + 255) / 256), dim3(256), 0, st, keys, n, bar, nbar);
+hipError_t launch_draft_init(unsigned long long* keys, int n, hipStream_t st) {
+  hipLaunchKernelGGL(draft_init_kernel, dim3((n + 255) / 256), dim3(256), 0, st, keys, n);
   return hipGetLastError();
 }
 

@@ -40,9 +40,6 @@ struct DraftStepArgs {
   unsigned long long* keys;  // [K][B] winner keys at key_index(k, B, b)
   float2* qpart;             // [K][B][G] (max, sum exp) of cache / T per slab
   uint32_t* status;
-  unsigned* bar;             // [K] grid-barrier arrival counters (resident kernel)
-  unsigned* abort_flag;      // set when a barrier wait times out (resident kernel)
-  int n_lds_tiles;           // resident kernel: LDS tiles per work-group (max)
   int zero;                  // always 0 (an offset the compiler cannot fold)
   // request-state indexing (all null / B for the plain call)
   const int32_t* idx_map;    // [B][K] state slot of row b at step k, < 0 inert; null: slot = b
@@ -96,17 +93,12 @@ __device__ __forceinline__ long long draft_pos_key(const DraftStepArgs& a, int b
 int draft_nb(int B, int r);
 int draft_slabs(int V, int cus);
 int draft_wave_slabs(int V, int cus);
-hipError_t launch_draft_init(unsigned long long* keys, int n, unsigned* bar, int nbar, hipStream_t st);
+hipError_t launch_draft_init(unsigned long long* keys, int n, hipStream_t st);
 hipError_t launch_draft_step(const DraftStepArgs& a, hipStream_t st);
 // Wave-independent streaming step (rank <= 256); hipErrorNotSupported
 // (nothing launched) for a larger rank.
 size_t draft_wave_lds(int NB, int r);
 hipError_t launch_draft_wave(const DraftStepArgs& a, hipStream_t st);
-// Resident path: one launch runs all K steps with w2 held on chip. Returns
-// hipErrorNotSupported (and launches nothing) when w2 does not fit.
-hipError_t draft_resident_plan(int V, int r, int G, size_t lds_limit, int* n_lds_tiles, size_t* lds_bytes);
-hipError_t launch_draft_resident(const DraftStepArgs& a, size_t lds_bytes, hipStream_t st);
-constexpr uint32_t kStatusBarrierTimeout = 4u;
 hipError_t launch_draft_finalize(const DraftFinalArgs& a, hipStream_t st);
 
 // ------------------------------------------------- top-k Markov drafting --
@@ -186,17 +178,28 @@ struct ReqState {  // the accept decision of one request, read by the residual d
 };
 
 // The kVerifyCounterBytes after the verify workspace's 256-byte status block
-// hold one arrival counter per request. Every call leaves them at zero, so
-// they sit at a fixed offset whatever (B, K, V) a call uses. Requests
-// b and b + 2048k share a 256-byte line; any other two counters do not (many
-// work-groups bumping counters of one line serialise on it).
+// hold one arrival counter and one 64-bit winner key per request. Every call
+// leaves them at zero, so they sit at a fixed offset whatever (B, K, V) a
+// call uses. The block is 2048 lines of 512 bytes: request b uses line
+// b mod 2048, its counter is 32-bit word b / 2048 of the line's first 128
+// bytes, its key 64-bit word b / 2048 of bytes [128, 384). With b < 65536
+// (the largest batch a call accepts) b / 2048 < 32, so no key overlaps a
+// counter and nothing leaves the line. Requests b and b + 2048 i share a
+// line; any other two do not (many work-groups bumping counters of one line
+// serialise on it).
 constexpr size_t kVerifyCounterOffset = 256;
-constexpr size_t kVerifyCounterBytes = (size_t)2048 * 256;
-__host__ __device__ constexpr int verify_counter_index(int b) { return (b & 2047) * 64 + (b >> 11); }
-// The winner key of request b's final draw (64-bit) sits in the upper half of
-// the same 256-byte line as its counter: index in 64-bit words from the start
-// of the counter block.
-__host__ __device__ constexpr int verify_key_index(int b) { return (b & 2047) * 32 + 16 + (b >> 11); }
+constexpr int kVerifyLines = 2048;
+constexpr int kVerifyLineBytes = 512;
+constexpr size_t kVerifyCounterBytes = (size_t)kVerifyLines * kVerifyLineBytes;
+constexpr int kVerifyMaxB = kVerifyLines * 32;  // b / 2048 < 32
+// index in 32-bit words from the start of the block
+__host__ __device__ constexpr int verify_counter_index(int b) {
+  return (b & (kVerifyLines - 1)) * (kVerifyLineBytes / 4) + (b >> 11);
+}
+// index in 64-bit words from the start of the block
+__host__ __device__ constexpr int verify_key_index(int b) {
+  return (b & (kVerifyLines - 1)) * (kVerifyLineBytes / 8) + 16 + (b >> 11);
+}
 
 struct VerifyArgs {
   int B, K, V, NC;

@@ -32,6 +32,8 @@
 #include "mds_device.h"
 #include "mds_internal.h"
 
+#include <type_traits>
+
 namespace mds {
 
 namespace {
@@ -306,8 +308,12 @@ __device__ void decide(const VerifyArgs& a, int b, int sl, ReqLds& L) {
       const float tx = L.tx[k];
       float logp = -INFINITY;
       if (!a.topp || kept(a.topp[row], tx, x)) logp = div_t(tx, T, invT) - L.m[k] - L.lz[k];
-      const float p = expf(logp);
-      const float q = expf(div_t(L.cx[k], T, invT) - L.lq[k]);
+      float p = expf(logp);
+      float q = expf(div_t(L.cx[k], T, invT) - L.lq[k]);
+      // a row with no finite logit (max -inf) has the one-hot at column 0 as
+      // its distribution, the column the winner rule gives it
+      if (L.m[k] == -INFINITY) p = x == 0 ? 1.0f : 0.0f;
+      if (L.lq[k] == -INFINITY) q = x == 0 ? 1.0f : 0.0f;
       const unsigned long long sd = L.seed;
       const unsigned long long pk = (unsigned long long)(L.pos0 + k);
       const Philox4 w = philox4x32_10(0u, (uint32_t)pk, (uint32_t)(pk >> 32), kSaltAccept, (uint32_t)sd,
@@ -555,9 +561,15 @@ struct DrawCtx {
   float T, invT, M, LZ, LQ;
   TopP tp;
   uint32_t pk0, pk1, sk0, sk1;
+  bool p_onehot, q_onehot;  // target / draft row without a finite logit: one-hot at column 0
 };
 
 __device__ __forceinline__ float draw_logp(const DrawCtx& d, float t, int c) {
+  if (d.p_onehot) return c == 0 ? 0.0f : -INFINITY;
+  return kept(d.tp, t, c) ? div_t(t, d.T, d.invT) - d.M - d.LZ : -INFINITY;
+}
+// the same for rows known to hold a finite logit
+__device__ __forceinline__ float draw_logp_finite(const DrawCtx& d, float t, int c) {
   return kept(d.tp, t, c) ? div_t(t, d.T, d.invT) - d.M - d.LZ : -INFINITY;
 }
 
@@ -598,6 +610,8 @@ __global__ __launch_bounds__(kThreads) void residual_kernel(VerifyArgs a) {
   d.LZ = rq.LZ;
   d.LQ = rq.LQ;
   d.tp = rq.tp;
+  d.p_onehot = rq.M == -INFINITY;
+  d.q_onehot = rq.LQ == -INFINITY;
   const unsigned long long sd = (unsigned long long)a.seeds[sl];
   const unsigned long long pk = (unsigned long long)(a.anchor_pos[b] + j);
   d.pk0 = (uint32_t)pk;
@@ -665,31 +679,42 @@ __global__ __launch_bounds__(kThreads) void residual_kernel(VerifyArgs a) {
   // multiplied, strict: the lower column keeps a tie); its score then takes
   // the same float operations as in the bonus draw
   float rb = 0.0f, eb = 1.0f;
+  // DEG: the target or the draft row has no finite logit (a request-uniform
+  // case), so p or q is the one-hot at column 0
+  auto scan = [&](auto deg_tag) {
+    constexpr bool DEG = decltype(deg_tag)::value;
 #pragma unroll
-  for (int i = 0; i < kPer / 4; ++i) {
-    const int c = tc + i * 1024;
-    if (c >= V) break;
-    const Philox4 w = philox4x32_10((uint32_t)(c >> 2), d.pk0, d.pk1, kSaltResample, d.sk0, d.sk1);
-    const uint32_t wd[4] = {w.x0, w.x1, w.x2, w.x3};
+    for (int i = 0; i < kPer / 4; ++i) {
+      const int c = tc + i * 1024;
+      if (c >= V) break;
+      const Philox4 w = philox4x32_10((uint32_t)(c >> 2), d.pk0, d.pk1, kSaltResample, d.sk0, d.sk1);
+      const uint32_t wd[4] = {w.x0, w.x1, w.x2, w.x3};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (c + e < V) {
-        const float logp = draw_logp(d, tv[4 * i + e], c + e);
-        if (resid) {
-          const int q = 4 * i + e;
-          const float cq = CBF16 ? bf16_bits_to_f32((q & 1) ? (cw[q >> 1] >> 16) : (cw[q >> 1] & 0xFFFFu)) : cv[q];
-          const float rv = __expf(logp) - __expf(div_t(cq, d.T, d.invT) - d.LQ);
-          const float e2 = neg_log2_uniform(wd[e]);
-          const bool take = rv > 0.0f && (bi < 0 || rv * eb > rb * e2);
-          rb = take ? rv : rb;
-          eb = take ? e2 : eb;
-          bi = take ? c + e : bi;
-        } else {
-          win_update(bv, bi, logp + gumbel_from_word(wd[e]), c + e);
+      for (int e = 0; e < 4; ++e) {
+        if (c + e < V) {
+          const float logp = DEG ? draw_logp(d, tv[4 * i + e], c + e) : draw_logp_finite(d, tv[4 * i + e], c + e);
+          if (resid) {
+            const int q = 4 * i + e;
+            const float cq = CBF16 ? bf16_bits_to_f32((q & 1) ? (cw[q >> 1] >> 16) : (cw[q >> 1] & 0xFFFFu)) : cv[q];
+            float qv = __expf(div_t(cq, d.T, d.invT) - d.LQ);
+            if (DEG && d.q_onehot) qv = c + e == 0 ? 1.0f : 0.0f;
+            const float rv = __expf(logp) - qv;
+            const float e2 = neg_log2_uniform(wd[e]);
+            const bool take = rv > 0.0f && (bi < 0 || rv * eb > rb * e2);
+            rb = take ? rv : rb;
+            eb = take ? e2 : eb;
+            bi = take ? c + e : bi;
+          } else {
+            win_update(bv, bi, logp + gumbel_from_word(wd[e]), c + e);
+          }
         }
       }
     }
-  }
+  };
+  if (d.p_onehot || (resid && d.q_onehot))
+    scan(std::integral_constant<bool, true>());
+  else
+    scan(std::integral_constant<bool, false>());
   if (resid && bi >= 0) bv = fmaxf(__logf(rb), -0x1.fffffep+127f) + gumbel_from_e2(eb);
   const unsigned long long key = block_max_key(bi >= 0 ? win_key(bv, (uint32_t)bi) : 0ull);
   // waves 1..3 are done; wave 0 publishes and, if last, finishes the request

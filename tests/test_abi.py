@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_abi_version(lib):
     import markov_draft_sampling_amd as mds
-    assert mds.abi_version() == 1
+    assert mds.abi_version() == 2
 
 
 def test_workspace_queries_validate_sizes():
@@ -97,3 +97,31 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(mds, "library_path", lambda: str(tmp_path / "missing.so"))
     with pytest.raises(mds.MdsError, match="missing"):
         mds.abi_version()
+
+
+def test_verify_counter_block_layout():
+    # every request of the largest batch has its own counter and its own key
+    # in the fixed block, and no key overlaps any counter
+    import numpy as np
+    import markov_draft_sampling_amd as mds
+    n = 65535
+    cnt = np.empty(n, np.int64)
+    key = np.empty(n, np.int64)
+    for b in range(n):
+        cnt[b], key[b] = mds.verify_slot_offsets(b)
+    lo, hi = 256, 256 + (1 << 20)
+    assert cnt.min() >= lo and cnt.max() + 4 <= hi and key.min() >= lo and key.max() + 8 <= hi
+    assert np.all(cnt % 4 == 0) and np.all(key % 8 == 0)
+    assert np.unique(cnt).size == n and np.unique(key).size == n
+    cover = np.zeros(hi, np.int8)
+    for off in range(4):
+        cover[cnt + off] += 1
+    for off in range(8):
+        cover[key + off] += 1
+    assert cover.max() == 1  # no byte belongs to two words
+    # requests b and b + 2048 i share a 512-byte line; no other two do
+    line = (cnt - lo) // 512
+    assert np.array_equal(line, (key - lo) // 512)
+    assert np.array_equal(line, np.arange(n) % 2048)
+    with pytest.raises(mds.MdsError, match="invalid argument"):
+        mds.verify_slot_offsets(65535)

@@ -15,12 +15,6 @@ from parity import Report, cache_to_numpy, compare_draft, full_parity
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(params=["auto", "stream"], autouse=True)
-def draft_path(request, monkeypatch):
-    monkeypatch.setenv("MDS_DRAFT_PATH", request.param)
-    return request.param
-
-
 def _ok(rep: Report):
     assert rep.ok(), rep.notes[:5]
 
@@ -77,3 +71,33 @@ def test_lm_head_single_row():
     ref, absd = oracle.draft_logits(hidden, lm, want_abs=True)
     err = np.abs(out.cpu().numpy().reshape(1, 37).astype(np.float64) - ref)
     assert (err <= 256 * 2.0 ** -24 * absd + 2.0 ** -24 * np.abs(ref)).all()
+
+
+@pytest.mark.parametrize("top_p", [None, 0.9])
+def test_rows_without_a_finite_logit(top_p):
+    # masked rows (every column -inf): a draft base row gives token 0 and a
+    # draft distribution q that is the one-hot at 0; a target row gives p
+    # (and its top-p kept set) the one-hot at 0; checked against the oracle
+    V, K, B = 3000, 3, 6
+    wl = workloads.make_custom(V, 64, K, B, seed=5, temperature=0.9, top_p=top_p)
+    wl.base[1, 0, :] = -np.inf
+    wl.base[2, 1, :] = -np.inf
+    wl.base[5, :, :] = -np.inf
+    tgt = wl.target.reshape(B, K + 1, V)
+    tgt[3, 0, :] = -np.inf
+    tgt[4, :, :] = -np.inf
+    tgt[2, 1, :] = -np.inf
+    tgt[5, :, :] = -np.inf
+    rep = full_parity(wl)
+    _ok(rep)
+    from parity import run_gpu
+    d = run_gpu(wl)
+    toks = d["draft_tokens"].cpu().numpy()
+    out = d["out_tokens"].cpu().numpy()
+    nacc = d["num_accepted"].cpu().numpy()
+    assert toks[1, 0] == 0 and toks[2, 1] == 0 and np.all(toks[5] == 0)
+    # request 5: p and q both one-hot at 0 and every draft 0, so all accepted
+    # and the bonus from the masked last row is 0
+    assert nacc[5] == K and np.all(out[5] == 0)
+    # request 4: every target row masked, so the emitted token is always 0
+    assert out[4, nacc[4]] == 0

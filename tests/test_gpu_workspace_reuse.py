@@ -1,6 +1,6 @@
 """Back-to-back draft calls of different shapes on one workspace (the
 workspace layout depends on B and K, so one call's partials can land where
-the next call keeps its winner keys and barrier counters): each call matches
+the next call keeps its winner keys): each call matches
 the oracle, and repeating a call repeats its tokens exactly."""
 from __future__ import annotations
 
@@ -11,12 +11,6 @@ import workloads
 from parity import Report, cache_to_numpy, compare_draft, dev_tensors
 
 pytestmark = pytest.mark.gpu
-
-
-@pytest.fixture(params=["stream", "auto"])
-def draft_path(request, monkeypatch):
-    monkeypatch.setenv("MDS_DRAFT_PATH", request.param)
-    return request.param
 
 
 def _draft(wl, ws):
@@ -30,7 +24,7 @@ def _draft(wl, ws):
     return d["draft_tokens"].cpu().numpy(), cache_to_numpy(d["cache"], wl.cache_dtype), d["draft_lse"].cpu().numpy()
 
 
-def test_calls_on_one_workspace(draft_path):
+def test_calls_on_one_workspace():
     import torch
     import markov_draft_sampling_amd as mds
     wa = workloads.make_workload("boosted_v32000", B=8)
