@@ -383,6 +383,33 @@ int mds_debug_top_p(int rows, int V, const float* target, int64_t row_stride, co
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mds_markov_draft_loop_noalloc - mds_markov_draft_loop without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * loop's scratch (winner keys and per-slab partials) lives in a fixed
+ * 8.5 MiB + 256 B array inside the library, one copy per device, held until
+ * the process ends. The call allocates nothing and launches the same kernels
+ * as mds_markov_draft_loop (plus, on its first call on a device, one clearing
+ * launch), so its outputs are identical.
+ *   K * B must be <= 1024 (else MDS_ERR_UNSUPPORTED, nothing enqueued).
+ *   status   device uint32 (written): the sticky status word that the plain
+ *            call keeps in its workspace (MDS_STATUS_* bits are OR-ed in);
+ *            the caller zeroes it and reads it after a synchronisation.
+ * Every call on one device shares that device's array and leaves its winner
+ * keys at zero: calls that may overlap on one device (different streams
+ * without ordering, or concurrent host threads' work on unordered streams)
+ * race on it and must be serialised by the caller. Other arguments, limits
+ * and errors as for mds_markov_draft_loop.
+ */
+int mds_markov_draft_loop_noalloc(int B, int K, int V, int r,
+                                  const void* base, int base_dtype, int64_t base_req_stride, int64_t base_step_stride,
+                                  const void* w1, const void* w2,
+                                  const int32_t* anchor_tokens, const int64_t* anchor_pos,
+                                  const float* temperature, const int64_t* seeds,
+                                  void* cache, int cache_dtype, int64_t cache_req_stride, int64_t cache_step_stride,
+                                  int32_t* draft_tokens, float* draft_lse, uint32_t* status, void* stream);
+
+/*
  * mds_verify_slot_offsets - layout hook (pure host function, no GPU needed):
  * byte offsets, from the start of a verification workspace, of request b's
  * 32-bit arrival counter and of its 64-bit final-draw winner key, for

@@ -17,7 +17,7 @@ import os
 
 __all__ = [
     "F32", "BF16", "MdsError", "library_path", "abi_version", "draft_workspace_bytes", "verify_workspace_bytes",
-    "new_workspace", "workspace_status", "verify_slot_offsets", "markov_draft_loop", "markov_draft_loop_timed", "rejection_verify",
+    "new_workspace", "workspace_status", "verify_slot_offsets", "markov_draft_loop", "markov_draft_loop_noalloc", "markov_draft_loop_timed", "rejection_verify",
     "debug_noise", "debug_gumbel", "debug_top_p", "STATUS_BAD_ANCHOR", "STATUS_BAD_DRAFT", "STATUS_BAD_INDEX", "SALT_DRAFT", "SALT_ACCEPT",
     "SALT_RESAMPLE",
 ]
@@ -69,6 +69,8 @@ _SIGS = {
     "mds_debug_noise": ([_c_int, _vp, _c_i64, _c_i64, ctypes.c_uint32, _vp, _vp, _vp], _c_int),
     "mds_debug_gumbel": ([_c_int, _vp, _vp, _vp], _c_int),
     "mds_verify_slot_offsets": ([_c_int, ctypes.POINTER(_c_sz), ctypes.POINTER(_c_sz)], _c_int),
+    "mds_markov_draft_loop_noalloc": ([_c_int] * 4 + [_vp, _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                      _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp], _c_int),
     "mds_debug_top_p": ([_c_int, _c_int, _vp, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp], _c_int),
 }
 
@@ -179,12 +181,14 @@ def _draft_args(base, w1, w2, anchor_tokens, anchor_pos, temperature, seeds, cac
     if draft_lse is not None:
         _need(draft_lse.dtype == torch.float32 and draft_lse.is_contiguous() and draft_lse.numel() == B * K,
               "draft_lse must be float32 [B, K]")
-    _need(workspace.dtype == torch.uint8 and workspace.is_contiguous(), "workspace must be a contiguous uint8 tensor")
+    if workspace is not None:
+        _need(workspace.dtype == torch.uint8 and workspace.is_contiguous(),
+              "workspace must be a contiguous uint8 tensor")
     r = w1.shape[1]
     return (B, K, V, r, _ptr(base), _dtype_code(base), base.stride(0), base.stride(1), _ptr(w1), _ptr(w2),
             _ptr(anchor_tokens), _ptr(anchor_pos), _ptr(temperature), _ptr(seeds), _ptr(cache), _dtype_code(cache),
             cache.stride(0), cache.stride(1), _ptr(draft_tokens), _ptr(draft_lse), _ptr(workspace),
-            workspace.numel())
+            0 if workspace is None else workspace.numel())
 
 
 def markov_draft_loop(base, w1, w2, anchor_tokens, anchor_pos, temperature, seeds, cache, draft_tokens,
@@ -201,6 +205,19 @@ def markov_draft_loop(base, w1, w2, anchor_tokens, anchor_pos, temperature, seed
                        workspace)
     _check(_lib().mds_markov_draft_loop(*args, _stream(stream, base.device)), "markov_draft_loop")
     return workspace
+
+
+def markov_draft_loop_noalloc(base, w1, w2, anchor_tokens, anchor_pos, temperature, seeds, cache, draft_tokens,
+                              draft_lse, status, stream=None) -> None:
+    """markov_draft_loop whose scratch lives inside the library (no workspace;
+    K * B <= 1024). status: int32/uint32 device tensor of one element, the
+    sticky status word (zeroed by the caller)."""
+    _need(status.numel() == 1 and status.element_size() == 4 and status.is_cuda, "status: one 4-byte device word")
+    args = _draft_args(base, w1, w2, anchor_tokens, anchor_pos, temperature, seeds, cache, draft_tokens, draft_lse,
+                       None)
+    # _draft_args ends with (workspace ptr, workspace bytes): replaced by the status word
+    _check(_lib().mds_markov_draft_loop_noalloc(*args[:-2], _vp(status.data_ptr()), _stream(stream, base.device)),
+           "markov_draft_loop_noalloc")
 
 
 def markov_draft_loop_timed(base, w1, w2, anchor_tokens, anchor_pos, temperature, seeds, cache, draft_tokens,

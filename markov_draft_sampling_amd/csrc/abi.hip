@@ -1,6 +1,7 @@
 // extern "C" entry points of libmds.so: argument validation on the host,
 // workspace layout, and the kernel sequence on the caller's stream. See
 // include/mds.h for the contract of each call.
+#include <mutex>
 #include <string>
 
 #include "../../include/mds.h"
@@ -150,7 +151,8 @@ int draft_impl(int B, int K, int V, int r, const void* base, int base_dtype, int
                const void* w1, const void* w2, const int32_t* anchor, const int64_t* anchor_pos,
                const float* temperature, const int64_t* seeds, void* cache, int cache_dtype, int64_t cache_rs,
                int64_t cache_ss, int32_t* draft_tokens, float* draft_lse, void* workspace, size_t ws_bytes,
-               void* stream, void* ev_begin, void* ev_end, int* n_launches, const Indexing& ix = Indexing()) {
+               void* stream, void* ev_begin, void* ev_end, int* n_launches, const Indexing& ix = Indexing(),
+               uint32_t* status = nullptr) {
   int rc;
   if ((rc = check_sizes(B, K, V)) || (rc = check_rank(r)) || (rc = check_indexing(ix))) return rc;
   if (!base || !w1 || !w2 || !anchor || (!anchor_pos && !ix.sample_pos) || !temperature || !seeds || !cache ||
@@ -194,7 +196,7 @@ int draft_impl(int B, int K, int V, int r, const void* base, int base_dtype, int
   a.cache_ss = cache_ss;
   a.keys = (unsigned long long*)(ws + L.keys);
   a.qpart = (float2*)(ws + L.qpart);
-  a.status = (uint32_t*)ws;
+  a.status = status ? status : (uint32_t*)ws;
   a.idx_map = ix.idx_map;
   a.row_map = ix.idx_map ? ix.row_map : nullptr;
   a.sample_pos = (const long long*)ix.sample_pos;
@@ -376,6 +378,26 @@ int topk_impl(int B, int K, int V, int r, int topk, const void* base, int base_d
   if ((e = mds::launch_topk_chain(a, st)) != hipSuccess) return hip_fail(e, "top-k chain launch");
   return ok();
 }
+
+// ------------------------------------------------ allocation-free draft call --
+// mds_markov_draft_loop_noalloc keeps its workspace in this array instead of
+// a caller's buffer: status block | the zero-kept winner-key region | per-slab
+// partials of at most kNoAllocMaxRows (request, step) rows. Every device the
+// library runs on holds its own copy until the process ends. In host code
+// `scratch` names a host-side stand-in: its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+constexpr int kNoAllocMaxRows = 1024;  // K * B
+constexpr size_t kNoAllocScratchBytes =
+    kAlign + (size_t)mds::kFixedKeys * 8 * mds::kKeyStride + (size_t)kNoAllocMaxRows * mds::kDraftMaxSlabs * 8;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct ScratchState {
+  unsigned char* ptr = nullptr;  // device address of this device's scratch
+  bool keys_zero = false;        // its winner-key region is known to be zero
+};
+std::mutex g_scratch_mu;
+ScratchState g_scratch[kMaxDevices];
 
 }  // namespace
 
@@ -617,6 +639,41 @@ int mds_debug_top_p(int rows, int V, const float* target, int64_t row_stride, co
   if ((e = mds::launch_debug_top_p_out(rows, a.topp, tau, cut, log_z, on, st)) != hipSuccess)
     return hip_fail(e, "top-p output launch");
   return ok();
+}
+
+int mds_markov_draft_loop_noalloc(int B, int K, int V, int r, const void* base, int base_dtype,
+                                  int64_t base_req_stride, int64_t base_step_stride, const void* w1, const void* w2,
+                                  const int32_t* anchor_tokens, const int64_t* anchor_pos, const float* temperature,
+                                  const int64_t* seeds, void* cache, int cache_dtype, int64_t cache_req_stride,
+                                  int64_t cache_step_stride, int32_t* draft_tokens, float* draft_lse,
+                                  uint32_t* status, void* stream) {
+  int rc;
+  if ((rc = check_sizes(B, K, V))) return rc;
+  if ((long long)K * B > kNoAllocMaxRows)
+    return fail(MDS_ERR_UNSUPPORTED, "mds_markov_draft_loop_noalloc needs K * B <= 1024 (its scratch is fixed)");
+  if (!status) return fail(MDS_ERR_INVALID_ARG, "status is NULL");
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "device query");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MDS_ERR_UNSUPPORTED, "device index beyond 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ScratchState& S = g_scratch[dev];
+  if (!S.ptr) {
+    void* p = nullptr;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return hip_fail(e, "scratch address");
+    S.ptr = (unsigned char*)p;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  if (!S.keys_zero) {  // first call on this device, or a launch failed since the region was last known zero
+    if ((e = mds::launch_draft_init((unsigned long long*)(S.ptr + kAlign), mds::kFixedKeys, st)) != hipSuccess)
+      return hip_fail(e, "scratch clear launch");
+    S.keys_zero = true;
+  }
+  rc = draft_impl(B, K, V, r, base, base_dtype, base_req_stride, base_step_stride, w1, w2, anchor_tokens, anchor_pos,
+                  temperature, seeds, cache, cache_dtype, cache_req_stride, cache_step_stride, draft_tokens, draft_lse,
+                  S.ptr, kNoAllocScratchBytes, stream, nullptr, nullptr, nullptr, Indexing(), status);
+  if (rc == MDS_ERR_HIP) S.keys_zero = false;  // launched steps may have left winner keys behind
+  return rc;
 }
 
 int mds_verify_slot_offsets(int b, size_t* counter_offset, size_t* key_offset) {
