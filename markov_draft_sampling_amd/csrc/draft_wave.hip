@@ -10,8 +10,10 @@
 //     (v_mfma_f32_16x16x32_bf16, lane l: row l % 16, rank elements
 //     8 (l / 16) + 32 s of slice s), and the next tile's rows and base logits
 //     are in flight while the current tile is computed;
-//   * the embeddings of the batch tile (the B operand) sit in LDS for the
-//     whole launch;
+//   * the embeddings of the batch tile (the B operand) are read once: into
+//     LDS by the work-group, or, on the fast path, by each wave straight into
+//     registers (previous tokens, then embedding rows, then the first tiles,
+//     so that this dependent chain has no other load queued ahead of it);
 //   * the epilogue runs in the accumulator layout: lane l owns request
 //     16 nt + l % 16 and the 4 consecutive columns 4 (l / 16) .. + 3 of the
 //     tile, so base loads and cache stores are 16-byte vector accesses.
@@ -163,41 +165,9 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
     }
   };
 
-  // the first tile's loads go out before the previous tokens and the
-  // embedding gather, whose latency they then overlap
   const int t_first = mt_begin + wave;
   u32x4 A[kRKMax], An[kRKMax];
   float bz[NT][4], bzn[NT][4];
-  if (t_first < mt_end) {
-    load_a(t_first, A);
-    load_base(t_first, bz);
-  }
-
-  // previous token of every request of the tile
-  const int cpr = r >> 3;  // 16-byte chunks per embedding row
-  for (int i = tid; i < NB; i += 256) {
-    const int b = b0 + i;
-    int prev = -1;  // rows that are not served get a zero embedding
-    if (draft_slot(a, b) >= 0) {
-      // the previous step's winner (key 0, i.e. -1, when that step was inert)
-      long long tk = (k == 0) ? (long long)a.anchor[b] : (long long)key_col(a.keys[key_index(k - 1, a.B, b)], F64);
-      if (tk < 0 || tk >= V) {
-        set_status(a.status, kStatusBadAnchor);
-        tk = 0;
-      }
-      prev = (int)tk;
-    }
-    s_prev[i] = prev;
-  }
-  __syncthreads();
-  // Markov embeddings w1[prev] -> LDS
-  for (int i = tid; i < NB * cpr; i += 256) {
-    const int row = i / cpr, ch = i - row * cpr;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (s_prev[row] >= 0) v = *(const u32x4*)(a.w1 + (size_t)s_prev[row] * r + ch * 8);
-    *(u32x4*)(s_e + row * rs + ch * 8) = v;
-  }
-  __syncthreads();
 
   // Running winner and q statistics per served request. The winner starts
   // at the lane's first column (value -inf), so a later column replaces it
@@ -226,6 +196,7 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
   bool all_valid = true;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) all_valid &= valid[nt];
+  // the same value in every wave of the work-group (the waves serve the same requests)
   const bool fast_req = a.vec_cache && __all(all_sampled && all_valid);
   const bool t1 = __all(all_t1);
 
@@ -237,6 +208,23 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
   // the general loop below.
   int t_gen = t_first;
   if (FL && fast_req && a.vec_base) {
+    // Direct path. Each wave reads the previous tokens of its lanes' requests
+    // and their embedding rows straight into MFMA B operands (request
+    // 16 nt + lr, rank elements 8 lg + 32 s of slice s): the tokens first,
+    // then the rows, then the first tiles. Loads complete in issue order, so
+    // nothing is queued ahead of this two-load chain, and no work-group
+    // barrier waits for it.
+    int pv[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int b = b0 + nt * 16 + lr;  // served (fast_req)
+      long long tk = (k == 0) ? (long long)a.anchor[b] : (long long)key_col(a.keys[key_index(k - 1, a.B, b)], F64);
+      if (tk < 0 || tk >= V) {
+        set_status(a.status, kStatusBadAnchor);
+        tk = 0;
+      }
+      pv[nt] = (int)tk;
+    }
     const int full_end = mt_end < V / 16 ? mt_end : V / 16;  // tiles [mt_begin, full_end) lie inside V
     // the embedding operands are the same for every tile: read once, kept in
     // registers for the whole loop (one wave per SIMD leaves room)
@@ -245,7 +233,8 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int s = 0; s < kRKMax; ++s)
-        Er[nt][s] = *(const bf16x8*)(s_e + (nt * 16 + lr) * rs + (s < RK ? s : 0) * 32 + lg * 8);
+        Er[nt][s] = *(const bf16x8*)(a.w1 + (size_t)pv[nt] * r + (s < RK ? s : 0) * 32 + lg * 8);
+    asm volatile("" ::: "memory");  // the tile loads stay behind the embedding loads
     // One full tile of the fast loop: bias by MFMA from the ring entry's w2
     // rows, then the branch-free epilogue. `live` is 1 for every tile the
     // loop computes; the accumulation of q statistics multiplies by it.
@@ -338,13 +327,7 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
         u32x4 Ar[kRing][kRKMax];
         float bzr[kRing][NT][4];
 #pragma unroll
-        for (int s = 0; s < kRKMax; ++s) Ar[0][s] = A[s];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) bzr[0][nt][i] = bz[nt][i];
-#pragma unroll
-        for (int e = 1; e < kRing; ++e) {
+        for (int e = 0; e < kRing; ++e) {
           const int te = t + 4 * e <= t_lastf ? t + 4 * e : t_lastf;  // past the last tile: that tile again (cache hits)
           load(te, Ar[e]);
           load_base_vec(te, bzr[e]);
@@ -373,10 +356,52 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
       t_gen = t1 ? run_fast(True(), True()) : run_fast(False(), True());
     else
       t_gen = t1 ? run_fast(True(), False()) : run_fast(False(), False());
-    if (t_gen < mt_end) {  // the partial last tile: its operands again, for the general loop
+    if (V & 15) {  // some work-group has a partial last tile: the general loop reads the embeddings from LDS
+      if (wave == 0) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int s = 0; s < kRKMax; ++s)
+            if (s < RK) *(bf16x8*)(s_e + (nt * 16 + lr) * rs + s * 32 + lg * 8) = Er[nt][s];
+      }
+      __syncthreads();
+    }
+    if (t_gen < mt_end) {  // the partial last tile, for the general loop
       load_a(t_gen, A);
       load_base(t_gen, bz);
     }
+  } else {
+    // the first tile's loads go out before the previous tokens and the
+    // embedding gather, whose latency they then overlap
+    if (t_first < mt_end) {
+      load_a(t_first, A);
+      load_base(t_first, bz);
+    }
+    // previous token of every request of the tile
+    const int cpr = r >> 3;  // 16-byte chunks per embedding row
+    for (int i = tid; i < NB; i += 256) {
+      const int b = b0 + i;
+      int prev = -1;  // rows that are not served get a zero embedding
+      if (draft_slot(a, b) >= 0) {
+        // the previous step's winner (key 0, i.e. -1, when that step was inert)
+        long long tk = (k == 0) ? (long long)a.anchor[b] : (long long)key_col(a.keys[key_index(k - 1, a.B, b)], F64);
+        if (tk < 0 || tk >= V) {
+          set_status(a.status, kStatusBadAnchor);
+          tk = 0;
+        }
+        prev = (int)tk;
+      }
+      s_prev[i] = prev;
+    }
+    __syncthreads();
+    // Markov embeddings w1[prev] -> LDS
+    for (int i = tid; i < NB * cpr; i += 256) {
+      const int row = i / cpr, ch = i - row * cpr;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (s_prev[row] >= 0) v = *(const u32x4*)(a.w1 + (size_t)s_prev[row] * r + ch * 8);
+      *(u32x4*)(s_e + row * rs + ch * 8) = v;
+    }
+    __syncthreads();
   }
 
   // the wave's last tile: the prefetch past it requests that tile again
