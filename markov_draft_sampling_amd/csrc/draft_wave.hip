@@ -185,19 +185,18 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
     qs[nt] = 0.0f;
     qnan[nt] = false;
   }
-  // Fast epilogue for full tiles when every request of the batch tile exists
-  // and samples (T > 0), with vector cache stores; T == 1 skips the division.
+  // Fast epilogue for full tiles when every served request of the batch tile
+  // samples (T > 0), with vector cache stores (none for the rows that are not
+  // served: padding past the batch, or inert at this step); T == 1 skips the
+  // division.
   bool all_sampled = true, all_t1 = true;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    all_sampled &= Tv[nt] > 0.0f;
-    all_t1 &= Tv[nt] == 1.0f;
+    all_sampled &= !valid[nt] || Tv[nt] > 0.0f;
+    all_t1 &= !valid[nt] || Tv[nt] == 1.0f;
   }
-  bool all_valid = true;
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) all_valid &= valid[nt];
   // the same value in every wave of the work-group (the waves serve the same requests)
-  const bool fast_req = a.vec_cache && __all(all_sampled && all_valid);
+  const bool fast_req = a.vec_cache && __all(all_sampled);
   const bool t1 = __all(all_t1);
 
   // Fast loop: the full tiles of a work-group whose requests all exist and
@@ -217,13 +216,16 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
     int pv[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const int b = b0 + nt * 16 + lr;  // served (fast_req)
-      long long tk = (k == 0) ? (long long)a.anchor[b] : (long long)key_col(a.keys[key_index(k - 1, a.B, b)], F64);
+      // rows that are not served read a request's token (an address inside
+      // the arrays) and keep a zero token without a status bit
+      const int b = b0 + nt * 16 + lr;
+      const int bb = b < a.B ? b : a.B - 1;
+      long long tk = (k == 0) ? (long long)a.anchor[bb] : (long long)key_col(a.keys[key_index(k - 1, a.B, bb)], F64);
       if (tk < 0 || tk >= V) {
-        set_status(a.status, kStatusBadAnchor);
+        if (valid[nt]) set_status(a.status, kStatusBadAnchor);
         tk = 0;
       }
-      pv[nt] = (int)tk;
+      pv[nt] = valid[nt] ? (int)tk : 0;
     }
     const int full_end = mt_end < V / 16 ? mt_end : V / 16;  // tiles [mt_begin, full_end) lie inside V
     // the embedding operands are the same for every tile: read once, kept in
@@ -238,9 +240,12 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
     // One full tile of the fast loop: bias by MFMA from the ring entry's w2
     // rows, then the branch-free epilogue. `live` is 1 for every tile the
     // loop computes; the accumulation of q statistics multiplies by it.
-    auto fast_tile = [&](auto t1_tag, auto full_tag, int t, const u32x4 (&Ab)[kRKMax], const float (&bzb)[NT][4]) {
+    // MASK: some row of the batch tile is not served (its cache stores are skipped)
+    auto fast_tile = [&](auto t1_tag, auto full_tag, auto mask_tag, int t, const u32x4 (&Ab)[kRKMax],
+                         const float (&bzb)[NT][4]) {
       constexpr bool T1 = decltype(t1_tag)::value;
       constexpr bool FULL = decltype(full_tag)::value;
+      constexpr bool MASK = decltype(mask_tag)::value;
       floatx4 acc[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -268,11 +273,11 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
           u32x2 w;
           w.x = h[0] | (h[1] << 16);
           w.y = h[2] | (h[3] << 16);
-          *(u32x2*)((uint16_t*)a.cache + rcache[nt] + c) = w;
+          if (!MASK || valid[nt]) *(u32x2*)((uint16_t*)a.cache + rcache[nt] + c) = w;
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i) cv[i] = z[i];
-          *(f32x4*)((float*)a.cache + rcache[nt] + c) = f32x4{z[0], z[1], z[2], z[3]};
+          if (!MASK || valid[nt]) *(f32x4*)((float*)a.cache + rcache[nt] + c) = f32x4{z[0], z[1], z[2], z[3]};
         }
         const Philox4 w = philox4x32_10((uint32_t)(c >> 2), pk0[nt], pk1[nt], kSaltDraft, sk0[nt], sk1[nt]);
         const uint32_t wd[4] = {w.x0, w.x1, w.x2, w.x3};
@@ -311,7 +316,7 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
     // to arrive. The loop is unrolled over the ring (no register copies,
     // which would wait for the loads) and runs whole turns only; the last
     // partial turn computes the entries already loaded.
-    auto run_fast = [&](auto t1_tag, auto full_tag) {
+    auto run_fast = [&](auto t1_tag, auto full_tag, auto mask_tag) {
       constexpr bool FULL = decltype(full_tag)::value;
       auto load = [&](int tt, u32x4 (&Ab)[kRKMax]) {
         if (FULL)
@@ -335,7 +340,7 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
         for (int turn = 0; turn < n_turns; ++turn) {
 #pragma unroll
           for (int e = 0; e < kRing; ++e) {
-            fast_tile(t1_tag, full_tag, t + 4 * e, Ar[e], bzr[e]);
+            fast_tile(t1_tag, full_tag, mask_tag, t + 4 * e, Ar[e], bzr[e]);
             const int tn = t + 4 * (e + kRing) <= t_lastf ? t + 4 * (e + kRing) : t_lastf;
             load(tn, Ar[e]);
             load_base_vec(tn, bzr[e]);
@@ -345,17 +350,22 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
         const int rest = n_tiles - n_turns * kRing;
 #pragma unroll
         for (int e = 0; e < kRing - 1; ++e)
-          if (e < rest) fast_tile(t1_tag, full_tag, t + 4 * e, Ar[e], bzr[e]);
+          if (e < rest) fast_tile(t1_tag, full_tag, mask_tag, t + 4 * e, Ar[e], bzr[e]);
         t += 4 * rest;
       }
       return t;
     };
     using True = std::integral_constant<bool, true>;
     using False = std::integral_constant<bool, false>;
-    if (RK == kRKMax)
-      t_gen = t1 ? run_fast(True(), True()) : run_fast(False(), True());
+    bool all_valid = true;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) all_valid &= valid[nt];
+    if (!__all(all_valid))  // padding rows (small batches): one general instance (the division by T = 1 is exact)
+      t_gen = run_fast(False(), False(), True());
+    else if (RK == kRKMax)
+      t_gen = t1 ? run_fast(True(), True(), False()) : run_fast(False(), True(), False());
     else
-      t_gen = t1 ? run_fast(True(), False()) : run_fast(False(), False());
+      t_gen = t1 ? run_fast(True(), False(), False()) : run_fast(False(), False(), False());
     if (V & 15) {  // some work-group has a partial last tile: the general loop reads the embeddings from LDS
       if (wave == 0) {
 #pragma unroll
@@ -448,11 +458,11 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
           u32x2 w;
           w.x = h[0] | (h[1] << 16);
           w.y = h[2] | (h[3] << 16);
-          *(u32x2*)((uint16_t*)a.cache + rcache[nt] + c) = w;
+          if (valid[nt]) *(u32x2*)((uint16_t*)a.cache + rcache[nt] + c) = w;
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i) cv[i] = z[i];
-          *(f32x4*)((float*)a.cache + rcache[nt] + c) = f32x4{z[0], z[1], z[2], z[3]};
+          if (valid[nt]) *(f32x4*)((float*)a.cache + rcache[nt] + c) = f32x4{z[0], z[1], z[2], z[3]};
         }
         const Philox4 w = philox4x32_10((uint32_t)(c >> 2), pk0[nt], pk1[nt], kSaltDraft, sk0[nt], sk1[nt]);
         const uint32_t wd[4] = {w.x0, w.x1, w.x2, w.x3};
