@@ -4,11 +4,11 @@
 // kernels over 8192-column statistics blocks whose partials per-request
 // kernels combine, plus residual-mass and resample kernels. Here, without
 // top-p, three launches do the whole pass:
-//   stats_kernel<false>  one work-group per (row, kStatsChunk-column block)
-//                    streams the target rows (and the draft cache rows when
-//                    the draft loop gave no log-normalisers): (max, sum exp)
-//                    of logit / T for sampled requests, the winner key of
-//                    the raw logits for greedy ones (PR #63554, Notes: greedy
+//   stats_wave_kernel  one wave per (row, kStatsChunk-column block) streams
+//                    the target rows (and the draft cache rows when the draft
+//                    loop gave no log-normalisers): (max, sum exp) of
+//                    logit / T for sampled requests, the winner key of the
+//                    raw logits for greedy ones (PR #63554, Notes: greedy
 //                    verification compares with the target argmax and never
 //                    reads the draft cache), one plain partial store per
 //                    block;
@@ -19,7 +19,7 @@
 //                    residual max(0, p - q) of the first rejected row, or
 //                    from p for the bonus token; the last one of a request
 //                    writes the output tokens.
-// With top-p, stats_kernel<true>'s last-arriving work-group per request
+// With top-p, stats_count_kernel's last-arriving work-group per request
 // combines, top_p_kernel (topp.hip) finds the kept sets, decide_kernel runs
 // the accept tests, then the residual pass.
 //
@@ -418,13 +418,11 @@ __device__ void combine_request(const VerifyArgs& a, int b, int sl, ReqLds& L, u
   if (a.decide) decide(a, b, sl, L);
 }
 
-// Grid (NC, rows) with rows = B(K+1) target rows, then B*K cache rows when
-// draft_lse is null; rows are split over y and z (y at most 32768).
-// LAST: the request's last-arriving work-group combines (and decides);
-// otherwise the partials are plain stores and combine_kernel follows, which
-// keeps the combining code, and its registers, out of this streaming pass.
-template <bool LAST>
-__global__ __launch_bounds__(kThreads) void stats_kernel(VerifyArgs a) {
+// The counting statistics pass (top-p path): one work-group per (row,
+// block); grid (NC, rows) with rows = B(K+1) target rows, then B*K cache
+// rows when draft_lse is null, split over y and z (y at most 32768). The
+// request's last-arriving work-group combines.
+__global__ __launch_bounds__(kThreads) void stats_count_kernel(VerifyArgs a) {
   const int chunk = blockIdx.x;
   const int row = (int)blockIdx.z * (int)gridDim.y + (int)blockIdx.y;
   const int K = a.K, V = a.V, NC = a.NC;
@@ -472,21 +470,6 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(VerifyArgs a) {
   // waves 1..3 are done; wave 0 publishes and, if it is the request's last
   // arrival, combines
   if (threadIdx.x >= 64) return;
-  if (!LAST) {
-    if (threadIdx.x == 0) {
-      if (slot) *slot = word;
-      // block 0 of target row k < K of a sampled request also records the
-      // target and cache logits at draft token k, for the accept test
-      const int k = row - b * (K + 1);
-      if (is_target && chunk == 0 && k < K && sl >= 0 && a.temp[sl] > 0.0f) {
-        int x;
-        float tx, cx;
-        draft_point(a, b, sl, k, x, tx, cx);
-        a.tq[b * K + k] = pack_ms(tx, cx);
-      }
-    }
-    return;
-  }
   __shared__ ReqLds L;
   __shared__ unsigned long long stage[kStage];
   int last = 0;
@@ -512,6 +495,140 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(VerifyArgs a) {
   last = __shfl(last, 0);
   if (!last) return;
   combine_request(a, b, sl, L, stage, true);
+}
+
+// ---- statistics without arrival counting: one wave per (row, block) ----
+constexpr int kWavePer = kStatsChunk / 64;  // values per lane: columns c0 + 256 i + 4 lane + e
+
+// The lane's kWavePer values of one block; when the whole block exists and
+// vector access is allowed (a wave-uniform test) every load is issued before
+// any value is used.
+template <bool BF16>
+__device__ __forceinline__ void load_wave_block(const void* rowp, int V, int c0, bool vec, float (&v)[kWavePer]) {
+  const int tc = c0 + (int)(threadIdx.x & 63) * 4;
+  if (vec && c0 + kStatsChunk <= V) {
+#pragma unroll
+    for (int i = 0; i < kWavePer / 4; ++i) {
+      if (BF16) {
+        const u32x2 w = __builtin_nontemporal_load((const u32x2*)((const uint16_t*)rowp + tc + i * 256));
+        v[4 * i + 0] = bf16_bits_to_f32(w.x & 0xFFFFu);
+        v[4 * i + 1] = bf16_bits_to_f32(w.x >> 16);
+        v[4 * i + 2] = bf16_bits_to_f32(w.y & 0xFFFFu);
+        v[4 * i + 3] = bf16_bits_to_f32(w.y >> 16);
+      } else {
+        const f32x4 w = __builtin_nontemporal_load((const f32x4*)((const float*)rowp + tc + i * 256));
+        v[4 * i + 0] = w.x;
+        v[4 * i + 1] = w.y;
+        v[4 * i + 2] = w.z;
+        v[4 * i + 3] = w.w;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kWavePer / 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = tc + i * 256 + e;
+        v[4 * i + e] = c < V ? load_f32_or_bf16(rowp, c, BF16) : 0.0f;
+      }
+  }
+}
+
+// (max, sum exp) of x = v / T of the whole block in every lane of the wave:
+// the lane's own pair, then the wave maximum, each lane's sum rescaled to it
+// once, and a wave sum. A NaN anywhere makes the sum NaN.
+__device__ __forceinline__ void wave_block_stats(float (&v)[kWavePer], int c0, int V, float T, float invT, float& M,
+                                                 float& S) {
+  const int tc = c0 + (int)(threadIdx.x & 63) * 4;
+  float m = -INFINITY, s = 0.0f;
+  bool has_nan = false;
+#pragma unroll
+  for (int j = 0; j < kWavePer; ++j) {
+    const bool valid = tc + (j >> 2) * 256 + (j & 3) < V;
+    const float x = valid ? div_t(v[j], T, invT) : -INFINITY;
+    has_nan |= x != x;
+    v[j] = (x == x) ? x : -INFINITY;
+    m = fmaxf(m, v[j]);
+  }
+  if (m != -INFINITY) {
+#pragma unroll
+    for (int j = 0; j < kWavePer; ++j) s += fast_exp(v[j] - m);
+  }
+  M = wave_max_f32(m);
+  float sc = m == -INFINITY ? 0.0f : s * fast_exp(m - M);
+  if (has_nan) sc = NAN;
+  S = wave_sum_f32(sc);
+}
+
+// winner key of the raw values over the block, in every lane
+__device__ __forceinline__ unsigned long long wave_block_key(const float (&v)[kWavePer], int c0, int V) {
+  const int tc = c0 + (int)(threadIdx.x & 63) * 4;
+  float bv = -INFINITY;
+  int bi = -1;
+#pragma unroll
+  for (int j = 0; j < kWavePer; ++j) {
+    const int c = tc + (j >> 2) * 256 + (j & 3);  // increasing in j
+    if (c < V) win_update(bv, bi, v[j], c);
+  }
+  return wave_max_u64(bi >= 0 ? win_key(bv, (uint32_t)bi) : 0ull);
+}
+
+// Grid (ceil(NC / 4), rows): wave w of work-group x takes block 4 x + w of
+// the row; rows = B(K+1) target rows, then B*K cache rows when draft_lse is
+// null (split over y and z, y at most 32768). One plain store per block;
+// combine_kernel follows.
+__global__ __launch_bounds__(kThreads) void stats_wave_kernel(VerifyArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int chunk = (int)blockIdx.x * 4 + wave;
+  const int row = (int)blockIdx.z * (int)gridDim.y + (int)blockIdx.y;
+  const int K = a.K, V = a.V, NC = a.NC;
+  const int n_t = a.B * (K + 1);
+  const int n_rows = n_t + (a.qpart ? a.B * K : 0);
+  if (row >= n_rows || chunk >= NC) return;
+  const bool is_target = row < n_t;
+  const int b = is_target ? row / (K + 1) : (row - n_t) / K;
+  const int sl = verify_slot(a, b);
+  if (sl < 0) return;  // padding request: combine_kernel reads nothing of it
+  const int c0 = chunk * kStatsChunk;
+  float v[kWavePer];
+  if (is_target) {
+    // the row's loads go out first: nothing about them depends on T
+    load_wave_block<false>(a.target + (long long)row * a.target_rs, V, c0, a.vec_target != 0, v);
+    asm volatile("" ::: "memory");
+    const float T = a.temp[sl];
+    unsigned long long word;
+    if (!(T > 0.0f)) {
+      word = wave_block_key(v, c0, V);
+    } else {
+      float m, s;
+      wave_block_stats(v, c0, V, T, 1.0f / T, m, s);
+      word = pack_ms(m, s);
+    }
+    if (lane == 0) {
+      a.tpart[(size_t)chunk * n_t + row] = word;
+      // block 0 of target row k < K of a sampled request also records the
+      // target and cache logits at draft token k, for the accept test
+      const int k = row - b * (K + 1);
+      if (chunk == 0 && k < K && T > 0.0f) {
+        int x;
+        float tx, cx;
+        draft_point(a, b, sl, k, x, tx, cx);
+        a.tq[b * K + k] = pack_ms(tx, cx);
+      }
+    }
+  } else {
+    const float T = a.temp[sl];
+    if (!(T > 0.0f)) return;  // greedy requests never read the cache
+    const int q = row - n_t, k = q - b * K;
+    const long long off = (long long)verify_cache_row(a, b, sl) * a.cache_rs + (long long)k * a.cache_ss;
+    if (a.cache_bf16)
+      load_wave_block<true>((const uint16_t*)a.cache + off, V, c0, a.vec_cache != 0, v);
+    else
+      load_wave_block<false>((const float*)a.cache + off, V, c0, a.vec_cache != 0, v);
+    float m, s;
+    wave_block_stats(v, c0, V, T, 1.0f / T, m, s);
+    if (lane == 0) a.qpart[(size_t)chunk * ((size_t)a.B * K) + q] = pack_ms(m, s);
+  }
 }
 
 // After a statistics pass without arrival counting: one wave per request.
@@ -779,9 +896,9 @@ hipError_t launch_verify_stats(const VerifyArgs& a, bool last_arrival, hipStream
   const int gy = rows < 32768 ? rows : 32768;
   const int gz = (rows + gy - 1) / gy;
   if (last_arrival)
-    hipLaunchKernelGGL(stats_kernel<true>, dim3(a.NC, gy, gz), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(stats_count_kernel, dim3(a.NC, gy, gz), dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL(stats_kernel<false>, dim3(a.NC, gy, gz), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(stats_wave_kernel, dim3((a.NC + 3) / 4, gy, gz), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
