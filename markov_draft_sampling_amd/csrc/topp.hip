@@ -10,9 +10,14 @@
 //     (w <= 1, so a row of < 2^24 columns sums below 2^64); the target mass
 //     is TQ = ceil(p * sum Q) (at least 1, so the maximum is always kept);
 //   * the order key is ord(logit) (monotone in the logit), the id breaks ties;
-//   * the bin that holds the crossing is narrowed over the 32-bit key in
-//     levels of 12, 12 and 8 bits with LDS histograms of (mass, count), one
-//     pass over the row per level;
+//   * first the columns are binned by how far x lies below the row maximum
+//     M (known from the statistics pass), 1/128 of a logit unit per bin:
+//     the bins are monotone in the logit and spread the columns evenly, so
+//     their LDS histogram of (mass, count) takes few colliding atomics, and
+//     every column with zero quantised mass falls into one last bin that is
+//     never counted; when the crossing bin holds too many columns (dense
+//     ties) the crossing is instead narrowed over the 32-bit key in levels of
+//     12, 12 and 8 bits, one pass over the row per level;
 //   * as soon as the crossing bin holds at most kCap columns they are gathered
 //     into LDS, sorted by (key desc, id asc) and prefix-summed exactly;
 //   * if a single key value holds more than kCap columns (ties), all of them
@@ -28,6 +33,15 @@ namespace {
 
 constexpr int kTp = 1024;
 constexpr int kCap = 4096;
+constexpr int kNB0 = 4096;             // bins below the row maximum
+constexpr float kBinScale = 128.0f;    // bins per unit of x
+
+// bin of x below the maximum M: floor((M - x) * 128), 4095 for x at least
+// 32 below M (exp(-32) < 2^-40: quantised mass 0), -inf and NaN
+__device__ __forceinline__ int max_bin(float x, float M) {
+  const float f = (M - x) * kBinScale;  // >= 0: M is the maximum of the same x
+  return f < (float)(kNB0 - 1) ? (f > 0.0f ? (int)f : 0) : kNB0 - 1;
+}
 
 __device__ __forceinline__ unsigned long long quantise(float w) {
   return (unsigned long long)(w * 1099511627776.0f);  // floor(w * 2^40), w in [0, 1]
@@ -115,79 +129,139 @@ __global__ __launch_bounds__(kTp) void top_p_kernel(VerifyArgs a) {
   }
   RowCtx rc{a.target + (long long)row * a.target_rs, a.V, a.vec_target != 0, T, 1.0f / T, s_M};
 
-  // narrowing levels: (shift, width) of the digit below the fixed prefix
-  const int shifts[3] = {20, 8, 0};
-  const int widths[3] = {12, 12, 8};
-  unsigned int prefix = 0;
-  int pbits = 0;
-  unsigned long long above = 0;  // mass of all columns ordered before the current bin
-  unsigned int cnt = 0;
-  for (int lvl = 0; lvl < 3; ++lvl) {
-    const int nb = 1 << widths[lvl], sh = shifts[lvl];
-    for (int i = tid; i < nb; i += kTp) {
-      h_mass[i] = 0;
-      h_cnt[i] = 0;
-    }
-    __syncthreads();
+  // total quantised mass and the histogram of the bins below the maximum
+  for (int i = tid; i < kNB0; i += kTp) {
+    h_mass[i] = 0;
+    h_cnt[i] = 0;
+  }
+  __syncthreads();
+  {
     unsigned long long sumq = 0;
-    const unsigned int pf = prefix;
-    const int pb = pbits;
     for_row(rc, [&](int, float t) {
-      const uint32_t o = ord_f32(t);
-      if (pb && (o >> (32 - pb)) != pf) return;
       const float x = div_t(t, rc.T, rc.invT);
       const unsigned long long q = quantise(fast_exp(x - rc.M));
-      const unsigned int d = (o >> sh) & (nb - 1);
-      atomicAdd(&h_mass[d], q);
-      atomicAdd(&h_cnt[d], 1u);
+      const int d = max_bin(x, rc.M);
+      if (d < kNB0 - 1) {  // the last bin holds mass 0 only: never the crossing
+        if (q) atomicAdd(&h_mass[d], q);
+        atomicAdd(&h_cnt[d], 1u);
+      }
       sumq += q;
     });
-    if (lvl == 0) {
-      unsigned long long tot;
-      block_excl_scan(sumq, scratch, &tot);
-      if (tid == 0) {
-        s_sumq = tot;
-        unsigned long long tq = (unsigned long long)ceil((double)p * (double)tot);
-        if (tq < 1) tq = 1;
-        if (tq > tot) tq = tot;
-        s_tq = tq;
-      }
-    }
-    __syncthreads();
-    // crossing bin, scanning digits from the top
+    unsigned long long tot;
+    block_excl_scan(sumq, scratch, &tot);
     if (tid == 0) {
-      s_digit = 0;
+      s_sumq = tot;
+      unsigned long long tq = (unsigned long long)ceil((double)p * (double)tot);
+      if (tq < 1) tq = 1;
+      if (tq > tot) tq = tot;
+      s_tq = tq;
+      s_digit = kNB0;
       s_cnt = 0;
-      s_above = above;
+      s_above = 0;
     }
     __syncthreads();
+    // crossing bin, in ascending bin (descending logit) order
     unsigned long long loc = 0;
-    const int d0 = nb - 1 - tid * 4;
-    for (int j = 0; j < 4; ++j)
-      if (d0 - j >= 0) loc += h_mass[d0 - j];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) loc += h_mass[tid * 4 + j];
     const unsigned long long ex = block_excl_scan(loc, scratch, nullptr);
-    {
-      const unsigned long long need = s_tq - above;
-      unsigned long long run = ex;
-      for (int j = 0; j < 4; ++j) {
-        const int d = d0 - j;
-        if (d < 0) break;
-        const unsigned long long mass = h_mass[d];
-        if (run < need && need <= run + mass) {
-          s_digit = (unsigned int)d;
-          s_above = above + run;
-          s_cnt = h_cnt[d];
-        }
-        run += mass;
+    const unsigned long long need = s_tq;
+    unsigned long long run = ex;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d = tid * 4 + j;
+      const unsigned long long mass = h_mass[d];
+      if (run < need && need <= run + mass) {
+        s_digit = (unsigned int)d;
+        s_above = run;
+        s_cnt = h_cnt[d];
       }
+      run += mass;
     }
     __syncthreads();
-    prefix = (prefix << widths[lvl]) | s_digit;
-    pbits += widths[lvl];
-    above = s_above;
-    cnt = s_cnt;
-    __syncthreads();
-    if (cnt <= (unsigned int)kCap) break;
+  }
+  const int bin0 = (int)s_digit;  // kNB0 if no bin crossed (cannot happen for finite rows)
+  unsigned long long above = s_above;
+  unsigned int cnt = s_cnt;
+  // filter of the crossing bin's columns for the gather below: the bin below
+  // the maximum, or (after narrowing) the key prefix
+  bool by_bin = bin0 < kNB0 && cnt <= (unsigned int)kCap;
+  unsigned int prefix = 0;
+  int pbits = 0;
+  if (!by_bin) {
+    above = 0;
+    cnt = 0;
+    // narrowing levels: (shift, width) of the digit below the fixed prefix
+    const int shifts[3] = {20, 8, 0};
+    const int widths[3] = {12, 12, 8};
+    for (int lvl = 0; lvl < 3; ++lvl) {
+      const int nb = 1 << widths[lvl], sh = shifts[lvl];
+      for (int i = tid; i < nb; i += kTp) {
+        h_mass[i] = 0;
+        h_cnt[i] = 0;
+      }
+      __syncthreads();
+      unsigned long long sumq = 0;
+      const unsigned int pf = prefix;
+      const int pb = pbits;
+      for_row(rc, [&](int, float t) {
+        const uint32_t o = ord_f32(t);
+        if (pb && (o >> (32 - pb)) != pf) return;
+        const float x = div_t(t, rc.T, rc.invT);
+        const unsigned long long q = quantise(fast_exp(x - rc.M));
+        const unsigned int d = (o >> sh) & (nb - 1);
+        atomicAdd(&h_mass[d], q);
+        atomicAdd(&h_cnt[d], 1u);
+        sumq += q;
+      });
+      if (lvl == 0) {
+        unsigned long long tot;
+        block_excl_scan(sumq, scratch, &tot);
+        if (tid == 0) {
+          s_sumq = tot;
+          unsigned long long tq = (unsigned long long)ceil((double)p * (double)tot);
+          if (tq < 1) tq = 1;
+          if (tq > tot) tq = tot;
+          s_tq = tq;
+        }
+      }
+      __syncthreads();
+      // crossing bin, scanning digits from the top
+      if (tid == 0) {
+        s_digit = 0;
+        s_cnt = 0;
+        s_above = above;
+      }
+      __syncthreads();
+      unsigned long long loc = 0;
+      const int d0 = nb - 1 - tid * 4;
+      for (int j = 0; j < 4; ++j)
+        if (d0 - j >= 0) loc += h_mass[d0 - j];
+      const unsigned long long ex = block_excl_scan(loc, scratch, nullptr);
+      {
+        const unsigned long long need = s_tq - above;
+        unsigned long long run = ex;
+        for (int j = 0; j < 4; ++j) {
+          const int d = d0 - j;
+          if (d < 0) break;
+          const unsigned long long mass = h_mass[d];
+          if (run < need && need <= run + mass) {
+            s_digit = (unsigned int)d;
+            s_above = above + run;
+            s_cnt = h_cnt[d];
+          }
+          run += mass;
+        }
+      }
+      __syncthreads();
+      prefix = (prefix << widths[lvl]) | s_digit;
+      pbits += widths[lvl];
+      above = s_above;
+      cnt = s_cnt;
+      __syncthreads();
+      if (cnt <= (unsigned int)kCap) break;
+    }
+
   }
 
   const unsigned long long tq = s_tq;
@@ -202,8 +276,8 @@ __global__ __launch_bounds__(kTp) void top_p_kernel(VerifyArgs a) {
     const int pb = pbits;
     for_row(rc, [&](int c, float t) {
       const uint32_t o = ord_f32(t);
-      if ((o >> (32 - pb)) != pf) return;
       const float x = div_t(t, rc.T, rc.invT);
+      if (by_bin ? max_bin(x, rc.M) != bin0 : (o >> (32 - pb)) != pf) return;
       const unsigned int slot = atomicAdd(&s_ncand, 1u);
       if (slot < (unsigned int)kCap) {
         c_key[slot] = ((unsigned long long)o << 32) | (uint32_t)(~(uint32_t)c);
