@@ -37,11 +37,18 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "draft+verify tokens/s at V=200k,K=7,B=32; HBM GB/s % of MI355X peak"
 
 
-def algorithmic_bytes(B, K, V, r, s_base=4, s_cache=4, s_tgt=4):
-    """Bytes the method must move per step (each w2 byte once per Markov step)."""
+def algorithmic_bytes(B, K, V, r, s_base=4, s_cache=4, s_tgt=4, top_p=False):
+    """Bytes the method must move per step (each w2 byte once per Markov step).
+
+    Verification reads every target row once for its statistics and one
+    target and one cache row per request for the final draw; with top-p the
+    kept set needs one more pass over the target rows (its threshold is not
+    known until the statistics are)."""
     draft_step = V * r * 2 + B * V * (s_base + s_cache)
     draft = K * draft_step
     verify = B * (K + 1) * V * s_tgt + B * V * (s_tgt + s_cache)
+    if top_p:
+        verify += B * (K + 1) * V * s_tgt
     return draft_step, draft, verify
 
 
@@ -121,7 +128,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--batch", type=int, default=32)
+    ap.add_argument("--batch", type=int, default=None, help="requests (default: the workload's own batch)")
+    ap.add_argument("--workload", default="headline_v200064",
+                    choices=("headline_v200064", "zipf_top_p_v151936", "boosted_v32000", "odd_vocab_v50017",
+                             "tiny_v4096"),
+                    help="seeded synthetic workload (the headline one by default; zipf_top_p_v151936 has bf16 base "
+                         "logits and cache and top-p 0.95 on the target)")
     ap.add_argument("--cpu-sample", type=int, default=32, help="requests the CPU oracle baseline runs on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="do not flush caches between timed steps")
@@ -148,27 +160,33 @@ def main():
     assert torch.cuda.is_available(), "no GPU"
     dev = torch.device("cuda:0")
     t_gen = time.perf_counter()
-    wl = workloads.make_workload("headline_v200064", B=a.batch)
+    wl = workloads.make_workload(a.workload, B=a.batch)
     B, K, V, r = wl.B, wl.K, wl.V, wl.r
-    print(f"# workload V={V} r={r} K={K} B={B} generated in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr,
-          flush=True)
+    if a.variant != "plain" and (a.workload != "headline_v200064" or wl.base_dtype != "f32"):
+        print("the variants run on the headline workload only", file=sys.stderr)
+        sys.exit(2)
+    print(f"# workload {a.workload} V={V} r={r} K={K} B={B} generated in {time.perf_counter() - t_gen:.1f}s",
+          file=sys.stderr, flush=True)
 
-    base = torch.from_numpy(wl.base).to(dev)  # [B, K+1, V]; the draft reads rows 0..K-1
+    bf16_of = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    # [B, K+1, V]; the draft reads rows 0..K-1
+    base = bf16_of(wl.base) if wl.base_dtype == "bf16" else torch.from_numpy(wl.base).to(dev)
     target = torch.from_numpy(wl.target).to(dev)
+    top_p = None if wl.top_p is None else torch.from_numpy(wl.top_p).to(dev)
     w1 = torch.from_numpy(wl.w1.view(np.int16)).view(torch.bfloat16).to(dev)
     w2 = torch.from_numpy(wl.w2.view(np.int16)).view(torch.bfloat16).to(dev)
     anchor = torch.from_numpy(wl.anchor_tokens).to(dev)
     apos = torch.from_numpy(wl.anchor_pos).to(dev)
     temp = torch.from_numpy(wl.temperature).to(dev)
     seeds = torch.from_numpy(wl.seeds).to(dev)
-    cache = torch.empty((B, K, V), dtype=torch.float32, device=dev)
+    cache = torch.empty((B, K, V), dtype=torch.bfloat16 if wl.cache_dtype == "bf16" else torch.float32, device=dev)
     toks = torch.empty((B, K), dtype=torch.int32, device=dev)
     lse = torch.empty((B, K), dtype=torch.float32, device=dev)
     out = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
     nacc = torch.empty((B,), dtype=torch.int32, device=dev)
     ws_d = mds.new_workspace(mds.draft_topk_workspace_bytes(B, K, V, r, a.topk) if a.variant == "topk" else
                              mds.draft_workspace_bytes(B, K, V, r), dev)
-    ws_v = mds.new_workspace(mds.verify_workspace_bytes(B, K, V, False, True), dev)
+    ws_v = mds.new_workspace(mds.verify_workspace_bytes(B, K, V, top_p is not None, True), dev)
     flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)  # 512 MiB, read to evict caches
     stream = torch.cuda.current_stream(dev)
     if a.variant == "lmhead":
@@ -200,7 +218,8 @@ def main():
             if events is not None:
                 launches.append(1)
             mds.markov_draft_loop(base, w1, w2, anchor, apos, temp, seeds, cache, toks, lse, workspace=ws_d)
-            mds.rejection_verify(target, cache, toks, temp, seeds, apos, out, nacc, draft_lse=lse, workspace=ws_v)
+            mds.rejection_verify(target, cache, toks, temp, seeds, apos, out, nacc, draft_lse=lse,
+                                 top_p=top_p, workspace=ws_v)
             return
         if a.variant == "plain":
             if events is None:
@@ -208,14 +227,16 @@ def main():
             else:
                 launches.append(mds.markov_draft_loop_timed(base, w1, w2, anchor, apos, temp, seeds, cache, toks, lse,
                                                             ws_d, events[0], events[1]))
-            mds.rejection_verify(target, cache, toks, temp, seeds, apos, out, nacc, draft_lse=lse, workspace=ws_v)
+            mds.rejection_verify(target, cache, toks, temp, seeds, apos, out, nacc, draft_lse=lse,
+                                 top_p=top_p, workspace=ws_v)
             return
         if a.variant == "topk":
             mds.markov_draft_loop_topk(base, w1, w2, anchor, None, spos, temp, seeds, cache, toks, a.topk,
                                        draft_lse=lse, workspace=ws_d, events=events)
             if events is not None:
                 launches.append(1)
-            mds.rejection_verify(target, cache, toks, temp, seeds, apos, out, nacc, draft_lse=lse, workspace=ws_v)
+            mds.rejection_verify(target, cache, toks, temp, seeds, apos, out, nacc, draft_lse=lse,
+                                 top_p=top_p, workspace=ws_v)
             return
         ix = a.variant == "indexed"
         r_ = mds.markov_draft_loop_ex(base, w1, w2, anchor, idx_bk if ix else None, spos, s_temp if ix else temp,
@@ -225,9 +246,10 @@ def main():
             launches.append(r_[1])
         if ix:
             mds.rejection_verify_indexed(target, cache, toks, idx_b, s_temp, s_seed, apos, out, nacc,
-                                         row_mapping=rmap, draft_lse=lse, workspace=ws_v)
+                                         row_mapping=rmap, draft_lse=lse, top_p=top_p, workspace=ws_v)
         else:
-            mds.rejection_verify(target, cache, toks, temp, seeds, apos, out, nacc, draft_lse=lse, workspace=ws_v)
+            mds.rejection_verify(target, cache, toks, temp, seeds, apos, out, nacc, draft_lse=lse,
+                                 top_p=top_p, workspace=ws_v)
 
     for _ in range(a.warmup):
         step()
@@ -271,7 +293,9 @@ def main():
 
     ms = float(np.mean(step_ms))
     tokens = B * K
-    draft_step_b, draft_b, verify_b = algorithmic_bytes(B, K, V, r)
+    s_b = 2 if wl.base_dtype == "bf16" else 4
+    s_c = 2 if wl.cache_dtype == "bf16" else 4
+    draft_step_b, draft_b, verify_b = algorithmic_bytes(B, K, V, r, s_base=s_b, s_cache=s_c, top_p=top_p is not None)
     kern_avg_ms = float(np.mean(draft_span_ms)) / n_launch
     bytes_per_launch = draft_b / n_launch
     if a.variant == "topk":
@@ -290,8 +314,8 @@ def main():
     if a.variant == "lmhead":
         traffic = recorded_traffic("lm_head_kernel_hbm_traffic_V200064_B32.md",
                                    ("lm_head.hip", "mds_device.h", "mds_internal.h"))
-    if (B != 32 or a.variant not in ("plain", "topk", "lmhead") or (a.variant == "topk" and a.topk != 64)
-            or (a.variant == "lmhead" and a.hidden != 4096)):
+    if (B != 32 or a.workload != "headline_v200064" or a.variant not in ("plain", "topk", "lmhead")
+            or (a.variant == "topk" and a.topk != 64) or (a.variant == "lmhead" and a.hidden != 4096)):
         traffic = None
     status = mds.workspace_status(ws_d) | mds.workspace_status(ws_v)
 
@@ -308,8 +332,10 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"Markov draft loop + rejection verify, V={V} r={r} K={K} B={B}, fp32 base/target/"
-                               f"cache, bf16 w1/w2, T=1" + {"plain": "", "indexed": ", request-state slots + row "
+        "config": {"workload": f"{a.workload}: Markov draft loop + rejection verify, V={V} r={r} K={K} B={B}, "
+                               + ("bf16 base/cache, fp32 target, top-p 0.95, T~U[0.7,1.0]" if wl.top_p is not None
+                                  else f"{wl.base_dtype} base, {wl.cache_dtype} cache, fp32 target") + ", bf16 w1/w2"
+                               + {"plain": "", "indexed": ", request-state slots + row "
                                "mapping", "fp64": ", float64 Gumbel",
                                "topk": f", top-k Markov drafting k={a.topk}",
                                "lmhead": f", base logits from the draft LM head (H={a.hidden}, bf16)"}[a.variant],
