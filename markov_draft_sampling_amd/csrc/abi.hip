@@ -510,7 +510,10 @@ int mds_draft_lm_head(int B, int K, int V, int H, const void* hidden, int64_t hi
   a.out_bf16 = out_dtype == MDS_BF16;
   a.vec_out = vec_ok(out, out_dtype, out_req_stride, out_step_stride);
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&a.cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "device query");
   if (ev_begin && (e = hipEventRecord((hipEvent_t)ev_begin, st)) != hipSuccess) return hip_fail(e, "event record");
   if ((e = mds::launch_lm_head(a, st)) != hipSuccess) return hip_fail(e, "LM head launch");
   if (ev_end && (e = hipEventRecord((hipEvent_t)ev_end, st)) != hipSuccess) return hip_fail(e, "event record");

@@ -7,126 +7,175 @@
 // accumulation on the matrix cores (v_mfma_f32_16x16x32_bf16), row m = b*K + k
 // written to the base-logit layout the draft loop reads.
 //
-// With B*K rows in the low hundreds the product is bound by the lm_head
-// stream (V*H*2 bytes, 1.64 GB at V = 200064, H = 4096), so each work-group
-// owns 128 vocabulary rows for all rows of its M tile (up to 256) and lm_head
-// is read from HBM once. One work-group per CU (accumulators in AGPRs, the
-// VGPRs free for deep prefetch): each of the four waves streams its own 32
-// vocabulary rows straight into MFMA A operands, two chunks of four 32-wide
-// slices of H ahead in registers, a row's 256 bytes of a chunk requested
-// together, with non-temporal loads (read once: they should not evict the
-// hidden rows, which every work-group re-reads, from L2). The M tile's hidden rows go through LDS in 128-wide
-// chunks (double buffered; rows padded to 272 bytes so the 16-byte fragment
-// reads of 16 consecutive rows hit distinct banks), loaded into registers a
-// whole chunk ahead. One barrier per chunk of four slices.
+// With B*K rows in the low hundreds the product is bound by memory traffic:
+// the lm_head stream (V*H*2 bytes, 1.64 GB at V = 200064, H = 4096, read once)
+// plus every work-group's re-read of its M tile's hidden rows (from L2). Each
+// work-group therefore owns as many vocabulary rows as its accumulators allow
+// (256 for up to 224 rows of M: 224 float accumulators a lane), one
+// work-group per CU. H is walked in chunks of 128 columns:
+//  - hidden rows: copied straight into LDS (buffer loads with the LDS flag, no
+//    registers), double buffered, 16-byte slots XOR-swizzled by row so the
+//    fragment reads of 16 consecutive rows hit distinct banks;
+//  - lm_head rows: each wave reads its own rows row-contiguously (whole 128-byte
+//    lines; a direct load in MFMA operand layout touches 16 rows per
+//    instruction and streams markedly slower), two chunks deep in registers,
+//    and stages each half chunk through a private LDS area into operand layout;
+//  - copies go out a few per slice of 32 columns and one barrier ends a chunk;
+//  - work-groups start at different chunks, so that they do not all read the
+//    same columns of the hidden rows (the same memory channels) at once.
 #include "mds_device.h"
 #include "mds_internal.h"
 
 namespace mds {
 namespace {
 
-constexpr int kNBW = 2;                   // 16-row vocabulary blocks per wave
-constexpr int kVT = 4 * kNBW * 16;        // vocabulary rows per work-group (128)
-constexpr int kKC = 128;                  // H columns per hidden chunk (4 slices)
-constexpr int kRS = kKC + 8;              // LDS row stride of a hidden chunk (bf16)
+constexpr int kKC = 128;  // H columns per chunk (4 slices of 32, 256 bytes a row)
+constexpr int kStagger = 7;  // chunk offset between consecutive work-groups
 
-// hidden chunk c of the M tile: thread t covers row 16 p + t / 16, 16-byte part t % 16.
-// Rows past M repeat row M - 1 (their results are never stored): every load
-// is unconditional, so the compiler can count outstanding loads exactly
-// instead of draining them at a branch.
-template <int MB>
-__device__ __forceinline__ void chunk_load(const LmHeadArgs& a, int m0, int c, int tid, u32x4 (&hs)[MB]) {
-#pragma unroll
-  for (int p = 0; p < MB; ++p) {
-    const int m = min(m0 + p * 16 + (tid >> 4), a.M - 1);
-    hs[p] = *(const u32x4*)(a.hidden + (size_t)m * a.hidden_rs + c * kKC + (tid & 15) * 8);
-  }
+// Work-group barrier once this wave's hidden-chunk copies have landed in LDS:
+// s_waitcnt vmcnt(N) lgkmcnt(0) (at most N newer loads, lm_head rows in
+// flight, stay outstanding; every LDS access of the wave has completed), then
+// s_barrier. No release fence: that would wait for every load in flight.
+template <int N>
+__device__ __forceinline__ void chunk_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
-template <int MB>
-__device__ __forceinline__ void chunk_store(uint16_t* buf, int tid, const u32x4 (&hs)[MB]) {
-#pragma unroll
-  for (int p = 0; p < MB; ++p) *(u32x4*)(buf + (p * 16 + (tid >> 4)) * kRS + (tid & 15) * 8) = hs[p];
-}
-
-template <int MB, bool OBF16>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void lm_head_kernel(LmHeadArgs a) {
+// MB: 16-row blocks of the M tile; NBW: 16-row vocabulary blocks per wave (the
+// work-group's four waves cover 64 NBW rows from vocabulary row v0 on)
+template <int MB, int NBW, bool OBF16>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void lm_head_kernel(LmHeadArgs a, int v0) {
+  constexpr int kNBW = NBW;
+  constexpr int kVT = 4 * kNBW * 16;
   constexpr int MT = MB * 16;
-  extern __shared__ __attribute__((aligned(16))) uint16_t s_h[];  // [2][MT * kRS]
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // hidden chunks, double buffered; 16-byte slot j of row R holds the row's slot j ^ (R & 15)
+  __shared__ __attribute__((aligned(16))) uint16_t s_h0[MT * kKC];
+  __shared__ __attribute__((aligned(16))) uint16_t s_h1[MT * kKC];
+  // each wave's lm_head rows for half a chunk (64 columns), staged from the row-contiguous loads
+  // into the MFMA operand layout; 16-byte slot t of row R sits at slot t ^ ((R / 2) % 8)
+  __shared__ __attribute__((aligned(16))) uint16_t s_a[4][16 * kNBW * 64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
   const int m0 = blockIdx.y * MT;
-  const int vw = blockIdx.x * kVT + w * kNBW * 16;  // first vocabulary row of this wave
+  const int vw = v0 + blockIdx.x * kVT + w * kNBW * 16;  // first vocabulary row of this wave
   const int S = a.H >> 5;                          // 32-wide slices of H (a multiple of 2 * 4)
+  const int NC = S / 4;                            // chunks of four slices
+  // this work-group's chunk order: coff, coff + 1, ... (mod NC)
+  const int coff = (int)((blockIdx.x * (unsigned)kStagger) % (unsigned)NC);
 
-  // A operands: vocabulary row vw + 16 nb + lr (clamped into range), elements 8 lg .. 8 lg + 7 of a slice
-  const uint16_t* arow[kNBW];
+  // hidden chunk c into LDS: wave w's instruction p fills rows 16 p + 4 w .. + 3 (1 KB), lane l
+  // landing in row 16 p + 4 w + l / 16, slot l % 16, so it fetches that row's slot (l % 16) ^ (4 w + l / 16).
+  // Buffer loads from the tile's first row: per-lane byte offsets (rows past M repeat row M - 1),
+  // the chunk's column offset as the scalar offset.
+  const int Mt = min(MT, a.M - m0);
+  const __amdgpu_buffer_rsrc_t hrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.hidden + (size_t)m0 * a.hidden_rs), (short)0, (int)((size_t)Mt * a.hidden_rs * 2),
+      0x00020000);  // descriptor word 3: raw byte-addressed access (32-bit data format)
+  const int R0 = w * 4 + (lane >> 4);
+  const int gsl = ((lane & 15) ^ R0) * 16;
+  auto dma_one = [&](uint16_t* buf, int c, int p) {
+    const int voff = min(p * 16 + R0, Mt - 1) * a.hidden_rs * 2 + gsl;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(hrs, (__attribute__((address_space(3))) void*)(buf + (p * 16 + w * 4) * kKC),
+                                             16, voff, (c + coff >= NC ? c + coff - NC : c + coff) * kKC * 2, 0, 0);
+  };
+  auto dma = [&](uint16_t* buf, int c) {
 #pragma unroll
-  for (int nb = 0; nb < kNBW; ++nb) {
-    const int v = min(vw + nb * 16 + lr, a.V - 1);
-    arow[nb] = a.lm_head + (size_t)v * a.H + lg * 8;
-  }
-  // A ring: three chunks of four slices; chunk c + 2 is requested while chunk c
-  // is multiplied, each row's 256 bytes of a chunk in one burst
-  u32x4 A[3][4][kNBW];
-#pragma unroll
-  for (int r = 0; r < 2; ++r)
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-#pragma unroll
-      for (int nb = 0; nb < kNBW; ++nb)
-        A[r][p][nb] = __builtin_nontemporal_load((const u32x4*)(arow[nb] + (r * 4 + p) * 32));
+    for (int p = 0; p < MB; ++p) dma_one(buf, c, p);
+  };
 
+  // lm_head rows of this wave: 16 NBW rows from vw on, read row-contiguously (half a chunk is
+  // 2 NBW loads of eight 128-byte row segments each: lane l takes row 8 i + l / 8, slot l % 8),
+  // rows past V repeat row V - 1; buffer loads from the work-group's first row, non-temporal
+  const int vt0 = v0 + blockIdx.x * kVT;
+  const int nrows = min(kVT, a.V - vt0);
+  const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.lm_head + (size_t)vt0 * a.H), (short)0, (int)((size_t)nrows * a.H * 2), 0x00020000);
+  constexpr int kAL = 2 * kNBW;  // loads per half chunk
+  int aoff[kAL];
+#pragma unroll
+  for (int i = 0; i < kAL; ++i) aoff[i] = min(w * 16 * kNBW + i * 8 + (lane >> 3), nrows - 1) * a.H * 2 + (lane & 7) * 16;
+  auto aload = [&](int c, int h, int i) {
+    return __builtin_amdgcn_raw_buffer_load_b128(ars, aoff[i], (c + coff >= NC ? c + coff - NC : c + coff) * 256 + h * 128, 2);
+  };
+  uint16_t* sa = s_a[w];
+  // staging slot of load i's lane: row 8 i + lane / 8, slot (lane % 8) ^ ((4 i + lane / 16) % 8)
+  int soff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) soff[i] = (lane >> 3) * 64 + (((lane & 7) ^ ((i * 4 + (lane >> 4)) & 7)) * 8);
+  // operand read of slice q of a half: row 16 nb + lr, slot (4 q + lg) ^ ((lr / 2) % 8)
+  int roff[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) roff[q] = lr * 64 + (((q * 4 + lg) ^ ((lr >> 1) & 7)) * 8);
   floatx4 acc[kNBW][MB];
 #pragma unroll
   for (int nb = 0; nb < kNBW; ++nb)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  u32x4 hs[MB];
-  chunk_load<MB>(a, m0, 0, tid, hs);
-  chunk_store<MB>(s_h, tid, hs);
-  __syncthreads();
+  // lm_head ring of two chunks. Per chunk c the copies go out before the slices' operand reads:
+  // lm_head half 0 of chunk c + 1 (slice 0), the two halves of hidden chunk c + 1 (slices 1
+  // and 2), lm_head half 1 of chunk c + 1 (slice 3). The wait for the hidden chunk at the end of
+  // chunk c leaves those last lm_head loads in flight (first staged at slice 2 of chunk c + 1).
+  dma(s_h0, 0);
+  u32x4 A[2][2][kAL];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < kAL; ++i) A[0][h][i] = aload(0, h, i);
+  chunk_barrier<0>();
 
-  const int NC = S / 4;  // chunks of four slices
-  for (int c0 = 0; c0 < NC; c0 += 6) {
+#pragma nounroll
+  for (int c0 = 0; c0 < NC; c0 += 2) {
 #pragma unroll
-    for (int cc = 0; cc < 6; ++cc) {
-      const int c = c0 + cc;  // chunk c: ring slot cc % 3, hidden rows in LDS buffer cc % 2
-      if (c < NC) {
-        // next hidden chunk first, then the A chunk two ahead: waiting for the
-        // former at the end of this chunk does not wait for the latter (the
-        // last chunks are requested again at the end: L2 hits, never used)
-        chunk_load<MB>(a, m0, min(c + 1, NC - 1), tid, hs);
-        const int cn = min(c + 2, NC - 1);
-#pragma unroll
-        for (int p = 0; p < 4; ++p)
-#pragma unroll
-          for (int nb = 0; nb < kNBW; ++nb)
-            A[(cc + 2) % 3][p][nb] = __builtin_nontemporal_load((const u32x4*)(arow[nb] + (cn * 4 + p) * 32));
+    for (int cc = 0; cc < 2; ++cc) {
+      const int c = c0 + cc;  // chunk c: ring slot and LDS buffer cc (NC is even: H is a multiple of 256)
+      {
+        uint16_t* cur = cc ? s_h1 : s_h0;
+        uint16_t* nxt = cc ? s_h0 : s_h1;
+        // the last chunk is requested again at the end (L2 hits, never used)
+        const int ch = min(c + 1, NC - 1);
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          const uint16_t* hb = s_h + (cc & 1) * MT * kRS + lr * kRS + p * 32 + lg * 8;
-          const bf16x8 a0 = __builtin_bit_cast(bf16x8, A[cc % 3][p][0]);
-          const bf16x8 a1 = __builtin_bit_cast(bf16x8, A[cc % 3][p][1]);
+          if (p == 0 || p == 3) {
+#pragma unroll
+            for (int i = 0; i < kAL; ++i) A[cc ^ 1][p == 3][i] = aload(ch, p == 3, i);
+          } else {
+#pragma unroll
+            for (int q = 0; q < MB; ++q)
+              if ((q < (MB + 1) / 2) == (p == 1)) dma_one(nxt, ch, q);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          if ((p & 1) == 0) {
+            // this half's lm_head rows into the wave's staging area (LDS operations of a wave
+            // complete in order: the previous half's operand reads are done before these land)
+#pragma unroll
+            for (int i = 0; i < kAL; ++i) *(u32x4*)(sa + i * 8 * 64 + soff[i & 1]) = A[cc][p >> 1][i];
+          }
+          const uint16_t* hb = cur + lr * kKC + (((p * 4 + lg) ^ lr) * 8);
+          bf16x8 af[kNBW];
+#pragma unroll
+          for (int nb = 0; nb < kNBW; ++nb) af[nb] = *(const bf16x8*)(sa + nb * 16 * 64 + roff[p & 1]);
           // all of the slice's hidden fragments first, so their LDS reads overlap
           bf16x8 bfr[MB];
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb) bfr[mb] = *(const bf16x8*)(hb + mb * 16 * kRS);
+          for (int mb = 0; mb < MB; ++mb) bfr[mb] = *(const bf16x8*)(hb + mb * 16 * kKC);
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb) {
-            acc[0][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bfr[mb], acc[0][mb], 0, 0, 0);
-            acc[1][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bfr[mb], acc[1][mb], 0, 0, 0);
-          }
-          // schedule: the slice's LDS reads all go out first, then the MFMAs
-          // (the scheduler would otherwise wait on each read before its two
-          // MFMAs, or chain one accumulator's MFMAs across slices)
-          __builtin_amdgcn_sched_group_barrier(0x100, MB, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 2 * MB, 0);
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < kNBW; ++nb)
+              acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[nb], bfr[mb], acc[nb][mb], 0, 0, 0);
+          if ((p & 1) == 0) __builtin_amdgcn_sched_group_barrier(0x200, kAL, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, MB + kNBW, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, kNBW * MB, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
-        chunk_store<MB>(s_h + ((cc + 1) & 1) * MT * kRS, tid, hs);
-        __syncthreads();
+        // hidden chunk c + 1 has landed in LDS (only lm_head half 1 of chunk c + 1 may be in flight)
+        chunk_barrier<kAL>();
       }
     }
   }
@@ -167,20 +216,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 }
 
+template <int MB, int NBW>
+hipError_t launch_mb(const LmHeadArgs& a, int v0, int n_tiles, int m_tiles, hipStream_t st) {
+  const dim3 grid(n_tiles, m_tiles);
+  if (a.out_bf16)
+    hipLaunchKernelGGL((lm_head_kernel<MB, NBW, true>), grid, dim3(256), 0, st, a, v0);
+  else
+    hipLaunchKernelGGL((lm_head_kernel<MB, NBW, false>), grid, dim3(256), 0, st, a, v0);
+  return hipGetLastError();
+}
+
+// One work-group per CU: the tiles of 64 NBW vocabulary rows (256 while the
+// accumulators fit, 128 for M tiles of 240 or 256 rows) run in rounds of `cus`. A last partial round (whose few work-groups would each still stream
+// their whole lm_head tile through one CU while the others idle) is instead
+// covered by 64-row tiles, NBW times as many work-groups each with 1/NBW of the
+// stream; a vocabulary too small for one round uses 64-row tiles throughout.
 template <int MB>
-hipError_t launch_mb(const LmHeadArgs& a, int m_tiles, hipStream_t st) {
-  const dim3 grid((a.V + kVT - 1) / kVT, m_tiles);
-  const size_t lds = (size_t)2 * MB * 16 * kRS * sizeof(uint16_t);
-  const void* fn = a.out_bf16 ? (const void*)lm_head_kernel<MB, true> : (const void*)lm_head_kernel<MB, false>;
-  if (lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+hipError_t launch_split(const LmHeadArgs& a, int m_tiles, hipStream_t st) {
+  constexpr int NBW = MB <= 14 ? 4 : 2;
+  constexpr int ROWS = 64 * NBW;
+  const int tiles = (a.V + ROWS - 1) / ROWS;
+  const int cus = a.cus > 0 ? a.cus : tiles;
+  const int full = m_tiles == 1 ? (tiles / cus) * cus : tiles;
+  if (full == tiles) return launch_mb<MB, NBW>(a, 0, tiles, m_tiles, st);
+  if (full > 0) {
+    const hipError_t e = launch_mb<MB, NBW>(a, 0, full, m_tiles, st);
     if (e != hipSuccess) return e;
   }
-  if (a.out_bf16)
-    hipLaunchKernelGGL((lm_head_kernel<MB, true>), grid, dim3(256), lds, st, a);
-  else
-    hipLaunchKernelGGL((lm_head_kernel<MB, false>), grid, dim3(256), lds, st, a);
-  return hipGetLastError();
+  const int v0 = full * ROWS;
+  return launch_mb<MB, 1>(a, v0, (a.V - v0 + 63) / 64, m_tiles, st);
 }
 
 }  // namespace
@@ -190,22 +254,22 @@ hipError_t launch_lm_head(const LmHeadArgs& a, hipStream_t st) {
   const int mb = M >= 256 ? 16 : (M + 15) / 16;
   const int m_tiles = (M + 255) / 256;
   switch (mb) {
-    case 1: return launch_mb<1>(a, m_tiles, st);
-    case 2: return launch_mb<2>(a, m_tiles, st);
-    case 3: return launch_mb<3>(a, m_tiles, st);
-    case 4: return launch_mb<4>(a, m_tiles, st);
-    case 5: return launch_mb<5>(a, m_tiles, st);
-    case 6: return launch_mb<6>(a, m_tiles, st);
-    case 7: return launch_mb<7>(a, m_tiles, st);
-    case 8: return launch_mb<8>(a, m_tiles, st);
-    case 9: return launch_mb<9>(a, m_tiles, st);
-    case 10: return launch_mb<10>(a, m_tiles, st);
-    case 11: return launch_mb<11>(a, m_tiles, st);
-    case 12: return launch_mb<12>(a, m_tiles, st);
-    case 13: return launch_mb<13>(a, m_tiles, st);
-    case 14: return launch_mb<14>(a, m_tiles, st);
-    case 15: return launch_mb<15>(a, m_tiles, st);
-    default: return launch_mb<16>(a, m_tiles, st);
+    case 1: return launch_split<1>(a, m_tiles, st);
+    case 2: return launch_split<2>(a, m_tiles, st);
+    case 3: return launch_split<3>(a, m_tiles, st);
+    case 4: return launch_split<4>(a, m_tiles, st);
+    case 5: return launch_split<5>(a, m_tiles, st);
+    case 6: return launch_split<6>(a, m_tiles, st);
+    case 7: return launch_split<7>(a, m_tiles, st);
+    case 8: return launch_split<8>(a, m_tiles, st);
+    case 9: return launch_split<9>(a, m_tiles, st);
+    case 10: return launch_split<10>(a, m_tiles, st);
+    case 11: return launch_split<11>(a, m_tiles, st);
+    case 12: return launch_split<12>(a, m_tiles, st);
+    case 13: return launch_split<13>(a, m_tiles, st);
+    case 14: return launch_split<14>(a, m_tiles, st);
+    case 15: return launch_split<15>(a, m_tiles, st);
+    default: return launch_split<16>(a, m_tiles, st);
   }
 }
 

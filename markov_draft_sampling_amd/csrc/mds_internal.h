@@ -140,6 +140,7 @@ struct LmHeadArgs {
   void* out;                  // row (b, k) at b*out_rs + k*out_ss elements, float32 or bf16
   long long out_rs, out_ss;
   int out_bf16, vec_out;
+  int cus;                    // compute units of the device (the launch splits its last partial round)
 };
 hipError_t launch_lm_head(const LmHeadArgs& a, hipStream_t st);
 hipError_t launch_topk_select(const TopkArgs& a, hipStream_t st);

@@ -59,7 +59,9 @@ def _run(B, K, V, H, seed, out_dtype="f32", pad=0, extra_steps=0):
 
 
 @pytest.mark.parametrize("B,K,V,H", [(1, 7, 4096, 256), (8, 7, 32000, 512), (32, 7, 12345, 256), (3, 5, 130, 256),
-                                     (2, 3, 999, 1024), (5, 3, 700, 768)])
+                                     (2, 3, 999, 1024), (5, 3, 700, 768),
+                                     # past one round of 128-row tiles on 256 CUs: 64-row tail tiles, ragged
+                                     (2, 3, 33001, 256)])
 def test_lm_head_matches_oracle(B, K, V, H):
     hidden, lm, got = _run(B, K, V, H, seed=B * 31 + V)
     _check(hidden, lm, got)
