@@ -217,12 +217,14 @@ __device__ __forceinline__ void wave_lds_sync() {
 // One wave combines nrows consecutive rows of NC packed partials, partial
 // (row, chunk) at p[chunk * cstride + row]: the max of the words (keys) or
 // their (max, sum exp) merge. Partials are read with device-scope atomic
-// loads and staged in LDS a page at a time (all loads of a page in flight
+// loads when coherent (published inside the same launch), else with plain
+// loads (stored by an earlier launch), and staged in LDS a page at a time (all loads of a page in flight
 // together); each row of the page is then merged by a group of lanes (a
 // power of two) and the group's results by shuffles. Results go to
 // om / os / okey [row].
 __device__ void wave_combine(const unsigned long long* p, size_t cstride, int nrows, int NC, bool keys,
-                             unsigned long long* stage, float* om, float* os, unsigned long long* okey) {
+                             unsigned long long* stage, float* om, float* os, unsigned long long* okey,
+                             bool coherent) {
   const int lane = threadIdx.x & 63;
   const int cpp = NC < kStage ? NC : kStage;  // chunks per page
   const int rpp = kStage / cpp;               // rows per page, >= 1
@@ -245,8 +247,8 @@ __device__ void wave_combine(const unsigned long long* p, size_t cstride, int nr
             int t = t0 + u * 64 + lane;
             t = t < n ? t : n - 1;
             const int rr = t / nc, cc = t - rr * nc;
-            w[u] = __hip_atomic_load(p + (size_t)(c0 + cc) * cstride + (r0 + rr), __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
+            const unsigned long long* q = p + (size_t)(c0 + cc) * cstride + (r0 + rr);
+            w[u] = coherent ? __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *q;
           }
         }
 #pragma unroll
@@ -387,13 +389,15 @@ __device__ void combine_request(const VerifyArgs& a, int b, int sl, ReqLds& L, u
     if (greedy) {
       L.x[lane] = x0;
     } else {
-      const unsigned long long w = __hip_atomic_load(a.tq + b * K + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned long long w =
+          counted ? __hip_atomic_load(a.tq + b * K + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : a.tq[b * K + lane];
       L.x[lane] = (x0 == -1) ? -1 : ((x0 < 0 || x0 >= a.V) ? 0 : x0);
       L.tx[lane] = unpack_m(w);
       L.cx[lane] = unpack_s(w);
     }
   }
-  wave_combine(a.tpart + (size_t)b * (K + 1), (size_t)a.B * (K + 1), K + 1, NC, greedy, stage, L.m, L.lz, L.key);
+  wave_combine(a.tpart + (size_t)b * (K + 1), (size_t)a.B * (K + 1), K + 1, NC, greedy, stage, L.m, L.lz, L.key,
+               counted);
   if (lane <= K) {
     const float s = L.lz[lane];
     const float lz = (s != s) ? NAN : __logf(s);
@@ -401,7 +405,7 @@ __device__ void combine_request(const VerifyArgs& a, int b, int sl, ReqLds& L, u
     a.rowstat[b * (K + 1) + lane] = RowStat{L.m[lane], lz, L.key[lane]};
   }
   if (a.qpart && !greedy) {
-    wave_combine(a.qpart + (size_t)b * K, (size_t)a.B * K, K, NC, false, stage, L.qm, L.lq, L.qkey);
+    wave_combine(a.qpart + (size_t)b * K, (size_t)a.B * K, K, NC, false, stage, L.qm, L.lq, L.qkey, counted);
     if (lane < K) {
       const float s = L.lq[lane];
       const float lq = (s != s) ? NAN : L.qm[lane] + __logf(s);
@@ -713,7 +717,7 @@ __device__ unsigned long long wave_draw_p(const VerifyArgs& a, const float* trow
 // draws from p over the whole row instead.
 template <bool CBF16>
 __global__ __launch_bounds__(kThreads) void residual_kernel(VerifyArgs a) {
-  constexpr int kPer = kResCols / kThreads;  // 8 columns: c0 + 1024 i + 4 tid + e
+  constexpr int kPer = kResCols / kThreads;  // columns c0 + 1024 i + 4 tid + e
   const int chunk = blockIdx.x, b = blockIdx.y;
   const ReqState rq = a.req[b];
   if (rq.mode == 2) return;
