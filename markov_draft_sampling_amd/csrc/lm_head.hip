@@ -11,11 +11,13 @@
 // the lm_head stream (V*H*2 bytes, 1.64 GB at V = 200064, H = 4096, read once)
 // plus every work-group's re-read of its M tile's hidden rows (from L2). Each
 // work-group therefore owns as many vocabulary rows as its accumulators allow
-// (256 for up to 224 rows of M: 224 float accumulators a lane), one
-// work-group per CU. H is walked in chunks of 128 columns:
+// (256 for up to 224 rows of M, in eight waves of 32 rows: 112 float
+// accumulators a lane, two waves per SIMD), one work-group per CU. H is
+// walked in chunks of 128 columns:
 //  - hidden rows: copied straight into LDS (buffer loads with the LDS flag, no
-//    registers), double buffered, 16-byte slots XOR-swizzled by row so the
-//    fragment reads of 16 consecutive rows hit distinct banks;
+//    registers; instruction q of wave w fills 4 rows, 4 NW q + 4 w ..),
+//    double buffered, 16-byte slots XOR-swizzled by row so the fragment reads
+//    of 16 consecutive rows hit distinct banks;
 //  - lm_head rows: each wave reads its own rows row-contiguously (whole 128-byte
 //    lines; a direct load in MFMA operand layout touches 16 rows per
 //    instruction and streams markedly slower), two chunks deep in registers,
@@ -45,19 +47,19 @@ __device__ __forceinline__ void chunk_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// MB: 16-row blocks of the M tile; NBW: 16-row vocabulary blocks per wave (the
-// work-group's four waves cover 64 NBW rows from vocabulary row v0 on)
-template <int MB, int NBW, bool OBF16>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void lm_head_kernel(LmHeadArgs a, int v0) {
+// MB: 16-row blocks of the M tile; NBW: 16-row vocabulary blocks per wave; NW:
+// waves (the work-group covers 16 NBW NW rows from vocabulary row v0 on)
+template <int MB, int NBW, int NW, bool OBF16>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void lm_head_kernel(LmHeadArgs a, int v0) {
   constexpr int kNBW = NBW;
-  constexpr int kVT = 4 * kNBW * 16;
+  constexpr int kVT = NW * kNBW * 16;
   constexpr int MT = MB * 16;
   // hidden chunks, double buffered; 16-byte slot j of row R holds the row's slot j ^ (R & 15)
   __shared__ __attribute__((aligned(16))) uint16_t s_h0[MT * kKC];
   __shared__ __attribute__((aligned(16))) uint16_t s_h1[MT * kKC];
   // each wave's lm_head rows for half a chunk (64 columns), staged from the row-contiguous loads
   // into the MFMA operand layout; 16-byte slot t of row R sits at slot t ^ ((R / 2) % 8)
-  __shared__ __attribute__((aligned(16))) uint16_t s_a[4][16 * kNBW * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t s_a[NW][16 * kNBW * 64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
@@ -68,24 +70,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // this work-group's chunk order: coff, coff + 1, ... (mod NC)
   const int coff = (int)((blockIdx.x * (unsigned)kStagger) % (unsigned)NC);
 
-  // hidden chunk c into LDS: wave w's instruction p fills rows 16 p + 4 w .. + 3 (1 KB), lane l
-  // landing in row 16 p + 4 w + l / 16, slot l % 16, so it fetches that row's slot (l % 16) ^ (4 w + l / 16).
+  // hidden chunk c into LDS: wave w's instruction p fills rows R = 4 NW p + 4 w .. + 3 (1 KB), lane
+  // l landing in row R + l / 16, slot l % 16, so it fetches that row's slot (l % 16) ^ ((4 w + l / 16) % 16).
   // Buffer loads from the tile's first row: per-lane byte offsets (rows past M repeat row M - 1),
   // the chunk's column offset as the scalar offset.
   const int Mt = min(MT, a.M - m0);
   const __amdgpu_buffer_rsrc_t hrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.hidden + (size_t)m0 * a.hidden_rs), (short)0, (int)((size_t)Mt * a.hidden_rs * 2),
       0x00020000);  // descriptor word 3: raw byte-addressed access (32-bit data format)
+  constexpr int kQ = (MT + 4 * NW - 1) / (4 * NW);  // copy instructions per wave and chunk
   const int R0 = w * 4 + (lane >> 4);
-  const int gsl = ((lane & 15) ^ R0) * 16;
+  const int gsl = ((lane & 15) ^ (R0 & 15)) * 16;
   auto dma_one = [&](uint16_t* buf, int c, int p) {
-    const int voff = min(p * 16 + R0, Mt - 1) * a.hidden_rs * 2 + gsl;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(hrs, (__attribute__((address_space(3))) void*)(buf + (p * 16 + w * 4) * kKC),
+    if (MT % (4 * NW) != 0 && p * 4 * NW + w * 4 >= MT) return;
+    const int voff = min(p * 4 * NW + R0, Mt - 1) * a.hidden_rs * 2 + gsl;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(hrs, (__attribute__((address_space(3))) void*)(buf + (p * 4 * NW + w * 4) * kKC),
                                              16, voff, (c + coff >= NC ? c + coff - NC : c + coff) * kKC * 2, 0, 0);
   };
   auto dma = [&](uint16_t* buf, int c) {
 #pragma unroll
-    for (int p = 0; p < MB; ++p) dma_one(buf, c, p);
+    for (int p = 0; p < kQ; ++p) dma_one(buf, c, p);
   };
 
   // lm_head rows of this wave: 16 NBW rows from vw on, read row-contiguously (half a chunk is
@@ -146,8 +150,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             for (int i = 0; i < kAL; ++i) A[cc ^ 1][p == 3][i] = aload(ch, p == 3, i);
           } else {
 #pragma unroll
-            for (int q = 0; q < MB; ++q)
-              if ((q < (MB + 1) / 2) == (p == 1)) dma_one(nxt, ch, q);
+            for (int q = 0; q < kQ; ++q)
+              if ((q < (kQ + 1) / 2) == (p == 1)) dma_one(nxt, ch, q);
           }
           __builtin_amdgcn_sched_barrier(0);
           if ((p & 1) == 0) {
@@ -216,35 +220,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 }
 
-template <int MB, int NBW>
+template <int MB, int NBW, int NW>
 hipError_t launch_mb(const LmHeadArgs& a, int v0, int n_tiles, int m_tiles, hipStream_t st) {
   const dim3 grid(n_tiles, m_tiles);
   if (a.out_bf16)
-    hipLaunchKernelGGL((lm_head_kernel<MB, NBW, true>), grid, dim3(256), 0, st, a, v0);
+    hipLaunchKernelGGL((lm_head_kernel<MB, NBW, NW, true>), grid, dim3(NW * 64), 0, st, a, v0);
   else
-    hipLaunchKernelGGL((lm_head_kernel<MB, NBW, false>), grid, dim3(256), 0, st, a, v0);
+    hipLaunchKernelGGL((lm_head_kernel<MB, NBW, NW, false>), grid, dim3(NW * 64), 0, st, a, v0);
   return hipGetLastError();
 }
 
-// One work-group per CU: the tiles of 64 NBW vocabulary rows (256 while the
-// accumulators fit, 128 for M tiles of 240 or 256 rows) run in rounds of `cus`. A last partial round (whose few work-groups would each still stream
-// their whole lm_head tile through one CU while the others idle) is instead
-// covered by 64-row tiles, NBW times as many work-groups each with 1/NBW of the
-// stream; a vocabulary too small for one round uses 64-row tiles throughout.
+// One work-group per CU: the 256-row tiles (eight waves of 32 rows, two per
+// SIMD; four of 64 for a 13-block M tile, whose eight-wave form would spill)
+// run in rounds of `cus`; M tiles of 15 or 16 blocks take 128-row tiles (four
+// waves of 32 rows) to keep their accumulators in registers. A last partial
+// round (whose few work-groups would each still stream their whole lm_head
+// tile through one CU while the others idle) is instead covered by 64-row
+// tiles (four waves of 16 rows); a vocabulary too small for one round uses
+// 64-row tiles throughout.
 template <int MB>
 hipError_t launch_split(const LmHeadArgs& a, int m_tiles, hipStream_t st) {
-  constexpr int NBW = MB <= 14 ? 4 : 2;
-  constexpr int ROWS = 64 * NBW;
+  constexpr int NWM = (MB <= 14 && MB != 13) ? 8 : 4;
+  constexpr int NBW = MB <= 14 ? 256 / 16 / NWM : 2;
+  constexpr int ROWS = 16 * NBW * NWM;
   const int tiles = (a.V + ROWS - 1) / ROWS;
   const int cus = a.cus > 0 ? a.cus : tiles;
   const int full = m_tiles == 1 ? (tiles / cus) * cus : tiles;
-  if (full == tiles) return launch_mb<MB, NBW>(a, 0, tiles, m_tiles, st);
+  if (full == tiles) return launch_mb<MB, NBW, NWM>(a, 0, tiles, m_tiles, st);
   if (full > 0) {
-    const hipError_t e = launch_mb<MB, NBW>(a, 0, full, m_tiles, st);
+    const hipError_t e = launch_mb<MB, NBW, NWM>(a, 0, full, m_tiles, st);
     if (e != hipSuccess) return e;
   }
   const int v0 = full * ROWS;
-  return launch_mb<MB, 1>(a, v0, (a.V - v0 + 63) / 64, m_tiles, st);
+  return launch_mb<MB, 1, 4>(a, v0, (a.V - v0 + 63) / 64, m_tiles, st);
 }
 
 }  // namespace
