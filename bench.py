@@ -68,6 +68,14 @@ def lm_head_bytes(M, V, H, s_out=4):
     return V * H * 2 + M * H * 2 + M * V * s_out
 
 
+def fused_draft_bytes(B, K, V, r, H, s_base=4, s_cache=4):
+    """The draft call from hidden states: the LM head (lm_head, hidden, base rows
+    of steps 1..K-1 written), step 0 in its work-groups (w2, cache row 0), then
+    steps 1..K-1 (w2, base row, cache row each)."""
+    return (V * H * 2 + B * K * H * 2 + B * (K - 1) * V * s_base + (V * r * 2 + B * V * s_cache)
+            + (K - 1) * (V * r * 2 + B * V * (s_base + s_cache)))
+
+
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "markov_draft_sampling_amd", "csrc")
 
@@ -137,11 +145,12 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=32, help="requests the CPU oracle baseline runs on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="do not flush caches between timed steps")
-    ap.add_argument("--variant", choices=("plain", "indexed", "fp64", "topk", "lmhead"), default="plain",
+    ap.add_argument("--variant", choices=("plain", "indexed", "fp64", "topk", "lmhead", "lmhead_fused"), default="plain",
                     help="plain: batch-indexed draft + verify; indexed: the same work through request-state slots, "
                          "a row mapping and per-step sample positions; fp64: the float64 Gumbel option; topk: "
                          "top-k Markov drafting (--topk candidates per row); lmhead: the draft LM head "
-                         "(hidden [B*K, --hidden] x lm_head [V, --hidden]) computes the base logits, then plain")
+                         "(hidden [B*K, --hidden] x lm_head [V, --hidden]) computes the base logits, then plain; "
+                         "lmhead_fused: the same as one call, step 0 inside the LM head's work-groups")
     ap.add_argument("--hidden", type=int, default=4096, help="hidden size of --variant lmhead")
     ap.add_argument("--topk", type=int, default=64, help="candidates per row of --variant topk")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -189,7 +198,7 @@ def main():
     ws_v = mds.new_workspace(mds.verify_workspace_bytes(B, K, V, top_p is not None, True), dev)
     flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)  # 512 MiB, read to evict caches
     stream = torch.cuda.current_stream(dev)
-    if a.variant == "lmhead":
+    if a.variant in ("lmhead", "lmhead_fused"):
         t_gen = time.perf_counter()
         hid_np, lm_np = workloads.make_lm_head(B * K, V, a.hidden, seed=1)
         hidden = torch.from_numpy(hid_np.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -213,6 +222,14 @@ def main():
         s_temp, s_seed = torch.from_numpy(s_temp).to(dev), torch.from_numpy(s_seed).to(dev)
 
     def step(events=None):
+        if a.variant == "lmhead_fused":
+            mds.markov_draft_loop_from_hidden(hidden, lm_head, base, w1, w2, anchor, apos, temp, seeds, cache, toks,
+                                              lse, workspace=ws_d, events=events)
+            if events is not None:
+                launches.append(1)
+            mds.rejection_verify(target, cache, toks, temp, seeds, apos, out, nacc, draft_lse=lse,
+                                 top_p=top_p, workspace=ws_v)
+            return
         if a.variant == "lmhead":
             mds.draft_lm_head(hidden, lm_head, base, K, events=events)
             if events is not None:
@@ -303,6 +320,8 @@ def main():
     if a.variant == "lmhead":
         bytes_per_launch = lm_head_bytes(B * K, V, a.hidden)
         draft_b += bytes_per_launch
+    if a.variant == "lmhead_fused":
+        bytes_per_launch = draft_b = fused_draft_bytes(B, K, V, r, a.hidden, s_base=s_b, s_cache=s_c)
     achieved = bytes_per_launch / (kern_avg_ms * 1e-3) / 1e9
     step_gbps = (draft_b + verify_b) / (ms * 1e-3) / 1e9
     acc_len = float((nacc.float() + 1).mean().item())
@@ -338,10 +357,12 @@ def main():
                                + {"plain": "", "indexed": ", request-state slots + row "
                                "mapping", "fp64": ", float64 Gumbel",
                                "topk": f", top-k Markov drafting k={a.topk}",
-                               "lmhead": f", base logits from the draft LM head (H={a.hidden}, bf16)"}[a.variant],
+                               "lmhead": f", base logits from the draft LM head (H={a.hidden}, bf16)",
+                               "lmhead_fused": f", the draft LM head (H={a.hidden}, bf16) with step 0 fused, "
+                               "one call"}[a.variant],
                    "V": V, "r": r, "K": K, "B": B, "variant": a.variant,
                    **({"topk": a.topk} if a.variant == "topk" else {}),
-                   **({"hidden": a.hidden} if a.variant == "lmhead" else {}),
+                   **({"hidden": a.hidden} if a.variant in ("lmhead", "lmhead_fused") else {}),
                    "cache_flushed_between_steps": not a.no_flush},
         "hbm": {"algorithmic_bytes_per_step": draft_b + verify_b, "achieved_GBps": step_gbps,
                 "peak_GBps": HBM_PEAK_GBPS, "frac": step_gbps / HBM_PEAK_GBPS},
@@ -349,6 +370,9 @@ def main():
                                 if a.variant == "topk" else
                                 "lm_head_kernel (draft LM head, bf16 MFMA, lm_head streamed once)"
                                 if a.variant == "lmhead" else
+                                "the draft call from hidden states (LM head with step 0 fused, steps 1..K-1, "
+                                "finalize): all its launches"
+                                if a.variant == "lmhead_fused" else
                                 "draft_wave_kernel (one Markov step, w2 streamed)"),
                      "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
@@ -375,7 +399,7 @@ def main():
         res["copy_calibration_bytes"] = {"read": src.numel() * 4, "write": dst.numel() * 4}
     if not a.no_cpu_baseline:
         kw = {"topk": a.topk} if a.variant == "topk" else ({"fp64_gumbel": True} if a.variant == "fp64" else {})
-        if a.variant == "lmhead":
+        if a.variant in ("lmhead", "lmhead_fused"):
             # the LM head dominates the oracle's time: at most 16 requests, once
             res["cpu_baseline"] = cpu_baseline(wl, min(a.cpu_sample, 16), repeats=1, lm=(hid_np, lm_np))
         else:

@@ -320,6 +320,37 @@ int mds_draft_lm_head(int B, int K, int V, int H, const void* hidden, int64_t hi
                       int64_t out_step_stride, void* stream, void* ev_begin, void* ev_end);
 
 /*
+ * mds_markov_draft_loop_from_hidden - the draft LM head followed by the
+ * K-step Markov draft loop (DSparkSpeculator API page, _sample_sequential:
+ * compute_draft_logits gives the base draft logits of every (request, step)
+ * row, which the sequential loop then consumes).
+ *   hidden, lm_head, H    as for mds_draft_lm_head
+ *   base                  MDS_F32 or MDS_BF16 rows [B, >=K, V] as the out of
+ *                         mds_draft_lm_head: receives the base logits of steps
+ *                         1 .. K-1; its step-0 rows are scratch (left unwritten
+ *                         when step 0 runs fused)
+ *   the other arguments   as for mds_markov_draft_loop (workspace of
+ *                         mds_draft_workspace_bytes(B, K, V, r))
+ *   ev_begin / ev_end     hipEvent_t (as void*) or NULL, recorded before the
+ *                         first and after the last launch of the call
+ * The results equal those of mds_draft_lm_head followed by
+ * mds_markov_draft_loop on the same buffers: draft tokens, the cache and base
+ * rows 1 .. K-1 bit for bit, draft_lse up to the order of float32 sums. When
+ * B <= 32, B*K <= 256 and r <= 256, step 0 runs inside the LM head's
+ * work-groups (its base row is neither stored nor read back, and one launch
+ * fewer); otherwise the two run one after the other. Errors as for the two.
+ */
+int mds_markov_draft_loop_from_hidden(int B, int K, int V, int r, int H, const void* hidden,
+                                      int64_t hidden_row_stride, const void* lm_head, void* base,
+                                      int base_dtype, int64_t base_req_stride, int64_t base_step_stride,
+                                      const void* w1, const void* w2, const int32_t* anchor_tokens,
+                                      const int64_t* anchor_pos, const float* temperature,
+                                      const int64_t* seeds, void* cache, int cache_dtype,
+                                      int64_t cache_req_stride, int64_t cache_step_stride,
+                                      int32_t* draft_tokens, float* draft_lse, void* workspace,
+                                      size_t workspace_bytes, void* stream, void* ev_begin, void* ev_end);
+
+/*
  * mds_rejection_verify_indexed - mds_rejection_verify with request-state
  * indexing: request b uses state slot s = idx_map[b] (temperature[s],
  * seeds[s], top_p[s], arrays of n_slots) and draft-logits cache rows

@@ -63,6 +63,9 @@ _SIGS = {
                                                    _vp, _vp, _c_int, _vp, _c_int, _c_i64, _c_i64, _vp, _vp,
                                                    ctypes.c_uint32, _vp, _c_sz, _vp, _vp, _vp], _c_int),
     "mds_draft_lm_head": ([_c_int] * 4 + [_vp, _c_i64, _vp, _vp, _c_int, _c_i64, _c_i64, _vp, _vp, _vp], _c_int),
+    "mds_markov_draft_loop_from_hidden": ([_c_int] * 5 + [_vp, _c_i64, _vp, _vp, _c_int, _c_i64, _c_i64, _vp, _vp, _vp,
+                                                          _vp, _vp, _vp, _vp, _c_int, _c_i64, _c_i64, _vp, _vp, _vp,
+                                                          _c_sz, _vp, _vp, _vp], _c_int),
     "mds_rejection_verify_indexed": ([_c_int] * 3 + [_vp, _c_i64, _vp, _c_int, _c_i64, _c_i64, _c_int, _vp, _vp, _vp,
                                                      _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp],
                                      _c_int),
@@ -421,6 +424,46 @@ def draft_lm_head(hidden, lm_head, out, K, stream=None, events=None):
                                   _dtype_code(out), out.stride(0), out.stride(1), _stream(stream, hidden.device),
                                   ev[0], ev[1])
     _check(rc, "draft_lm_head")
+
+
+def _event_ptrs(events, stream, device):
+    """(begin, end) void pointers of an optional torch.cuda.Event pair."""
+    import torch
+    if events is None:
+        return (None, None)
+    st = stream if stream is not None else torch.cuda.current_stream(device)
+    for e in events:  # torch creates the underlying HIP event on its first record
+        if not e.cuda_event:
+            e.record(st)
+    return (_vp(events[0].cuda_event), _vp(events[1].cuda_event))
+
+
+def markov_draft_loop_from_hidden(hidden, lm_head, base, w1, w2, anchor_tokens, anchor_pos, temperature, seeds, cache,
+                                  draft_tokens, draft_lse=None, workspace=None, stream=None, events=None):
+    """The draft LM head then the K-step draft loop in one call
+    (mds_markov_draft_loop_from_hidden); K = draft_tokens.shape[1].
+
+    hidden bf16 [B*K, H], lm_head bf16 [V, H] as for draft_lm_head; base
+    float32 or bf16 [B, >=K, V] receives the base logits of steps 1..K-1
+    (its step-0 rows are scratch). The rest as for markov_draft_loop.
+    events: optional (begin, end) torch.cuda.Event pair recorded around the
+    call's launches. Returns the workspace used.
+    """
+    import torch
+    B, K = draft_tokens.shape
+    V, H = lm_head.shape
+    _need(hidden.is_cuda and hidden.dtype == torch.bfloat16 and hidden.dim() == 2 and hidden.shape[1] == H
+          and hidden.stride(1) == 1 and hidden.shape[0] == B * K, "hidden must be bf16 [B*K, H] with unit column stride")
+    _need(lm_head.dtype == torch.bfloat16 and lm_head.is_contiguous(), "lm_head must be contiguous bf16 [V, H]")
+    if workspace is None:
+        workspace = new_workspace(draft_workspace_bytes(B, K, V, w1.shape[1]), base.device)
+    args = _draft_args(base, w1, w2, anchor_tokens, anchor_pos, temperature, seeds, cache, draft_tokens, draft_lse,
+                       workspace)
+    ev = _event_ptrs(events, stream, base.device)
+    rc = _lib().mds_markov_draft_loop_from_hidden(*args[:4], H, _ptr(hidden), hidden.stride(0), _ptr(lm_head),
+                                                  *args[4:], _stream(stream, base.device), ev[0], ev[1])
+    _check(rc, "markov_draft_loop_from_hidden")
+    return workspace
 
 
 def rejection_verify_indexed(target, cache, draft_tokens, idx_map, temperature, seeds, anchor_pos, out_tokens,

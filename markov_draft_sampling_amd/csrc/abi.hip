@@ -152,7 +152,7 @@ int draft_impl(int B, int K, int V, int r, const void* base, int base_dtype, int
                const float* temperature, const int64_t* seeds, void* cache, int cache_dtype, int64_t cache_rs,
                int64_t cache_ss, int32_t* draft_tokens, float* draft_lse, void* workspace, size_t ws_bytes,
                void* stream, void* ev_begin, void* ev_end, int* n_launches, const Indexing& ix = Indexing(),
-               uint32_t* status = nullptr) {
+               uint32_t* status = nullptr, const mds::LmHeadArgs* lm = nullptr) {
   int rc;
   if ((rc = check_sizes(B, K, V)) || (rc = check_rank(r)) || (rc = check_indexing(ix))) return rc;
   if (!base || !w1 || !w2 || !anchor || (!anchor_pos && !ix.sample_pos) || !temperature || !seeds || !cache ||
@@ -209,6 +209,10 @@ int draft_impl(int B, int K, int V, int r, const void* base, int base_dtype, int
   if (e != hipSuccess) return hip_fail(e, "device query");
   const bool wave_kernel = r <= 256;
   a.G = wave_kernel ? mds::draft_wave_slabs(V, cus) : mds::draft_slabs(V, cus);
+  a.Gq = a.G;
+  // lm: step 0 runs in the draft LM head's work-groups, one q partial each
+  const int G0 = lm ? mds::lm_head_work_groups(*lm) : a.G;
+  if (G0 > a.Gq) a.Gq = G0;
   // keys in the zero-kept region need no clearing
   if (!L.fixed_keys) {
     if ((e = mds::launch_draft_init(a.keys, K * B, st)) != hipSuccess) return hip_fail(e, "draft init launch");
@@ -216,13 +220,16 @@ int draft_impl(int B, int K, int V, int r, const void* base, int base_dtype, int
   if (ev_begin && (e = hipEventRecord((hipEvent_t)ev_begin, st)) != hipSuccess) return hip_fail(e, "event record");
   for (int k = 0; k < K; ++k) {
     a.k = k;
-    e = wave_kernel ? mds::launch_draft_wave(a, st) : mds::launch_draft_step(a, st);
+    if (k == 0 && lm)
+      e = mds::launch_lm_head(*lm, st, &a);
+    else
+      e = wave_kernel ? mds::launch_draft_wave(a, st) : mds::launch_draft_step(a, st);
     if (e != hipSuccess) return hip_fail(e, "draft step launch");
   }
   if (ev_end && (e = hipEventRecord((hipEvent_t)ev_end, st)) != hipSuccess) return hip_fail(e, "event record");
   if (n_launches) *n_launches = K;
   mds::DraftFinalArgs f{B, K, a.G, a.keys, a.qpart, temperature, draft_tokens, draft_lse,
-                        a.idx_map, a.row_map, a.n_slots, a.n_rows, a.fp64};
+                        a.idx_map, a.row_map, a.n_slots, a.n_rows, a.fp64, G0, a.Gq};
   if ((e = mds::launch_draft_finalize(f, st)) != hipSuccess) return hip_fail(e, "draft finalize launch");
   return ok();
 }
@@ -399,6 +406,40 @@ struct ScratchState {
 std::mutex g_scratch_mu;
 ScratchState g_scratch[kMaxDevices];
 
+// Checks the LM head's arguments and fills a (with the device's CU count).
+int lm_head_args(int B, int K, int V, int H, const void* hidden, int64_t hidden_row_stride, const void* lm_head,
+                 void* out, int out_dtype, int64_t out_req_stride, int64_t out_step_stride, mds::LmHeadArgs& a) {
+  int rc;
+  if ((rc = check_sizes(B, K, V))) return rc;
+  if (H < 256 || H > 65536 || H % 256) return fail(MDS_ERR_UNSUPPORTED, "H must be a multiple of 256 in [256, 65536]");
+  if (!hidden || !lm_head || !out) return fail(MDS_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (out_dtype != MDS_F32 && out_dtype != MDS_BF16) return fail(MDS_ERR_INVALID_ARG, "out dtype must be MDS_F32 or MDS_BF16");
+  if (hidden_row_stride < H || hidden_row_stride % 8)
+    return fail(MDS_ERR_INVALID_ARG, "hidden_row_stride must be >= H and a multiple of 8");
+  if (!aligned(hidden, 16) || !aligned(lm_head, 16))
+    return fail(MDS_ERR_INVALID_ARG, "hidden and lm_head must be 16-byte aligned");
+  if (!rows_disjoint(B, K, V, out_req_stride, out_step_stride))
+    return fail(MDS_ERR_INVALID_ARG, "out strides make rows overlap or are shorter than V");
+  a = mds::LmHeadArgs{};
+  a.M = B * K;
+  a.K = K;
+  a.V = V;
+  a.H = H;
+  a.hidden = (const uint16_t*)hidden;
+  a.hidden_rs = hidden_row_stride;
+  a.lm_head = (const uint16_t*)lm_head;
+  a.out = out;
+  a.out_rs = out_req_stride;
+  a.out_ss = out_step_stride;
+  a.out_bf16 = out_dtype == MDS_BF16;
+  a.vec_out = vec_ok(out, out_dtype, out_req_stride, out_step_stride);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&a.cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "device query");
+  return MDS_OK;
+}
+
 }  // namespace
 
 namespace mds {
@@ -485,39 +526,50 @@ int mds_markov_draft_loop_topk(int B, int K, int V, int r, int topk, const void*
 int mds_draft_lm_head(int B, int K, int V, int H, const void* hidden, int64_t hidden_row_stride, const void* lm_head,
                       void* out, int out_dtype, int64_t out_req_stride, int64_t out_step_stride, void* stream,
                       void* ev_begin, void* ev_end) {
+  mds::LmHeadArgs a;
   int rc;
-  if ((rc = check_sizes(B, K, V))) return rc;
-  if (H < 256 || H > 65536 || H % 256) return fail(MDS_ERR_UNSUPPORTED, "H must be a multiple of 256 in [256, 65536]");
-  if (!hidden || !lm_head || !out) return fail(MDS_ERR_INVALID_ARG, "a required pointer is NULL");
-  if (out_dtype != MDS_F32 && out_dtype != MDS_BF16) return fail(MDS_ERR_INVALID_ARG, "out dtype must be MDS_F32 or MDS_BF16");
-  if (hidden_row_stride < H || hidden_row_stride % 8)
-    return fail(MDS_ERR_INVALID_ARG, "hidden_row_stride must be >= H and a multiple of 8");
-  if (!aligned(hidden, 16) || !aligned(lm_head, 16))
-    return fail(MDS_ERR_INVALID_ARG, "hidden and lm_head must be 16-byte aligned");
-  if (!rows_disjoint(B, K, V, out_req_stride, out_step_stride))
-    return fail(MDS_ERR_INVALID_ARG, "out strides make rows overlap or are shorter than V");
-  mds::LmHeadArgs a{};
-  a.M = B * K;
-  a.K = K;
-  a.V = V;
-  a.H = H;
-  a.hidden = (const uint16_t*)hidden;
-  a.hidden_rs = hidden_row_stride;
-  a.lm_head = (const uint16_t*)lm_head;
-  a.out = out;
-  a.out_rs = out_req_stride;
-  a.out_ss = out_step_stride;
-  a.out_bf16 = out_dtype == MDS_BF16;
-  a.vec_out = vec_ok(out, out_dtype, out_req_stride, out_step_stride);
+  if ((rc = lm_head_args(B, K, V, H, hidden, hidden_row_stride, lm_head, out, out_dtype, out_req_stride,
+                         out_step_stride, a)))
+    return rc;
   hipStream_t st = (hipStream_t)stream;
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&a.cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return hip_fail(e, "device query");
+  hipError_t e;
   if (ev_begin && (e = hipEventRecord((hipEvent_t)ev_begin, st)) != hipSuccess) return hip_fail(e, "event record");
   if ((e = mds::launch_lm_head(a, st)) != hipSuccess) return hip_fail(e, "LM head launch");
   if (ev_end && (e = hipEventRecord((hipEvent_t)ev_end, st)) != hipSuccess) return hip_fail(e, "event record");
   return ok();
+}
+
+int mds_markov_draft_loop_from_hidden(int B, int K, int V, int r, int H, const void* hidden, int64_t hidden_row_stride,
+                                      const void* lm_head, void* base, int base_dtype, int64_t base_req_stride,
+                                      int64_t base_step_stride, const void* w1, const void* w2,
+                                      const int32_t* anchor_tokens, const int64_t* anchor_pos,
+                                      const float* temperature, const int64_t* seeds, void* cache, int cache_dtype,
+                                      int64_t cache_req_stride, int64_t cache_step_stride, int32_t* draft_tokens,
+                                      float* draft_lse, void* workspace, size_t workspace_bytes, void* stream,
+                                      void* ev_begin, void* ev_end) {
+  mds::LmHeadArgs lm;
+  int rc;
+  if ((rc = lm_head_args(B, K, V, H, hidden, hidden_row_stride, lm_head, base, base_dtype, base_req_stride,
+                         base_step_stride, lm)))
+    return rc;
+  // step 0 inside the LM head's work-groups when one M tile holds every row
+  // (B*K <= 256), the step kernel's batch tile holds every request (B <= 32),
+  // the rank takes the streaming step kernel and the LM head's work-groups fit
+  // the q partial slots; otherwise the LM head and the loop run one after
+  // the other
+  const bool fused = B <= 32 && B * K <= 256 && r <= 256 && mds::lm_head_work_groups(lm) <= mds::kDraftMaxSlabs;
+  if (fused)
+    return draft_impl(B, K, V, r, base, base_dtype, base_req_stride, base_step_stride, w1, w2, anchor_tokens,
+                      anchor_pos, temperature, seeds, cache, cache_dtype, cache_req_stride, cache_step_stride,
+                      draft_tokens, draft_lse, workspace, workspace_bytes, stream, ev_begin, ev_end, nullptr,
+                      Indexing(), nullptr, &lm);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  if (ev_begin && (e = hipEventRecord((hipEvent_t)ev_begin, st)) != hipSuccess) return hip_fail(e, "event record");
+  if ((e = mds::launch_lm_head(lm, st)) != hipSuccess) return hip_fail(e, "LM head launch");
+  return draft_impl(B, K, V, r, base, base_dtype, base_req_stride, base_step_stride, w1, w2, anchor_tokens,
+                    anchor_pos, temperature, seeds, cache, cache_dtype, cache_req_stride, cache_step_stride,
+                    draft_tokens, draft_lse, workspace, workspace_bytes, stream, nullptr, ev_end, nullptr);
 }
 
 int mds_verify_workspace_bytes(int B, int K, int V, int has_top_p, int has_draft_lse, size_t* out_bytes) {

@@ -391,7 +391,7 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftStepArgs a) {
     if (draft_slot(a, b) < 0) continue;  // no winner and no partial for rows that are not served
     const unsigned long long key = s_key[i];
     if (key) atomicMax(&a.keys[key_index(k, a.B, b)], key);
-    a.qpart[((size_t)k * a.B + b) * a.G + g] = make_float2(s_qm[i], s_qs[i]);
+    a.qpart[((size_t)k * a.B + b) * a.Gq + g] = make_float2(s_qm[i], s_qs[i]);
   }
 }
 
@@ -422,10 +422,15 @@ __global__ __launch_bounds__(256) void draft_finalize_kernel(DraftFinalArgs a) {
   }
   const float T = a.temp[sl];  // in flight with the partials
   float m = -INFINITY, s = 0.0f;
-  const float2* qp = a.qpart + ((size_t)k * a.B + b) * a.G;
-  for (int i = lane; i < a.G; i += 64) {
-    const float2 p = qp[i];
-    lse_merge(m, s, p.x, p.y);
+  const float2* qp = a.qpart + ((size_t)k * a.B + b) * a.Gq;
+  const int n = k == 0 ? a.G0 : a.G;
+  // four partials a lane in flight at a time (an empty one merges as a no-op)
+  for (int i0 = lane; i0 < n; i0 += 256) {
+    float2 p[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) p[u] = i0 + 64 * u < n ? qp[i0 + 64 * u] : make_float2(-INFINITY, 0.0f);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) lse_merge(m, s, p[u].x, p[u].y);
   }
   wave_lse_merge(m, s);
   if (lane == 0) {

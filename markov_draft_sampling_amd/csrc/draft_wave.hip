@@ -608,7 +608,7 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
       lse_merge(m, s, s_qm[w * NB + i], s_qs[w * NB + i]);
     }
     if (key) atomicMax(&a.keys[key_index(k, a.B, b)], key);
-    a.qpart[((size_t)k * a.B + b) * a.G + g] = make_float2(m, s);
+    a.qpart[((size_t)k * a.B + b) * a.Gq + g] = make_float2(m, s);
   }
 }
 

@@ -38,7 +38,8 @@ struct DraftStepArgs {
   void* cache;
   long long cache_rs, cache_ss;
   unsigned long long* keys;  // [K][B] winner keys at key_index(k, B, b)
-  float2* qpart;             // [K][B][G] (max, sum exp) of cache / T per slab
+  float2* qpart;             // [K][B][Gq] (max, sum exp) of cache / T per slab
+  int Gq;                    // partials per (step, request) row of qpart (>= G)
   uint32_t* status;
   int zero;                  // always 0 (an offset the compiler cannot fold)
   // request-state indexing (all null / B for the plain call)
@@ -50,9 +51,9 @@ struct DraftStepArgs {
 };
 
 struct DraftFinalArgs {
-  int B, K, G;
+  int B, K, G;               // G: q partials of each step after the first
   unsigned long long* keys;  // read, then cleared
-  const float2* qpart;
+  const float2* qpart;       // [K][B][Gq]
   const float* temp;
   int32_t* tokens;
   float* lse;
@@ -60,6 +61,8 @@ struct DraftFinalArgs {
   const int32_t* row_map;
   int n_slots, n_rows;
   int fp64;  // keys in the fp64 format
+  int G0;    // q partials of step 0
+  int Gq;    // partials per (step, request) row of qpart
 };
 
 // The state slot of batch row b at draft step k, or -1 when the row is inert
@@ -142,7 +145,11 @@ struct LmHeadArgs {
   int out_bf16, vec_out;
   int cus;                    // compute units of the device (the launch splits its last partial round)
 };
-hipError_t launch_lm_head(const LmHeadArgs& a, hipStream_t st);
+// step0 non-null: the LM head also runs step 0 of the draft loop (M = B*K
+// <= 256, B <= 32, rank <= 256, the fp32 Gumbel): the step-0 logit rows are not
+// stored, and the q partials of step 0 take lm_head_work_groups(a) slots
+hipError_t launch_lm_head(const LmHeadArgs& a, hipStream_t st, const DraftStepArgs* step0 = nullptr);
+int lm_head_work_groups(const LmHeadArgs& a);
 hipError_t launch_topk_select(const TopkArgs& a, hipStream_t st);
 hipError_t launch_topk_merge(const TopkArgs& a, hipStream_t st);
 hipError_t launch_topk_chain(const TopkArgs& a, hipStream_t st);
