@@ -6,7 +6,10 @@ A step is one pass of the whole hot path over one batch: the K-step Markov
 draft loop (fused projection + sampling + cache write per step) followed by
 rejection verification, on synthetic inputs of the headline workload:
 V=200064, r=256 (w2 = 102 MB bf16), K=7, B=32, fp32 base logits, target and
-draft-logits cache. Inputs are resident in HBM before timing starts.
+draft-logits cache. Inputs are resident in HBM before timing starts. The
+Markov step kernels read w2 in its tiled order (mds_tile_markov_w2, made once
+from the row-major matrix before the first step, as weights are prepared at
+load time; --w2-layout row-major reads the [V, r] matrix itself).
 
 Timing: W untimed steps, then S timed steps. Before each timed step a 512 MiB
 buffer is read so the Infinity Cache (MALL) and L2 hold none of the inputs
@@ -151,6 +154,10 @@ def main():
                          "top-k Markov drafting (--topk candidates per row); lmhead: the draft LM head "
                          "(hidden [B*K, --hidden] x lm_head [V, --hidden]) computes the base logits, then plain; "
                          "lmhead_fused: the same as one call, step 0 inside the LM head's work-groups")
+    ap.add_argument("--w2-layout", choices=("tiled", "row-major"), default="tiled",
+                    help="w2 as read by the dense Markov step kernels of the plain, indexed and fp64 variants: "
+                         "tiled once before the timed steps, or the row-major [V, r] matrix (the LM head and top-k "
+                         "variants read it row-major)")
     ap.add_argument("--hidden", type=int, default=4096, help="hidden size of --variant lmhead")
     ap.add_argument("--topk", type=int, default=64, help="candidates per row of --variant topk")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -206,6 +213,16 @@ def main():
         print(f"# LM head inputs H={a.hidden} generated in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr,
               flush=True)
     spos = (apos[:, None] + 1 + torch.arange(K, device=dev)[None, :]).contiguous()
+    tiled = a.w2_layout == "tiled" and a.variant in ("plain", "indexed", "fp64")
+    w2_step, tile_ms = w2, None
+    if tiled:  # once, as at weight-load time (timed on a second call: the first one loads the kernel)
+        w2_step = mds.tile_markov_w2(w2)
+        t_a, t_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t_a.record(stream)
+        w2_step = mds.tile_markov_w2(w2)
+        t_b.record(stream)
+        torch.cuda.synchronize()
+        tile_ms = t_a.elapsed_time(t_b)
     if a.variant == "indexed":
         # request b lives in slot perm[b] of 2B slots; slot s owns cache row rowmap[s]
         rng = np.random.default_rng(17)
@@ -238,7 +255,7 @@ def main():
             mds.rejection_verify(target, cache, toks, temp, seeds, apos, out, nacc, draft_lse=lse,
                                  top_p=top_p, workspace=ws_v)
             return
-        if a.variant == "plain":
+        if a.variant == "plain" and not tiled:
             if events is None:
                 mds.markov_draft_loop(base, w1, w2, anchor, apos, temp, seeds, cache, toks, lse, workspace=ws_d)
             else:
@@ -256,9 +273,10 @@ def main():
                                  top_p=top_p, workspace=ws_v)
             return
         ix = a.variant == "indexed"
-        r_ = mds.markov_draft_loop_ex(base, w1, w2, anchor, idx_bk if ix else None, spos, s_temp if ix else temp,
-                                      s_seed if ix else seeds, cache, toks, row_mapping=rmap if ix else None,
-                                      draft_lse=lse, fp64_gumbel=a.variant == "fp64", workspace=ws_d, events=events)
+        r_ = mds.markov_draft_loop_ex(base, w1, w2_step, anchor, idx_bk if ix else None, spos,
+                                      s_temp if ix else temp, s_seed if ix else seeds, cache, toks,
+                                      row_mapping=rmap if ix else None, draft_lse=lse,
+                                      fp64_gumbel=a.variant == "fp64", workspace=ws_d, events=events, w2_tiled=tiled)
         if events is not None:
             launches.append(r_[1])
         if ix:
@@ -334,6 +352,7 @@ def main():
         traffic = recorded_traffic("lm_head_kernel_hbm_traffic_V200064_B32.md",
                                    ("lm_head.hip", "mds_device.h", "mds_internal.h"))
     if (B != 32 or a.workload != "headline_v200064" or a.variant not in ("plain", "topk", "lmhead")
+            or (a.variant == "plain" and not tiled)
             or (a.variant == "topk" and a.topk != 64) or (a.variant == "lmhead" and a.hidden != 4096)):
         traffic = None
     status = mds.workspace_status(ws_d) | mds.workspace_status(ws_v)
@@ -361,6 +380,7 @@ def main():
                                "lmhead_fused": f", the draft LM head (H={a.hidden}, bf16) with step 0 fused, "
                                "one call"}[a.variant],
                    "V": V, "r": r, "K": K, "B": B, "variant": a.variant,
+                   "w2_layout": "tiled" if tiled else "row-major",
                    **({"topk": a.topk} if a.variant == "topk" else {}),
                    **({"hidden": a.hidden} if a.variant in ("lmhead", "lmhead_fused") else {}),
                    "cache_flushed_between_steps": not a.no_flush},
@@ -381,6 +401,7 @@ def main():
                      **({"mfma_TFLOPs": 2.0 * B * K * V * a.hidden / (kern_avg_ms * 1e-3) / 1e12,
                          "mfma_peak_TFLOPs": 2500.0} if a.variant == "lmhead" else {})},
         "warm": {"ms_per_step": warm_ms, "value": tokens / (warm_ms * 1e-3)},
+        "w2_tiling_ms": tile_ms,
         "step_ms_p10_p50_p90": [float(np.percentile(step_ms, q)) for q in (10, 50, 90)],
         "draft_kernels_ms": float(np.mean(draft_span_ms)),
         "acceptance_length": acc_len,

@@ -200,6 +200,7 @@ int mds_rejection_verify(int B, int K, int V,
 
 /* flags of mds_markov_draft_loop_ex */
 #define MDS_DRAFT_FP64_GUMBEL 1u /* the API page's use_fp64_gumbel: Gumbel variate and score in float64 */
+#define MDS_DRAFT_W2_TILED 2u    /* w2 given in the tiled order of mds_tile_markov_w2 (r <= 256) */
 
 /*
  * mds_markov_draft_loop_ex - mds_markov_draft_loop with the pages'
@@ -227,6 +228,10 @@ int mds_rejection_verify(int B, int K, int V,
  * z/T + g in float64; the winner is the first NaN, else the first maximum of
  * the float64 scores at a resolution of 2^-28 relative (candidates closer
  * than that go to the lower column); needs r <= 256.
+ * flags: MDS_DRAFT_W2_TILED: w2 points to the output of mds_tile_markov_w2
+ * for (V, r) instead of the row-major [V, r] matrix; the results are those
+ * of the row-major call on the matrix it was made from. Needs r <= 256
+ * (else MDS_ERR_UNSUPPORTED).
  * Workspace and errors as for mds_markov_draft_loop.
  * ev_begin / ev_end (hipEvent_t as void*, or NULL) are recorded on `stream`
  * around the Markov step launches and *n_step_launches (if not NULL) gets
@@ -252,6 +257,32 @@ int mds_markov_draft_loop_ex(int B, int K, int V, int r,
 int mds_draft_topk_workspace_bytes(int B, int K, int V, int r, int topk, size_t* out_bytes);
 
 /*
+ * mds_markov_w2_tiled_bytes / mds_tile_markov_w2 - markov_w2, the Markov
+ * head's [V, r] bias factor (DSparkSpeculator API page, _sample_markov_chain),
+ * stored once in the order in which the Markov step kernel reads it, for
+ * callers that keep the weights resident between calls
+ * (mds_markov_draft_loop_ex with MDS_DRAFT_W2_TILED).
+ *
+ * Tiled order: with T = ceil(V / 16) tiles of 16 rows, element (v, j) of w2
+ * (v < V, j < r) is at index
+ *   (v / 16) * 16 r + (j / 32) * 512 + ((v % 16) + 16 * ((j % 32) / 8)) * 8 + j % 8
+ * of the tiled array (T * 16 * r bf16 elements; the rows v in [V, 16 T) of
+ * the last tile are zero). Each 1 KB block then holds one wave's operand of
+ * one 16-row, 32-rank matrix-core product.
+ *
+ * mds_markov_w2_tiled_bytes: *out_bytes = 32 * r * ceil(V / 16) (host only).
+ * mds_tile_markov_w2: w2 bf16 [V, r] row-major (device), w2_tiled (device,
+ * w2_tiled_bytes >= mds_markov_w2_tiled_bytes, written), both 16-byte
+ * aligned and not overlapping; one kernel on `stream` (hipStream_t as void*).
+ * Errors: V outside [2, 2^24), r not a multiple of 32 in [32, 512], NULL,
+ * misaligned or overlapping pointers or a short w2_tiled give
+ * MDS_ERR_INVALID_ARG / MDS_ERR_UNSUPPORTED as for the draft calls, with
+ * nothing enqueued.
+ */
+int mds_markov_w2_tiled_bytes(int V, int r, size_t* out_bytes);
+int mds_tile_markov_w2(int V, int r, const void* w2, void* w2_tiled, size_t w2_tiled_bytes, void* stream);
+
+/*
  * mds_markov_draft_loop_topk - top-k Markov drafting (DSparkSpeculator API
  * page, _sample_sequential_topk): the draft loop of mds_markov_draft_loop_ex
  * with the Markov bias applied only to each step's topk candidates.
@@ -273,7 +304,8 @@ int mds_draft_topk_workspace_bytes(int B, int K, int V, int r, int topk, size_t*
  *   topk        1 <= topk <= min(256, V), and ceil(V/8192) * topk <= 7168
  *               (else MDS_ERR_INVALID_ARG / MDS_ERR_UNSUPPORTED);
  *   flags       MDS_DRAFT_FP64_GUMBEL: float64 variates and scores, winner
- *               taken exactly over the float64 scores;
+ *               taken exactly over the float64 scores (MDS_DRAFT_W2_TILED is
+ *               not supported here: MDS_ERR_UNSUPPORTED);
  *   workspace   >= mds_draft_topk_workspace_bytes(B, K, V, r, topk) bytes,
  *               256-byte aligned, zeroed when allocated and not written by the
  *               caller between calls (it may be shared with the dense draft

@@ -17,7 +17,8 @@ import os
 
 __all__ = [
     "F32", "BF16", "MdsError", "library_path", "abi_version", "draft_workspace_bytes", "verify_workspace_bytes",
-    "new_workspace", "workspace_status", "verify_slot_offsets", "markov_draft_loop", "markov_draft_loop_noalloc", "markov_draft_loop_timed", "rejection_verify",
+    "new_workspace", "workspace_status", "verify_slot_offsets", "markov_w2_tiled_bytes", "tile_markov_w2",
+    "markov_draft_loop", "markov_draft_loop_noalloc", "markov_draft_loop_timed", "rejection_verify",
     "debug_noise", "debug_gumbel", "debug_top_p", "STATUS_BAD_ANCHOR", "STATUS_BAD_DRAFT", "STATUS_BAD_INDEX", "SALT_DRAFT", "SALT_ACCEPT",
     "SALT_RESAMPLE",
 ]
@@ -25,7 +26,7 @@ __all__ = [
 F32, BF16 = 0, 1
 STATUS_BAD_ANCHOR, STATUS_BAD_DRAFT, STATUS_BAD_INDEX = 1, 2, 8
 SALT_DRAFT, SALT_ACCEPT, SALT_RESAMPLE = 1 << 30, 1, 2
-DRAFT_FP64_GUMBEL = 1
+DRAFT_FP64_GUMBEL, DRAFT_W2_TILED = 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -59,6 +60,8 @@ _SIGS = {
                                                  ctypes.c_uint32, _vp, _c_sz, _vp, _vp, _vp, ctypes.POINTER(_c_int)],
                                  _c_int),
     "mds_draft_topk_workspace_bytes": ([_c_int] * 5 + [ctypes.POINTER(_c_sz)], _c_int),
+    "mds_markov_w2_tiled_bytes": ([_c_int, _c_int, ctypes.POINTER(_c_sz)], _c_int),
+    "mds_tile_markov_w2": ([_c_int, _c_int, _vp, _vp, _c_sz, _vp], _c_int),
     "mds_markov_draft_loop_topk": ([_c_int] * 5 + [_vp, _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _c_int, _vp,
                                                    _vp, _vp, _c_int, _vp, _c_int, _c_i64, _c_i64, _vp, _vp,
                                                    ctypes.c_uint32, _vp, _c_sz, _vp, _vp, _vp], _c_int),
@@ -275,17 +278,37 @@ def rejection_verify(target, cache, draft_tokens, temperature, seeds, anchor_pos
     return workspace
 
 
+def markov_w2_tiled_bytes(V: int, r: int) -> int:
+    out = _c_sz()
+    _check(_lib().mds_markov_w2_tiled_bytes(V, r, ctypes.byref(out)), "markov_w2_tiled_bytes")
+    return out.value
+
+
+def tile_markov_w2(w2, stream=None):
+    """w2 bf16 [V, r] -> a new bf16 [ceil(V/16), 16*r] tensor holding it in the
+    tiled order of mds_tile_markov_w2 (for markov_draft_loop_ex(w2_tiled=True))."""
+    import torch
+    _need(w2.is_cuda and w2.dtype == torch.bfloat16 and w2.dim() == 2 and w2.is_contiguous(),
+          "w2 must be a contiguous bf16 [V, r] GPU tensor")
+    V, r = w2.shape
+    n = markov_w2_tiled_bytes(V, r) // 2
+    out = torch.empty((n // (16 * r), 16 * r), dtype=torch.bfloat16, device=w2.device)
+    _check(_lib().mds_tile_markov_w2(V, r, _ptr(w2), _ptr(out), 2 * n, _stream(stream, w2.device)), "tile_markov_w2")
+    return out
+
+
 def markov_draft_loop_ex(base, w1, w2, anchor_tokens, idx_map, sample_pos, temperature, seeds, cache, draft_tokens,
                          row_mapping=None, draft_lse=None, fp64_gumbel=False, workspace=None, stream=None,
-                         events=None):
+                         events=None, w2_tiled=False):
     """Draft loop with request-state indexing and options (mds_markov_draft_loop_ex).
 
     idx_map int32 [B, K] (state slot per row and step, < 0 inert) or None
     (slot = batch row), sample_pos int64 [B, K] (predicted position P; the
     draw is keyed by P - 1), temperature / seeds [n_slots], row_mapping int32
     [n_slots] or None, cache [n_cache_rows, K, V]; fp64_gumbel: float64 Gumbel
-    variates and scores. base, anchor_tokens, draft_tokens, draft_lse are
-    batch-indexed. events: optional (begin, end) torch.cuda.Event pair
+    variates and scores; w2_tiled: w2 is tile_markov_w2's output for the
+    [V, r] matrix (w1 [V, r] gives r). base, anchor_tokens, draft_tokens,
+    draft_lse are batch-indexed. events: optional (begin, end) torch.cuda.Event pair
     recorded around the Markov step launches; then returns (workspace, number
     of launches).
     """
@@ -297,7 +320,12 @@ def markov_draft_loop_ex(base, w1, w2, anchor_tokens, idx_map, sample_pos, tempe
     _need(cache.dim() == 3 and cache.shape[1] == K and cache.shape[2] == V and cache.stride(2) == 1,
           "cache must be [n_cache_rows, K, V] with unit column stride")
     _need(w1.dtype == torch.bfloat16 and w2.dtype == torch.bfloat16 and w1.is_contiguous() and w2.is_contiguous()
-          and w1.shape == w2.shape and w1.shape[0] == V, "w1 and w2 must be contiguous bf16 [V, r]")
+          and w1.dim() == 2 and w1.shape[0] == V, "w1 and w2 must be contiguous bf16, w1 [V, r]")
+    r = w1.shape[1]
+    if w2_tiled:
+        _need(tuple(w2.shape) == ((V + 15) // 16, 16 * r), "tiled w2 must be tile_markov_w2's [ceil(V/16), 16 r]")
+    else:
+        _need(w2.shape == w1.shape, "w2 must be [V, r]")
     _need(anchor_tokens.dtype == torch.int32 and anchor_tokens.numel() == B and anchor_tokens.is_contiguous(),
           "anchor_tokens must be int32 [B]")
     if idx_map is not None:
@@ -330,7 +358,8 @@ def markov_draft_loop_ex(base, w1, w2, anchor_tokens, idx_map, sample_pos, tempe
         B, K, V, w1.shape[1], _ptr(base), _dtype_code(base), base.stride(0), base.stride(1), _ptr(w1), _ptr(w2),
         _ptr(anchor_tokens), _ptr(idx_map), _ptr(sample_pos), n_slots, _ptr(temperature), _ptr(seeds),
         _ptr(row_mapping), cache.shape[0], _ptr(cache), _dtype_code(cache), cache.stride(0), cache.stride(1),
-        _ptr(draft_tokens), _ptr(draft_lse), DRAFT_FP64_GUMBEL if fp64_gumbel else 0, _ptr(workspace),
+        _ptr(draft_tokens), _ptr(draft_lse), (DRAFT_FP64_GUMBEL if fp64_gumbel else 0) | (DRAFT_W2_TILED if w2_tiled
+                                                                                           else 0), _ptr(workspace),
         workspace.numel(), _stream(stream, base.device), ev[0], ev[1], ctypes.byref(n))
     _check(rc, "markov_draft_loop_ex")
     return (workspace, n.value) if events is not None else workspace

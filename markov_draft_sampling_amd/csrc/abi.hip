@@ -141,7 +141,7 @@ struct Indexing {
 };
 
 int check_indexing(const Indexing& ix) {
-  if (ix.flags & ~MDS_DRAFT_FP64_GUMBEL) return fail(MDS_ERR_INVALID_ARG, "unknown flag bits");
+  if (ix.flags & ~(MDS_DRAFT_FP64_GUMBEL | MDS_DRAFT_W2_TILED)) return fail(MDS_ERR_INVALID_ARG, "unknown flag bits");
   if (!ix.idx_map) return MDS_OK;
   if (ix.n_slots < 1 || ix.n_rows < 1) return fail(MDS_ERR_INVALID_ARG, "n_slots and n_cache_rows must be >= 1");
   return MDS_OK;
@@ -166,6 +166,8 @@ int draft_impl(int B, int K, int V, int r, const void* base, int base_dtype, int
     return fail(MDS_ERR_INVALID_ARG, "cache strides make rows overlap or are shorter than V");
   const bool fp64 = (ix.flags & MDS_DRAFT_FP64_GUMBEL) != 0;
   if (fp64 && r > 256) return fail(MDS_ERR_UNSUPPORTED, "the fp64 Gumbel option needs r <= 256");
+  const bool tiled = (ix.flags & MDS_DRAFT_W2_TILED) != 0;
+  if (tiled && r > 256) return fail(MDS_ERR_UNSUPPORTED, "tiled w2 needs r <= 256");
   if (!aligned(w1, 16) || !aligned(w2, 16)) return fail(MDS_ERR_INVALID_ARG, "w1 and w2 must be 16-byte aligned");
   if (!aligned(workspace, kAlign)) return fail(MDS_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   const DraftLayout L = draft_layout(B, K, V);
@@ -203,6 +205,7 @@ int draft_impl(int B, int K, int V, int r, const void* base, int base_dtype, int
   a.n_slots = ix.idx_map ? ix.n_slots : B;
   a.n_rows = n_rows;
   a.fp64 = fp64;
+  a.w2_tiled = tiled;
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -329,6 +332,7 @@ int topk_impl(int B, int K, int V, int r, int topk, const void* base, int base_d
   if ((rc = check_sizes(B, K, V)) || (rc = check_rank(r)) || (rc = check_indexing(ix)) ||
       (rc = check_topk(B, K, V, topk)))
     return rc;
+  if (ix.flags & MDS_DRAFT_W2_TILED) return fail(MDS_ERR_UNSUPPORTED, "top-k drafting reads row-major w2");
   if (!base || !w1 || !w2 || !anchor || !ix.sample_pos || !temperature || !seeds || !cache || !draft_tokens ||
       !workspace)
     return fail(MDS_ERR_INVALID_ARG, "a required pointer is NULL");
@@ -490,6 +494,28 @@ int mds_draft_workspace_bytes(int B, int K, int V, int r, size_t* out_bytes) {
   if ((rc = check_sizes(B, K, V)) || (rc = check_rank(r))) return rc;
   if (!out_bytes) return fail(MDS_ERR_INVALID_ARG, "out_bytes is NULL");
   *out_bytes = draft_layout(B, K, V).total;
+  return ok();
+}
+
+int mds_markov_w2_tiled_bytes(int V, int r, size_t* out_bytes) {
+  int rc;
+  if ((rc = check_sizes(1, 1, V)) || (rc = check_rank(r))) return rc;
+  if (!out_bytes) return fail(MDS_ERR_INVALID_ARG, "out_bytes is NULL");
+  *out_bytes = mds::w2_tiled_elems(V, r) * 2;
+  return ok();
+}
+
+int mds_tile_markov_w2(int V, int r, const void* w2, void* w2_tiled, size_t w2_tiled_bytes, void* stream) {
+  int rc;
+  if ((rc = check_sizes(1, 1, V)) || (rc = check_rank(r))) return rc;
+  if (!w2 || !w2_tiled) return fail(MDS_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned(w2, 16) || !aligned(w2_tiled, 16)) return fail(MDS_ERR_INVALID_ARG, "w2 and w2_tiled must be 16-byte aligned");
+  const size_t need = mds::w2_tiled_elems(V, r) * 2;
+  if (w2_tiled_bytes < need) return fail(MDS_ERR_INVALID_ARG, "w2_tiled is smaller than mds_markov_w2_tiled_bytes");
+  const uintptr_t i0 = (uintptr_t)w2, i1 = i0 + (size_t)V * r * 2, o0 = (uintptr_t)w2_tiled, o1 = o0 + need;
+  if (i0 < o1 && o0 < i1) return fail(MDS_ERR_INVALID_ARG, "w2 and w2_tiled overlap");
+  const hipError_t e = mds::launch_tile_w2((const uint16_t*)w2, (uint16_t*)w2_tiled, V, r, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "tile launch");
   return ok();
 }
 

@@ -95,24 +95,35 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
     rcache[nt] = (long long)(valid[nt] ? draft_cache_row(a, b, sl) : 0) * a.cache_rs + (long long)k * a.cache_ss;
   }
 
-  // Tile loaders. w2 rows past V are read from row V - 1: they only feed
-  // bias columns past V, which the epilogue never uses. No select touches
-  // the loaded data, so the next tile's loads stay in flight.
-  auto load_a = [&](int t, u32x4 (&A)[kRKMax]) {
+  // Tile loaders. Row-major w2: a load covers 64 bytes of each of 16 rows,
+  // and rows past V are read from row V - 1 (they only feed bias columns
+  // past V, which the epilogue never uses). Tiled w2 (tile_w2_kernel): the
+  // same operands in load order, so a load covers 1 KB of one tile, and the
+  // last tile is padded. No select touches the loaded data, so the next
+  // tile's loads stay in flight.
+  const bool tiled = a.w2_tiled != 0;
+  const int sstep = tiled ? 512 : 32;  // elements from one rank slice to the next
+  auto a_lane = [&](int t) {
     const int v = t * 16 + lr;
-    const uint16_t* p = a.w2 + (size_t)(v < V ? v : V - 1) * r + lg * 8;
-    // all kRKMax slices, past the rank clamped to its last slice (same
-    // lines, no extra traffic): a fixed number of loads per tile lets the
-    // compiler wait for exactly the tile in use, not for the one in flight
-#pragma unroll
-    for (int s = 0; s < kRKMax; ++s) A[s] = *(const u32x4*)(p + (s < RK ? s : RK - 1) * 32);
+    return tiled ? a.w2 + (size_t)t * 16 * r + lane * 8 : a.w2 + (size_t)(v < V ? v : V - 1) * r + lg * 8;
   };
-  // rank r = 32 kRKMax: every slice is real, the offsets are constants
-  auto load_a_full = [&](int t, u32x4 (&A)[kRKMax]) {
-    const int v = t * 16 + lr;
-    const uint16_t* p = a.w2 + (size_t)(v < V ? v : V - 1) * r + lg * 8;
+  auto load_a = [&](int t, u32x4 (&A)[kRKMax]) {
+    const uint16_t* p = a_lane(t);
 #pragma unroll
-    for (int s = 0; s < kRKMax; ++s) A[s] = *(const u32x4*)(p + s * 32);
+    for (int s = 0; s < kRKMax; ++s) A[s] = *(const u32x4*)(p + (s < RK ? s : RK - 1) * sstep);
+  };
+  // The fast loop's loader, with the layout a constant (the slice offsets
+  // then fold into the load instructions); FULL: rank r = 32 kRKMax, every
+  // slice real.
+  auto load_a_fixed = [&](auto tiled_tag, auto full_tag, int t, u32x4 (&A)[kRKMax]) {
+    constexpr bool TL = decltype(tiled_tag)::value;
+    constexpr bool FULL = decltype(full_tag)::value;
+    constexpr int SS = TL ? 512 : 32;
+    const int v = t * 16 + lr;
+    const uint16_t* p = TL ? a.w2 + (size_t)t * 16 * (FULL ? 32 * kRKMax : r) + lane * 8
+                           : a.w2 + (size_t)(v < V ? v : V - 1) * (FULL ? 32 * kRKMax : r) + lg * 8;
+#pragma unroll
+    for (int s = 0; s < kRKMax; ++s) A[s] = *(const u32x4*)(p + (FULL ? s : (s < RK ? s : RK - 1)) * SS);
   };
   auto load_base_vec = [&](int t, float (&bz)[NT][4]) {
     const int c = t * 16 + lg * 4;
@@ -316,14 +327,8 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
     // to arrive. The loop is unrolled over the ring (no register copies,
     // which would wait for the loads) and runs whole turns only; the last
     // partial turn computes the entries already loaded.
-    auto run_fast = [&](auto t1_tag, auto full_tag, auto mask_tag) {
-      constexpr bool FULL = decltype(full_tag)::value;
-      auto load = [&](int tt, u32x4 (&Ab)[kRKMax]) {
-        if (FULL)
-          load_a_full(tt, Ab);
-        else
-          load_a(tt, Ab);
-      };
+    auto run_fast = [&](auto t1_tag, auto full_tag, auto mask_tag, auto tiled_tag) {
+      auto load = [&](int tt, u32x4 (&Ab)[kRKMax]) { load_a_fixed(tiled_tag, full_tag, tt, Ab); };
       int t = t_first;
       if (t < full_end) {
         const int t_lastf = t_first + ((full_end - 1 - t_first) / 4) * 4;
@@ -357,15 +362,18 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
     };
     using True = std::integral_constant<bool, true>;
     using False = std::integral_constant<bool, false>;
+    auto fast = [&](auto t1_tag, auto full_tag, auto mask_tag) {  // the w2 layout a constant of the loop
+      return tiled ? run_fast(t1_tag, full_tag, mask_tag, True()) : run_fast(t1_tag, full_tag, mask_tag, False());
+    };
     bool all_valid = true;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) all_valid &= valid[nt];
     if (!__all(all_valid))  // padding rows (small batches): one general instance (the division by T = 1 is exact)
-      t_gen = run_fast(False(), False(), True());
+      t_gen = fast(False(), False(), True());
     else if (RK == kRKMax)
-      t_gen = t1 ? run_fast(True(), True(), False()) : run_fast(False(), True(), False());
+      t_gen = t1 ? fast(True(), True(), False()) : fast(False(), True(), False());
     else
-      t_gen = t1 ? run_fast(True(), False(), False()) : run_fast(False(), False(), False());
+      t_gen = t1 ? fast(True(), False(), False()) : fast(False(), False(), False());
     if (V & 15) {  // some work-group has a partial last tile: the general loop reads the embeddings from LDS
       if (wave == 0) {
 #pragma unroll
@@ -632,7 +640,33 @@ hipError_t launch_wave_nb(const DraftStepArgs& a, int bt, hipStream_t st) {
   return a.cache_bf16 ? launch_wave<NB, false, true, F64>(a, bt, st) : launch_wave<NB, false, false, F64>(a, bt, st);
 }
 
+// The tiled order of w2 that the step kernel reads with 1 KB loads. Tile t
+// (rows 16 t .. 16 t + 15) takes 16 r consecutive elements; in it, rank
+// slice s (elements 32 s .. 32 s + 31) takes 512, and the 8 elements at
+// 8 l hold elements 32 s + 8 g .. + 7 of row 16 t + m, l = m + 16 g: lane
+// l's piece of the A operand of the 16x16x32 MFMA for that slice. Rows past
+// V are zero. One thread per 16-byte piece.
+__global__ __launch_bounds__(256) void tile_w2_kernel(const uint16_t* __restrict__ w2, uint16_t* __restrict__ out,
+                                                      int V, int r, long long n) {
+  const long long c = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (c >= n) return;
+  const int per_tile = 2 * r;  // 16-byte pieces per tile
+  const long long t = c / per_tile;
+  const int q = (int)(c - t * per_tile);
+  const int l = q & 63;
+  const long long v = t * 16 + (l & 15);
+  u32x4 x = {0u, 0u, 0u, 0u};
+  if (v < V) x = *(const u32x4*)(w2 + v * r + 32 * (q >> 6) + 8 * (l >> 4));
+  *(u32x4*)(out + c * 8) = x;
+}
+
 }  // namespace
+
+hipError_t launch_tile_w2(const uint16_t* w2, uint16_t* out, int V, int r, hipStream_t st) {
+  const long long n = (long long)w2_tiled_elems(V, r) / 8;
+  hipLaunchKernelGGL(tile_w2_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, w2, out, V, r, n);
+  return hipGetLastError();
+}
 
 size_t draft_wave_lds(int NB, int r) {
   return (size_t)NB * (r + 8) * 2 + (size_t)NB * 4 + (size_t)4 * NB * 8 + (size_t)8 * NB * 4;

@@ -48,6 +48,7 @@ struct DraftStepArgs {
   const long long* sample_pos;  // [B][K] predicted position P (draw keyed by P - 1); null: anchor_pos + k
   int n_slots, n_rows;
   int fp64;                  // fp64 Gumbel option: float64 scores, 64-bit keys of the fp64 format
+  int w2_tiled;              // w2 in the 16-row tile order of tile_w2_kernel (step kernels for r <= 256 only)
 };
 
 struct DraftFinalArgs {
@@ -101,6 +102,10 @@ hipError_t launch_draft_step(const DraftStepArgs& a, hipStream_t st);
 // Wave-independent streaming step (rank <= 256); hipErrorNotSupported
 // (nothing launched) for a larger rank.
 size_t draft_wave_lds(int NB, int r);
+// w2 [V, r] row-major -> the tiled order the step kernels read with 1 KB loads
+// (w2_tiled_elems(V, r) bf16 elements, rows past V zero)
+__host__ __forceinline__ size_t w2_tiled_elems(int V, int r) { return (size_t)((V + 15) / 16) * 16 * r; }
+hipError_t launch_tile_w2(const uint16_t* w2, uint16_t* out, int V, int r, hipStream_t st);
 hipError_t launch_draft_wave(const DraftStepArgs& a, hipStream_t st);
 hipError_t launch_draft_finalize(const DraftFinalArgs& a, hipStream_t st);
 

@@ -125,3 +125,39 @@ def test_verify_counter_block_layout():
     assert np.array_equal(line, np.arange(n) % 2048)
     with pytest.raises(mds.MdsError, match="invalid argument"):
         mds.verify_slot_offsets(65535)
+
+
+def test_tiled_w2_size_and_host_validation():
+    import markov_draft_sampling_amd as mds
+    # 32 r bytes per 16-row tile, the last tile padded
+    assert mds.markov_w2_tiled_bytes(200064, 256) == 12504 * 16 * 256 * 2
+    assert mds.markov_w2_tiled_bytes(33001, 256) == 2063 * 16 * 256 * 2
+    assert mds.markov_w2_tiled_bytes(17, 512) == 2 * 16 * 512 * 2
+    with pytest.raises(mds.MdsError, match="invalid argument"):
+        mds.markov_w2_tiled_bytes(1, 256)
+    with pytest.raises(mds.MdsError, match="unsupported"):
+        mds.markov_w2_tiled_bytes(1000, 48)
+    f = mds._lib().mds_tile_markov_w2
+    fake, need = 1 << 24, 63 * 16 * 64 * 2  # addresses never dereferenced: validation fails first
+    assert f(1000, 64, None, fake, need, None) == -1
+    assert f(1000, 64, fake + 8, fake + (1 << 22), need, None) == -1  # misaligned
+    assert f(1000, 64, fake, fake + (1 << 22), need - 16, None) == -1  # too short
+    assert f(1000, 64, fake, fake + 1000 * 64, need, None) == -1  # overlaps w2
+
+
+def test_tiled_w2_flag_limits_on_the_host():
+    import markov_draft_sampling_amd as mds
+    lib = mds._lib()
+    fake = 1 << 24
+    B, K, V = 2, 3, 1000
+    # _ex: tiled w2 with rank 512 is unsupported (checked before any device work)
+    args = [B, K, V, 512, fake, mds.F32, K * V, V, fake, fake, fake, None, fake, B, fake, fake, None, B, fake,
+            mds.F32, K * V, V, fake, None, mds.DRAFT_W2_TILED, fake, 1 << 30, None, None, None, None]
+    assert lib.mds_markov_draft_loop_ex(*args) == -2
+    args[24] = 4  # unknown flag bit
+    assert lib.mds_markov_draft_loop_ex(*args) == -1
+    # top-k drafting reads row-major w2 only
+    targs = [B, K, V, 256, 8] + args[4:]
+    targs[5 + 24 - 4] = mds.DRAFT_W2_TILED
+    targs = targs[:-1]  # no launch-count argument
+    assert lib.mds_markov_draft_loop_topk(*targs) == -2
