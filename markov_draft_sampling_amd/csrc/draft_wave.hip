@@ -71,6 +71,21 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
   const int mt_begin = (int)(((long long)g * a.nMT) / a.G);
   const int mt_end = (int)(((long long)(g + 1) * a.nMT) / a.G);
 
+  // The previous tokens of the lane's requests, for the fast path: their
+  // loads depend on nothing, so they go out ahead of the per-request
+  // parameters and the two round trips overlap (the tokens, and then the
+  // embedding rows, are the kernel's dependent chain).
+  unsigned long long tkw[NT];
+  if (FL) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int b = b0 + nt * 16 + lr;
+      const int bb = b < a.B ? b : a.B - 1;
+      tkw[nt] = (k == 0) ? (unsigned long long)(long long)a.anchor[bb] : a.keys[key_index(k - 1, a.B, bb)];
+    }
+    asm volatile("" ::: "memory");
+  }
+
   // the requests this lane serves: 16 nt + lr of the batch tile
   bool valid[NT];
   float Tv[NT], invT[NT];
@@ -218,20 +233,18 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
   // the general loop below.
   int t_gen = t_first;
   if (FL && fast_req && a.vec_base) {
-    // Direct path. Each wave reads the previous tokens of its lanes' requests
-    // and their embedding rows straight into MFMA B operands (request
-    // 16 nt + lr, rank elements 8 lg + 32 s of slice s): the tokens first,
-    // then the rows, then the first tiles. Loads complete in issue order, so
-    // nothing is queued ahead of this two-load chain, and no work-group
-    // barrier waits for it.
+    // Direct path. Each wave reads the embedding rows of its lanes'
+    // requests' previous tokens (loaded at the start) straight into MFMA B
+    // operands (request 16 nt + lr, rank elements 8 lg + 32 s of slice s),
+    // then the first tiles. Loads complete in issue order, so nothing is
+    // queued ahead of this dependent chain, and no work-group barrier waits
+    // for it.
     int pv[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       // rows that are not served read a request's token (an address inside
       // the arrays) and keep a zero token without a status bit
-      const int b = b0 + nt * 16 + lr;
-      const int bb = b < a.B ? b : a.B - 1;
-      long long tk = (k == 0) ? (long long)a.anchor[bb] : (long long)key_col(a.keys[key_index(k - 1, a.B, bb)], F64);
+      long long tk = (k == 0) ? (long long)tkw[nt] : (long long)key_col(tkw[nt], F64);
       if (tk < 0 || tk >= V) {
         if (valid[nt]) set_status(a.status, kStatusBadAnchor);
         tk = 0;
