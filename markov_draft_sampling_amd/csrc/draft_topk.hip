@@ -130,11 +130,53 @@ __device__ __forceinline__ int slot_cache_row(const TopkArgs& a, int b, int s) {
   return !a.idx_map ? b : (a.row_map ? a.row_map[s] : s);
 }
 
+// Lane i's copy of lane i ^ m's word: DPP quad permutations for m = 1, 2,
+// the LDS swizzle's bit mode (within 32 lanes) for m = 4..16, a permute for 32.
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v, int m) {
+  if (m == 1) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
+  if (m == 2) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
+  if (m == 4) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (4 << 10));
+  if (m == 8) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (8 << 10));
+  if (m == 16) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (16 << 10));
+  return (uint32_t)__shfl_xor((int)v, m);
+}
+
+// The 64 keys of a wave in decreasing order over the lanes (lane i: the
+// (i+1)-th largest), by a bitonic network of lane exchanges.
+__device__ __forceinline__ unsigned long long wave_sort_desc(unsigned long long x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const unsigned long long y =
+          ((unsigned long long)lane_xor((uint32_t)(x >> 32), stride) << 32) | lane_xor((uint32_t)x, stride);
+      // runs of `size` lanes alternate direction, the last one decreasing;
+      // the lower lane of a pair keeps the smaller key in an increasing run
+      const bool keep_min = ((lane & stride) == 0) == ((lane & size) != 0);
+      x = keep_min ? (y < x ? y : x) : (y > x ? y : x);
+    }
+  }
+  return x;
+}
+
+// Keys of a decreasing list of 64 greater than x.
+__device__ __forceinline__ int count_above(const unsigned long long* list, unsigned long long x) {
+  int pos = list[63] > x ? 64 : 0;
+#pragma unroll
+  for (int step = 32; step >= 1; step >>= 1)
+    if (pos < 64 && list[pos + step - 1] > x) pos += step;
+  return pos;
+}
+
 // ------------------------------------------------- 1. chunk selection --
 // Thread t holds columns c0 + 1024 j + 4 t + i (j < 8, i < 4). The k-th
 // largest of the 256 per-thread maxima, t0, is a lower bound of the chunk's
 // k-th largest key, and only the k threads whose maximum reaches t0 can hold
-// keys >= t0: at most 32 k survivors go to LDS for the exact selection.
+// keys >= t0: at most 32 k survivors go to LDS for the exact selection. A
+// thread's maximum is t0 when exactly k - 1 maxima exceed it (the keys are
+// distinct): each wave sorts its 64 maxima, and every thread counts the
+// larger ones by binary search in the four sorted lists.
 template <bool BBF16, bool CBF16>
 __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(TopkArgs a) {
   extern __shared__ unsigned long long s_keys[];  // [32 * topk]
@@ -174,13 +216,11 @@ __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(TopkArgs a) {
     const unsigned long long key = c < V ? win_key(v[j], (uint32_t)c) : 0ull;
     tmax = key > tmax ? key : tmax;
   }
-  s_tmax[tid] = tmax;
+  s_tmax[tid] = wave_sort_desc(tmax);  // wave w's maxima, decreasing, at s_tmax[64 w ..]
   __syncthreads();
   int above = 0;  // thread maxima larger than this thread's
-  for (int u = 0; u < kThreads; u += 2) {
-    const unsigned long long x0 = s_tmax[u], x1 = s_tmax[u + 1];
-    above += (x0 > tmax) + (x1 > tmax);
-  }
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) above += count_above(s_tmax + 64 * w, tmax);
   if (tmax != 0ull && above == a.topk - 1) s_t0 = tmax;  // distinct nonzero keys: one writer at most
   __syncthreads();
   const unsigned long long t0 = s_t0 ? s_t0 : 1ull;

@@ -96,6 +96,25 @@ def test_topk_ties_nan_and_inf_rows():
     assert np.isfinite(cache[4, 0, :16]).all() and (cache[4, 0, 16:] == -np.inf).all()
 
 
+@pytest.mark.parametrize("topk", [16, 64, 256])
+def test_topk_chunk_survivor_paths(topk):
+    # Per 8192-column chunk, the survivors of the thread-maximum bound: few
+    # (random chunks, ~70 for k = 64), many (chunk 0 of row (0, 0): 63
+    # threads whose 32 values all lie above the bound, 2017 survivors),
+    # equal values over 64 threads, a chunk decreasing with the column, and
+    # the ragged tail chunk.
+    V = 3 * 8192 + 100
+    wl = workloads.make_custom(V, 64, 2, 3, seed=topk)
+    cols = np.arange(8192)
+    thread = (cols % 1024) // 4
+    base = wl.base
+    base[0, 0, :8192] = np.where(thread < 64, 1000.0 - thread, -1000.0)
+    base[1, 1, 2 * 8192:3 * 8192] = np.linspace(50.0, -50.0, 8192, dtype=np.float32)
+    base[2, 0, :8192] = np.where(thread < 64, 7.0, -7.0)  # equal values: the lower column ranks first
+    d = _run(wl, topk)
+    _check(wl, d, topk)
+
+
 def test_topk_fp64_gumbel():
     wl = workloads.make_workload("boosted_v32000", B=6)
     d = _run(wl, 50, fp64=True)
