@@ -215,11 +215,11 @@ def main():
     spos = (apos[:, None] + 1 + torch.arange(K, device=dev)[None, :]).contiguous()
     tiled = a.w2_layout == "tiled" and a.variant in ("plain", "indexed", "fp64")
     w2_step, tile_ms = w2, None
-    if tiled:  # once, as at weight-load time (timed on a second call: the first one loads the kernel)
+    if tiled:  # once, as at weight-load time (timed on a second call into the same buffer)
         w2_step = mds.tile_markov_w2(w2)
         t_a, t_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t_a.record(stream)
-        w2_step = mds.tile_markov_w2(w2)
+        mds.tile_markov_w2(w2, out=w2_step)
         t_b.record(stream)
         torch.cuda.synchronize()
         tile_ms = t_a.elapsed_time(t_b)

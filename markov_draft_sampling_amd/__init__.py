@@ -284,15 +284,19 @@ def markov_w2_tiled_bytes(V: int, r: int) -> int:
     return out.value
 
 
-def tile_markov_w2(w2, stream=None):
-    """w2 bf16 [V, r] -> a new bf16 [ceil(V/16), 16*r] tensor holding it in the
-    tiled order of mds_tile_markov_w2 (for markov_draft_loop_ex(w2_tiled=True))."""
+def tile_markov_w2(w2, out=None, stream=None):
+    """w2 bf16 [V, r] -> bf16 [ceil(V/16), 16*r] holding it in the tiled order
+    of mds_tile_markov_w2 (for markov_draft_loop_ex(w2_tiled=True)), written
+    into `out` when given, else into a new tensor; returns it."""
     import torch
     _need(w2.is_cuda and w2.dtype == torch.bfloat16 and w2.dim() == 2 and w2.is_contiguous(),
           "w2 must be a contiguous bf16 [V, r] GPU tensor")
     V, r = w2.shape
     n = markov_w2_tiled_bytes(V, r) // 2
-    out = torch.empty((n // (16 * r), 16 * r), dtype=torch.bfloat16, device=w2.device)
+    if out is None:
+        out = torch.empty((n // (16 * r), 16 * r), dtype=torch.bfloat16, device=w2.device)
+    _need(out.dtype == torch.bfloat16 and out.is_contiguous() and tuple(out.shape) == (n // (16 * r), 16 * r),
+          "out must be a contiguous bf16 [ceil(V/16), 16 r] tensor")
     _check(_lib().mds_tile_markov_w2(V, r, _ptr(w2), _ptr(out), 2 * n, _stream(stream, w2.device)), "tile_markov_w2")
     return out
 

@@ -34,15 +34,20 @@ def test_tiled_order_follows_the_index_formula(V, r):
     print(f"tile w2: V={V} r={r}", flush=True)
     rng = np.random.default_rng([V, r])
     w2 = rng.integers(0, 1 << 16, (V, r), dtype=np.uint16)  # bit patterns: the tiling only moves them
-    got = mds.tile_markov_w2(_bf16(w2))
-    torch.cuda.synchronize()
+    w2d = _bf16(w2)
+    got = mds.tile_markov_w2(w2d)
     T = -(-V // 16)
     assert tuple(got.shape) == (T, 16 * r)
+    # into a given buffer holding other values: every element, padding included, is written
+    buf = torch.full((T, 16 * r), 7.0, dtype=torch.bfloat16, device="cuda")
+    assert mds.tile_markov_w2(w2d, out=buf) is buf
+    torch.cuda.synchronize()
     # element (v, j) at t*16r + s*512 + (m + 16 g)*8 + e with v = 16 t + m, j = 32 s + 8 g + e
     padded = np.zeros((T * 16, r), np.uint16)
     padded[:V] = w2
     want = padded.reshape(T, 16, r // 32, 4, 8).transpose(0, 2, 3, 1, 4).reshape(T, 16 * r)
-    assert np.array_equal(got.view(torch.int16).cpu().numpy().view(np.uint16), want)
+    for t in (got, buf):
+        assert np.array_equal(t.view(torch.int16).cpu().numpy().view(np.uint16), want)
 
 
 def _run_both(wl, temp=None, fp64=False, indexed=False):
