@@ -211,7 +211,8 @@ int draft_impl(int B, int K, int V, int r, const void* base, int base_dtype, int
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return hip_fail(e, "device query");
   const bool wave_kernel = r <= 256;
-  a.G = wave_kernel ? mds::draft_wave_slabs(V, cus) : mds::draft_slabs(V, cus);
+  const int nb = mds::draft_nb(B, r);
+  a.G = wave_kernel ? mds::draft_wave_slabs(V, cus, (B + nb - 1) / nb) : mds::draft_slabs(V, cus);
   a.Gq = a.G;
   // lm: step 0 runs in the draft LM head's work-groups, one q partial each
   const int G0 = lm ? mds::lm_head_work_groups(*lm) : a.G;
@@ -460,11 +461,14 @@ int draft_slabs(int V, int cus) {
 }
 
 // Wave-independent kernel: one work-group per CU (measured best against two
-// per CU for the V = 200064, B = 32 step), at least 8 tiles per slab.
-int draft_wave_slabs(int V, int cus) {
+// per CU for the V = 200064, B = 32 step), at least 8 tiles per slab. With up
+// to kDraftFastTiles batch tiles the slabs of all tiles together fill the CUs
+// once (V = 200064: B = 128 as 64 slabs x 4 tiles, 92 against 102 us per
+// launch for 256 x 4 two per CU; B = 96 as 80 x 3, 75 against 83 us).
+int draft_wave_slabs(int V, int cus, int bt) {
   const int nMT = (V + 15) / 16;
   int G = (nMT + kDraftMinTilesPerSlab - 1) / kDraftMinTilesPerSlab;
-  const int cap = cus > 0 ? cus : kDraftMaxSlabs;
+  const int cap = cus > 0 ? cus / (bt <= kDraftFastTiles ? bt : 1) : kDraftMaxSlabs;
   if (G > cap) G = cap;
   if (G > kDraftMaxSlabs) G = kDraftMaxSlabs;
   if (G > 64) G &= ~7;

@@ -35,8 +35,9 @@ constexpr int kRing = 2;   // ring entries (tiles in flight + the tile in use) p
 
 // F64: the fp64 Gumbel option (scores and the running winner in float64).
 // FL: compile the fixed-count fast loop; it raises the register count to one
-// wave per SIMD, so it is used when the grid has one work-group per CU (one
-// batch tile) and left out otherwise.
+// wave per SIMD, so it is used when the grid has one work-group per CU (up to
+// kDraftFastTiles batch tiles, their slabs filling the CUs once) and left out
+// otherwise.
 template <int NB, bool BBF16, bool CBF16, bool F64, bool FL>
 __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
   using Score = typename std::conditional<F64, double, float>::type;
@@ -637,9 +638,9 @@ template <int NB, bool BBF16, bool CBF16, bool F64>
 hipError_t launch_wave(const DraftStepArgs& a, int bt, hipStream_t st) {
   DraftStepArgs b = a;
   b.BT = bt;
-  if (bt == 1)
-    hipLaunchKernelGGL((draft_wave_kernel<NB, BBF16, CBF16, F64, true>), dim3(a.G), dim3(256), draft_wave_lds(NB, a.r),
-                       st, b);
+  if (bt <= kDraftFastTiles)
+    hipLaunchKernelGGL((draft_wave_kernel<NB, BBF16, CBF16, F64, true>), dim3(a.G * bt), dim3(256),
+                       draft_wave_lds(NB, a.r), st, b);
   else
     hipLaunchKernelGGL((draft_wave_kernel<NB, BBF16, CBF16, F64, false>), dim3(a.G * bt), dim3(256),
                        draft_wave_lds(NB, a.r), st, b);

@@ -96,7 +96,10 @@ __device__ __forceinline__ long long draft_pos_key(const DraftStepArgs& a, int b
 
 int draft_nb(int B, int r);
 int draft_slabs(int V, int cus);
-int draft_wave_slabs(int V, int cus);
+// Batch tiles up to which the wave kernel runs one work-group per CU over
+// all of them (the fixed-count fast loop needs the CU to itself).
+constexpr int kDraftFastTiles = 4;
+int draft_wave_slabs(int V, int cus, int bt);
 hipError_t launch_draft_init(unsigned long long* keys, int n, hipStream_t st);
 hipError_t launch_draft_step(const DraftStepArgs& a, hipStream_t st);
 // Wave-independent streaming step (rank <= 256); hipErrorNotSupported
