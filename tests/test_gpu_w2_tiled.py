@@ -146,3 +146,15 @@ def test_tiled_matches_the_oracle():
     compare_draft(wl, np.arange(wl.B), k1, c1, l1.view(np.float32), rep)
     assert rep.ok(), rep
     assert rep.tokens_total == wl.B * wl.K
+
+
+def test_tiled_headline_matches_the_oracle():
+    # the draft call exactly as the benchmark times it (indexed entry point,
+    # tiled w2, per-step sample positions) against the oracle on every request
+    print("tiled vs oracle: headline V=200064 r=256 K=7 B=32", flush=True)
+    wl = workloads.make_workload("headline_v200064", B=32)
+    (_, _, _, _), (k1, c1, l1, st) = _run_both(wl)
+    rep = Report()
+    compare_draft(wl, np.arange(wl.B), k1, c1, l1.view(np.float32), rep)
+    assert rep.ok(), rep.notes[:5]
+    assert rep.tokens_total == wl.B * wl.K and st == 0
