@@ -30,6 +30,17 @@ namespace mds {
 
 namespace {
 
+// The fp64 option's float64 score of column col: the column's noise word
+// again, then z / T + (-ln(-ln u)) in float64 (T = 1: z itself). Kept out of
+// line: the fast loop calls it for the few columns that can still win.
+__device__ __noinline__ double score64_of(float z, float T, int t1, uint32_t col, uint32_t pk0, uint32_t pk1,
+                                          uint32_t sk0, uint32_t sk1) {
+  const Philox4 w = philox4x32_10(col >> 2, pk0, pk1, kSaltDraft, sk0, sk1);
+  const uint32_t sel = col & 3u;
+  const uint32_t wd = sel == 0 ? w.x0 : (sel == 1 ? w.x1 : (sel == 2 ? w.x2 : w.x3));
+  return (t1 ? (double)z : (double)z / (double)T) + gumbel64_from_word(wd);
+}
+
 constexpr int kRKMax = 8;  // rank slices of 32 (r <= 256)
 constexpr int kRing = 2;   // ring entries (tiles in flight + the tile in use) per wave in the fast loop
 
@@ -262,9 +273,38 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
       for (int s = 0; s < kRKMax; ++s)
         Er[nt][s] = *(const bf16x8*)(a.w1 + (size_t)pv[nt] * r + (s < RK ? s : 0) * 32 + lg * 8);
     asm volatile("" ::: "memory");  // the tile loads stay behind the embedding loads
+    // fp64 option: every element's float32 score comes first (within ~1e-5
+    // of its float64 score), and a lane scores in float64 only the elements
+    // that can still win. It keeps its two best float32 scores per request
+    // tile (stable: an equal later score does not displace an earlier one);
+    // an element that leaves or never enters them while within the margin of
+    // the running maximum is scored at once, and anything below the margin is
+    // beaten, in float64 too, by the element holding that maximum. After the
+    // loop the two kept are scored, and all are merged by the winner rule:
+    // the first NaN, else the largest score, the lower column on a tie.
+    float k2s[NT][2], k2z[NT][2];
+    int k2c[NT][2], nanc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      nanc[nt] = -1;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        k2s[nt][j] = -INFINITY;
+        k2z[nt][j] = 0.0f;
+        k2c[nt][j] = -1;
+      }
+    }
+    auto margin = [](float m) { return m - (1e-4f + 1e-5f * fabsf(m)); };
+    auto exact = [&](auto t1_tag, int nt, float zz, int col) {
+      const double sv = score64_of(zz, Tv[nt], decltype(t1_tag)::value, (uint32_t)col, pk0[nt], pk1[nt], sk0[nt],
+                                   sk1[nt]);
+      const double b = (double)bv[nt];
+      const bool take = sv != sv ? (b == b || col < bi[nt]) : (b == b && (sv > b || (sv == b && col < bi[nt])));
+      bv[nt] = take ? (Score)sv : bv[nt];
+      bi[nt] = take ? col : bi[nt];
+    };
     // One full tile of the fast loop: bias by MFMA from the ring entry's w2
-    // rows, then the branch-free epilogue. `live` is 1 for every tile the
-    // loop computes; the accumulation of q statistics multiplies by it.
+    // rows, then the branch-free epilogue.
     // MASK: some row of the batch tile is not served (its cache stores are skipped)
     auto fast_tile = [&](auto t1_tag, auto full_tag, auto mask_tag, int t, const u32x4 (&Ab)[kRKMax],
                          const float (&bzb)[NT][4]) {
@@ -314,16 +354,30 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          Score sv;
-          if (F64)
-            sv = (T1 ? (double)z[i] : (double)z[i] / (double)Tv[nt]) + gumbel64_from_word(wd[i]);
-          else
-            sv = y[i] + gumbel_from_word(wd[i]);
-          // the winner rule as one mask: a held NaN stays; otherwise a NaN
-          // or a strictly larger score replaces it
-          const bool take = (bv[nt] == bv[nt]) & !(sv <= bv[nt]);
-          bv[nt] = take ? sv : bv[nt];
-          bi[nt] = take ? c + i : bi[nt];
+          if constexpr (F64) {
+            const float s32 = y[i] + gumbel_from_word(wd[i]);
+            const bool up0 = s32 > k2s[nt][0], up1 = s32 > k2s[nt][1];
+            // the element that leaves the two (or never enters): an old
+            // second, or this one; NaN goes to nanc, -inf can never win
+            const float ds = up1 ? k2s[nt][1] : s32;
+            const float dz = up1 ? k2z[nt][1] : z[i];
+            const int dc = up1 ? k2c[nt][1] : c + i;
+            k2s[nt][1] = up0 ? k2s[nt][0] : (up1 ? s32 : k2s[nt][1]);
+            k2z[nt][1] = up0 ? k2z[nt][0] : (up1 ? z[i] : k2z[nt][1]);
+            k2c[nt][1] = up0 ? k2c[nt][0] : (up1 ? c + i : k2c[nt][1]);
+            k2s[nt][0] = up0 ? s32 : k2s[nt][0];
+            k2z[nt][0] = up0 ? z[i] : k2z[nt][0];
+            k2c[nt][0] = up0 ? c + i : k2c[nt][0];
+            if (s32 != s32 && nanc[nt] < 0) nanc[nt] = c + i;
+            if (dc >= 0 && ds > -INFINITY && ds >= margin(k2s[nt][0])) exact(t1_tag, nt, dz, dc);
+          } else {
+            const Score sv = y[i] + gumbel_from_word(wd[i]);
+            // the winner rule as one mask: a held NaN stays; otherwise a NaN
+            // or a strictly larger score replaces it
+            const bool take = (bv[nt] == bv[nt]) & !(sv <= bv[nt]);
+            bv[nt] = take ? sv : bv[nt];
+            bi[nt] = take ? c + i : bi[nt];
+          }
         }
         const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));  // NaN-ignoring max
         const float mn = fmaxf(qm[nt], mx);
@@ -371,6 +425,21 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
         for (int e = 0; e < kRing - 1; ++e)
           if (e < rest) fast_tile(t1_tag, full_tag, mask_tag, t + 4 * e, Ar[e], bzr[e]);
         t += 4 * rest;
+        if constexpr (F64) {  // the kept two and the first NaN join the lane's winner
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+              if (k2c[nt][j] >= 0) exact(t1_tag, nt, k2z[nt][j], k2c[nt][j]);
+            if (nanc[nt] >= 0) {
+              const double b = (double)bv[nt];
+              if (b == b || nanc[nt] < bi[nt]) {
+                bv[nt] = (Score)NAN;
+                bi[nt] = nanc[nt];
+              }
+            }
+          }
+        }
       }
       return t;
     };

@@ -20,8 +20,7 @@ __host__ __device__ __forceinline__ size_t key_index(int k, int B, int b) {
 // keys that each call leaves at zero (the finalize pass clears the keys it
 // reads, and nothing else writes there), so a streaming call with
 // K * B <= kFixedKeys needs no clearing launch whatever the workspace held
-// before; larger calls, and the persistent kernel (whose barrier counters
-// need clearing too), keep theirs elsewhere and clear them first.
+// before; larger calls keep theirs elsewhere and clear them first.
 constexpr int kFixedKeys = 4096;
 
 struct DraftStepArgs {

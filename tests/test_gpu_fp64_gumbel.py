@@ -100,3 +100,61 @@ def test_fp64_gumbel_needs_rank_up_to_256():
     with pytest.raises(mds.MdsError):
         mds.markov_draft_loop_ex(d["base"], d["w1"], d["w2"], d["anchor_tokens"], None, spos, d["temperature"],
                                  d["seeds"], d["cache"], d["draft_tokens"], fp64_gumbel=True)
+
+
+@pytest.mark.parametrize("T", [1.0, 0.7])
+@pytest.mark.parametrize("V", [50016, 50017])
+def test_fp64_near_ties_decided_exactly(V, T):
+    # Planted columns whose float64 scores z / T + g all lie within 2e-7 of 1
+    # (zero w2 rows: z is the base logit; the base holds fp32((s - g) T) for
+    # a random target s with the oracle's own float64 noise g): apart for the
+    # float64 keys (2^-28 relative; the top two at least 1e-8), in no reliable
+    # order for float32 scores, whose rounding is of the same size. Per row
+    # sixteen of them sit in one lane (columns c0 .. c0 + 3 of one tile and of
+    # the wave's next three tiles, c0 + 64 j ..), four more in other lanes and
+    # waves. The draft tokens must equal the oracle's exact float64 winners,
+    # with no excuse. V = 50016: aligned rows, the fast loop with its float32
+    # filter; V = 50017: unaligned rows, the general loop (float64 throughout).
+    print(f"fp64 near ties: V={V} T={T}", flush=True)
+    wl = workloads.make_custom(V, 64, 3, 4, seed=21, temperature=T)
+    B, K, V = wl.B, wl.K, wl.V
+    rng = np.random.default_rng(5)
+    wl.base[:] = -50.0
+    planted = {}
+    lane_misses = 0
+    T32 = np.float32(T)
+    for b in range(B):
+        for k in range(K):
+            c0 = 2048 + 1664 * (b * K + k)  # a multiple of 64: lane-aligned
+            cols = np.concatenate([(c0 + 64 * np.arange(4)[:, None] + np.arange(4)).ravel(),
+                                   c0 + np.array([4, 9, 16, 77])])
+            g = oracle.gumbel(oracle.uniform24(oracle.noise_words(int(wl.seeds[b]), int(wl.anchor_pos[b]) + k,
+                                                                  oracle.SALT_DRAFT, cols)))
+            for _ in range(1000):  # redraw until the float64 top two are clearly apart for the 2^-28 keys
+                z = ((1.0 + rng.random(len(cols)) * 2e-7 - g) * T).astype(np.float32)
+                s64 = z.astype(np.float64) / np.float64(T32) + g
+                top = np.sort(s64)
+                if top[-1] - top[-2] >= 1e-8:
+                    break
+            else:
+                raise AssertionError("no planted row with a clear float64 winner")
+            wl.base[b, k, cols] = z
+            planted[(b, k)] = cols
+            # the construction's power: float32 scores (numpy's rounding) that
+            # leave the float64 winner out of its lane's top two
+            s32 = z / T32 + g.astype(np.float32)
+            win = int(np.argmax(s64))
+            lane_misses += win < 16 and win not in np.argsort(-s32[:16], kind="stable")[:2]
+    assert lane_misses >= 2
+    allc = np.unique(np.concatenate(list(planted.values())))
+    wl.w2[allc] = 0  # bias 0 at the planted columns, whatever the previous token
+    d64 = _run(wl)
+    toks = d64["draft_tokens"].cpu().numpy()
+    ref = oracle.draft_loop(wl.draft_base, wl.base_dtype, wl.w1, wl.w2, wl.anchor_tokens, wl.anchor_pos, wl.seeds,
+                            wl.temperature, wl.cache_dtype, teacher=toks, fp64_gumbel=True)
+    np.testing.assert_array_equal(toks, ref["tokens"])
+    for (b, k), cols in planted.items():
+        assert toks[b, k] in cols
+    # every row is a near-tie at float32 resolution (the general parity rule
+    # would excuse any of them), yet each was decided exactly
+    assert (ref["margin"] < 1e-5).all(), ref["margin"]
