@@ -313,14 +313,67 @@ __device__ __forceinline__ void better(S& s, int& c, S s2, int c2) {
   c = take ? c2 : c;
 }
 
+// Reductions over a wave for the chain's steps, without LDS round trips:
+// DPP within each row of 16 lanes (the quad permutations, then rotations by
+// 4 and 8 lanes, so every lane holds its row's result), then the four rows'
+// results read as scalars. The operations are associative and commutative
+// (max, sum, the winner order), and every lane returns the same value.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_val(float v) { return __uint_as_float(dpp32<CTRL>(__float_as_uint(v))); }
+template <int CTRL>
+__device__ __forceinline__ int dpp_val(int v) { return (int)dpp32<CTRL>((uint32_t)v); }
+template <int CTRL>
+__device__ __forceinline__ double dpp_val(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint64_t lo = dpp32<CTRL>((uint32_t)u), hi = dpp32<CTRL>((uint32_t)(u >> 32));
+  return __longlong_as_double((long long)((hi << 32) | lo));
+}
+__device__ __forceinline__ float lane_val(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ int lane_val(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+__device__ __forceinline__ double lane_val(double v, int l) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+  return __longlong_as_double((long long)((hi << 32) | lo));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppRor4 = 0x124, kDppRor8 = 0x128;
+
 template <typename S>
-__device__ __forceinline__ void wave_better(S& s, int& c) {
+__device__ __forceinline__ void row_better(S& s, int& c) {
+  better(s, c, dpp_val<kDppXor1>(s), dpp_val<kDppXor1>(c));
+  better(s, c, dpp_val<kDppXor2>(s), dpp_val<kDppXor2>(c));
+  better(s, c, dpp_val<kDppRor4>(s), dpp_val<kDppRor4>(c));
+  better(s, c, dpp_val<kDppRor8>(s), dpp_val<kDppRor8>(c));
+}
+template <typename S>
+__device__ __forceinline__ void wave_better_dpp(S& s, int& c) {
+  row_better(s, c);
+  S s0 = lane_val(s, 0);
+  int c0 = lane_val(c, 0);
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const S s2 = __shfl_xor(s, off);
-    const int c2 = __shfl_xor(c, off);
-    better(s, c, s2, c2);
-  }
+  for (int l = 16; l < 64; l += 16) better(s0, c0, lane_val(s, l), lane_val(c, l));
+  s = s0;
+  c = c0;
+}
+__device__ __forceinline__ float wave_max_dpp(float x) {
+  x = fmaxf(x, dpp_val<kDppXor1>(x));
+  x = fmaxf(x, dpp_val<kDppXor2>(x));
+  x = fmaxf(x, dpp_val<kDppRor4>(x));
+  x = fmaxf(x, dpp_val<kDppRor8>(x));
+  return fmaxf(fmaxf(lane_val(x, 0), lane_val(x, 16)), fmaxf(lane_val(x, 32), lane_val(x, 48)));
+}
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+  x += dpp_val<kDppXor1>(x);
+  x += dpp_val<kDppXor2>(x);
+  x += dpp_val<kDppRor4>(x);
+  x += dpp_val<kDppRor8>(x);
+  return (lane_val(x, 0) + lane_val(x, 16)) + (lane_val(x, 32) + lane_val(x, 48));
 }
 
 __device__ __forceinline__ float dot8(u32x4 w, const float* e) {
@@ -335,6 +388,7 @@ __device__ __forceinline__ float dot8(u32x4 w, const float* e) {
 }
 
 constexpr int kChainBatch = 8;  // 16-byte w2 chunks a thread loads ahead of the embedding
+constexpr int kMaxSteps = 32;   // K <= 32 (checked at the boundary)
 
 template <bool BBF16, bool CBF16, bool F64>
 __global__ __launch_bounds__(kThreads) void topk_chain_kernel(TopkArgs a, int tpc) {
@@ -345,25 +399,34 @@ __global__ __launch_bounds__(kThreads) void topk_chain_kernel(TopkArgs a, int tp
   __shared__ float s_wm[4], s_wsum[4];
   __shared__ int s_wnan[4];
   __shared__ int s_prev;
+  __shared__ int s_sl[kMaxSteps];
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = a.r, nch = r >> 3;
   const int ci = tid / tpc, part = tid - ci * tpc;
   if (tid == 0) s_prev = a.anchor[b];
+  // every step's state slot up front (one thread per step), and this
+  // thread's candidate one step ahead: a step's loads then need nothing
+  // but its own candidate and the previous token
+  if (tid < a.K) s_sl[tid] = row_slot(a, b, tid, a.status);
+  auto cand_of = [&](int k) { return ci < a.topk ? a.cand[((size_t)b * a.K + k) * a.topk + ci] : -1; };
+  int cc_next = cand_of(0);
   for (int k = 0; k < a.K; ++k) {
     const int row = b * a.K + k;
-    const int sl = row_slot(a, b, k, tid == 0 ? a.status : nullptr);
-    __syncthreads();  // s_prev of the previous step is visible; s_e is free
+    __syncthreads();  // s_prev of the previous step (and s_sl) visible; s_e is free
+    const int sl = s_sl[k];
+    const int cc = cc_next;
     if (sl < 0) {  // inert step: no sample, no cache write; the next step has no previous token
       if (tid == 0) {
         a.tokens[row] = -1;
         if (a.lse) a.lse[row] = NAN;
         s_prev = -1;
       }
+      if (k + 1 < a.K) cc_next = cand_of(k + 1);
       continue;
     }
-    // w2 rows of the candidates and their base logits go out first
-    const int cc = ci < a.topk ? a.cand[(size_t)row * a.topk + ci] : -1;
+    // w2 rows of the candidates, their base logits and the step's
+    // parameters go out first
     const bool has = cc >= 0 && cc < a.V;
     const int col = has ? cc : 0;
     const uint16_t* w2row = a.w2 + (size_t)col * r;
@@ -378,14 +441,20 @@ __global__ __launch_bounds__(kThreads) void topk_chain_kernel(TopkArgs a, int tp
       bv = BBF16 ? bf16_bits_to_f32(((const uint16_t*)a.base)[b * a.base_rs + k * a.base_ss + col])
                  : ((const float*)a.base)[b * a.base_rs + k * a.base_ss + col];
     }
-    // embedding of the previous token
+    const float T = a.temp[sl];
+    const unsigned long long seed = (unsigned long long)a.seeds[sl];
+    const unsigned long long pos = (unsigned long long)(a.sample_pos[row] - 1);
+    // embedding of the previous token, then the next step's candidate
     long long tk = s_prev;
     if (tk < 0 || tk >= a.V) {
       if (tid == 0) set_status(a.status, kStatusBadAnchor);
       tk = 0;
     }
+    u32x4 ew = {0u, 0u, 0u, 0u};
+    if (tid < nch) ew = *(const u32x4*)(a.w1 + (size_t)tk * r + 8 * tid);
+    if (k + 1 < a.K) cc_next = cand_of(k + 1);
     for (int j = tid; j < nch; j += kThreads) {
-      const u32x4 x = *(const u32x4*)(a.w1 + (size_t)tk * r + 8 * j);
+      const u32x4 x = j == tid ? ew : *(const u32x4*)(a.w1 + (size_t)tk * r + 8 * j);
       const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
@@ -402,10 +471,9 @@ __global__ __launch_bounds__(kThreads) void topk_chain_kernel(TopkArgs a, int tp
     }
     for (int j = part + kChainBatch * tpc; has && j < nch; j += tpc)
       acc += dot8(*(const u32x4*)(w2row + 8 * j), s_e + 8 * j);
-    for (int off = tpc >> 1; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    for (int off = tpc >> 1; off >= 1; off >>= 1) acc += __uint_as_float(lane_xor(__float_as_uint(acc), off));
 
     // biased logit, cache write, score and log-sum-exp terms at the candidate
-    const float T = a.temp[sl];
     const bool samp = T > 0.0f;
     Score s = (Score)0;
     int c = -1;
@@ -425,8 +493,6 @@ __global__ __launch_bounds__(kThreads) void topk_chain_kernel(TopkArgs a, int tp
       c = col;
       if (samp) {
         const float invT = 1.0f / T;
-        const unsigned long long seed = (unsigned long long)a.seeds[sl];
-        const unsigned long long pos = (unsigned long long)(a.sample_pos[row] - 1);
         const Philox4 w = philox4x32_10((uint32_t)col >> 2, (uint32_t)pos, (uint32_t)(pos >> 32), kSaltDraft,
                                         (uint32_t)seed, (uint32_t)(seed >> 32));
         const uint32_t sel = col & 3;
@@ -443,8 +509,8 @@ __global__ __launch_bounds__(kThreads) void topk_chain_kernel(TopkArgs a, int tp
       }
     }
     // winner, and max / NaN flag of cache / T
-    wave_better(s, c);
-    float m = wave_max_f32(x);
+    wave_better_dpp(s, c);
+    float m = wave_max_dpp(x);
     int anynan = __any(xnan) ? 1 : 0;
     if (lane == 0) {
       s_ws[wv] = s;
@@ -469,7 +535,7 @@ __global__ __launch_bounds__(kThreads) void topk_chain_kernel(TopkArgs a, int tp
       lse = m;
     } else if (samp && !anynan) {
       float e = (has && part == 0 && x > -INFINITY) ? __expf(x - m) : 0.0f;
-      e = wave_sum_f32(e);
+      e = wave_sum_dpp(e);
       if (lane == 0) s_wsum[wv] = e;
       __syncthreads();
       lse = m + __logf(s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3]);
