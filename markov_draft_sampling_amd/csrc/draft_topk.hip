@@ -387,82 +387,112 @@ __device__ __forceinline__ float dot8(u32x4 w, const float* e) {
   return acc;
 }
 
-constexpr int kChainBatch = 8;  // 16-byte w2 chunks a thread loads ahead of the embedding
+constexpr int kChainBatch = 8;  // 16-byte w2 chunks a thread loads per step
 constexpr int kMaxSteps = 32;   // K <= 32 (checked at the boundary)
 
 template <bool BBF16, bool CBF16, bool F64>
 __global__ __launch_bounds__(kThreads) void topk_chain_kernel(TopkArgs a, int tpc) {
   using Score = typename std::conditional<F64, double, float>::type;
   __shared__ float s_e[512];
+  // per-wave results: a wave writes the next step's only after the next
+  // step's embedding barrier, which every wave reaches after reading these
   __shared__ Score s_ws[4];
   __shared__ int s_wc[4];
   __shared__ float s_wm[4], s_wsum[4];
   __shared__ int s_wnan[4];
-  __shared__ int s_prev;
   __shared__ int s_sl[kMaxSteps];
-  const int b = blockIdx.x;
+  __shared__ float s_T[kMaxSteps];
+  __shared__ unsigned long long s_seed[kMaxSteps], s_pos[kMaxSteps];
+  const int b = blockIdx.x, K = a.K;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = a.r, nch = r >> 3;
   const int ci = tid / tpc, part = tid - ci * tpc;
-  if (tid == 0) s_prev = a.anchor[b];
-  // every step's state slot up front (one thread per step), and this
-  // thread's candidate one step ahead: a step's loads then need nothing
-  // but its own candidate and the previous token
-  if (tid < a.K) s_sl[tid] = row_slot(a, b, tid, a.status);
-  auto cand_of = [&](int k) { return ci < a.topk ? a.cand[((size_t)b * a.K + k) * a.topk + ci] : -1; };
-  int cc_next = cand_of(0);
-  for (int k = 0; k < a.K; ++k) {
-    const int row = b * a.K + k;
-    __syncthreads();  // s_prev of the previous step (and s_sl) visible; s_e is free
-    const int sl = s_sl[k];
-    const int cc = cc_next;
-    if (sl < 0) {  // inert step: no sample, no cache write; the next step has no previous token
-      if (tid == 0) {
-        a.tokens[row] = -1;
-        if (a.lse) a.lse[row] = NAN;
-        s_prev = -1;
-      }
-      if (k + 1 < a.K) cc_next = cand_of(k + 1);
-      continue;
-    }
-    // w2 rows of the candidates, their base logits and the step's
-    // parameters go out first
+  auto cand_of = [&](int k) { return ci < a.topk ? a.cand[((size_t)b * K + k) * a.topk + ci] : -1; };
+
+  // A step's loads: the w2 rows of this thread's candidate and its base
+  // logit, the embedding row of the previous token (a row past V reads row 0
+  // and is flagged when the step is live), and the next step's candidate.
+  // They are issued as soon as the previous token is known, so they fly
+  // while the previous step finishes its log-sum-exp and this step draws
+  // its noise.
+  int cc = -1, cc_next = cand_of(0);
+  u32x4 wch[kChainBatch];
+  u32x4 ew = {0u, 0u, 0u, 0u};
+  float bv = 0.0f;
+  bool tk_bad = false;
+  auto issue = [&](int k, long long tk) {
+    cc = cc_next;
+    if (k + 1 < K) cc_next = cand_of(k + 1);
     const bool has = cc >= 0 && cc < a.V;
     const int col = has ? cc : 0;
     const uint16_t* w2row = a.w2 + (size_t)col * r;
-    u32x4 wch[kChainBatch];
 #pragma unroll
     for (int q = 0; q < kChainBatch; ++q) {
       const int j = part + q * tpc;
       if (has && j < nch) wch[q] = *(const u32x4*)(w2row + 8 * j);
     }
-    float bv = 0.0f;
+    bv = 0.0f;
     if (has && part == 0) {
       bv = BBF16 ? bf16_bits_to_f32(((const uint16_t*)a.base)[b * a.base_rs + k * a.base_ss + col])
                  : ((const float*)a.base)[b * a.base_rs + k * a.base_ss + col];
     }
-    const float T = a.temp[sl];
-    const unsigned long long seed = (unsigned long long)a.seeds[sl];
-    const unsigned long long pos = (unsigned long long)(a.sample_pos[row] - 1);
-    // embedding of the previous token, then the next step's candidate
-    long long tk = s_prev;
-    if (tk < 0 || tk >= a.V) {
-      if (tid == 0) set_status(a.status, kStatusBadAnchor);
-      tk = 0;
+    tk_bad = tk < 0 || tk >= a.V;
+    if (tk_bad) tk = 0;
+    if (tid < nch) ew = *(const u32x4*)(a.w1 + (size_t)tk * r + 8 * tid);  // r <= 512: one chunk per thread
+  };
+  // step 0's loads go out with the per-step state: slots, temperatures,
+  // seeds and sample positions, one thread per step
+  issue(0, (long long)a.anchor[b]);
+  if (tid < K) {
+    const int sl = row_slot(a, b, tid, a.status);
+    s_sl[tid] = sl;
+    const int ss = sl < 0 ? 0 : sl;
+    s_T[tid] = a.temp[ss];
+    s_seed[tid] = (unsigned long long)a.seeds[ss];
+    s_pos[tid] = (unsigned long long)(a.sample_pos[b * K + tid] - 1);
+  }
+  __syncthreads();
+  for (int k = 0; k < K; ++k) {
+    const int row = b * K + k;
+    const int sl = s_sl[k];
+    if (sl < 0) {  // inert step: no sample, no cache write; the next step has no previous token
+      if (tid == 0) {
+        a.tokens[row] = -1;
+        if (a.lse) a.lse[row] = NAN;
+      }
+      if (k + 1 < K) issue(k + 1, -1);
+      continue;
     }
-    u32x4 ew = {0u, 0u, 0u, 0u};
-    if (tid < nch) ew = *(const u32x4*)(a.w1 + (size_t)tk * r + 8 * tid);
-    if (k + 1 < a.K) cc_next = cand_of(k + 1);
-    for (int j = tid; j < nch; j += kThreads) {
-      const u32x4 x = j == tid ? ew : *(const u32x4*)(a.w1 + (size_t)tk * r + 8 * j);
-      const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+    if (tk_bad && tid == 0) set_status(a.status, kStatusBadAnchor);
+    const float T = s_T[k];
+    const bool samp = T > 0.0f;
+    const float invT = samp ? 1.0f / T : 1.0f;
+    const bool has = cc >= 0 && cc < a.V;
+    const bool mine = has && part == 0;  // this thread scores the candidate
+    const int col = has ? cc : 0;
+    // the noise at the candidate, while the loads are in flight
+    Score g = (Score)0;
+    if (mine && samp) {
+      const unsigned long long seed = s_seed[k], pos = s_pos[k];
+      const Philox4 w = philox4x32_10((uint32_t)col >> 2, (uint32_t)pos, (uint32_t)(pos >> 32), kSaltDraft,
+                                      (uint32_t)seed, (uint32_t)(seed >> 32));
+      const uint32_t sel = col & 3;
+      const uint32_t wd = sel == 0 ? w.x0 : (sel == 1 ? w.x1 : (sel == 2 ? w.x2 : w.x3));
+      if constexpr (F64)
+        g = gumbel64_from_word(wd);
+      else
+        g = gumbel_from_word(wd);
+    }
+    if (tid < nch) {
+      const uint32_t xs[4] = {ew.x, ew.y, ew.z, ew.w};
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
-        s_e[8 * j + 2 * h] = __uint_as_float(xs[h] << 16);
-        s_e[8 * j + 2 * h + 1] = __uint_as_float(xs[h] & 0xFFFF0000u);
+        s_e[8 * tid + 2 * h] = __uint_as_float(xs[h] << 16);
+        s_e[8 * tid + 2 * h + 1] = __uint_as_float(xs[h] & 0xFFFF0000u);
       }
     }
-    __syncthreads();
+    __syncthreads();  // the embedding is in s_e
+    const uint16_t* w2row = a.w2 + (size_t)col * r;
     float acc = 0.0f;
 #pragma unroll
     for (int q = 0; q < kChainBatch; ++q) {
@@ -474,12 +504,11 @@ __global__ __launch_bounds__(kThreads) void topk_chain_kernel(TopkArgs a, int tp
     for (int off = tpc >> 1; off >= 1; off >>= 1) acc += __uint_as_float(lane_xor(__float_as_uint(acc), off));
 
     // biased logit, cache write, score and log-sum-exp terms at the candidate
-    const bool samp = T > 0.0f;
     Score s = (Score)0;
     int c = -1;
     float x = -INFINITY;
     int xnan = 0;
-    if (has && part == 0) {
+    if (mine) {
       const float z = bv + acc;
       const long long off = (long long)slot_cache_row(a, b, sl) * a.cache_rs + (long long)k * a.cache_ss + col;
       float cv = z;
@@ -492,15 +521,10 @@ __global__ __launch_bounds__(kThreads) void topk_chain_kernel(TopkArgs a, int tp
       }
       c = col;
       if (samp) {
-        const float invT = 1.0f / T;
-        const Philox4 w = philox4x32_10((uint32_t)col >> 2, (uint32_t)pos, (uint32_t)(pos >> 32), kSaltDraft,
-                                        (uint32_t)seed, (uint32_t)(seed >> 32));
-        const uint32_t sel = col & 3;
-        const uint32_t wd = sel == 0 ? w.x0 : (sel == 1 ? w.x1 : (sel == 2 ? w.x2 : w.x3));
-        if (F64)
-          s = (Score)((double)z / (double)T + gumbel64_from_word(wd));
+        if constexpr (F64)
+          s = (Score)((double)z / (double)T + g);
         else
-          s = (Score)(div_t(z, T, invT) + gumbel_from_word(wd));
+          s = (Score)(div_t(z, T, invT) + g);
         x = div_t(cv, T, invT);
         xnan = x != x;
         if (xnan) x = -INFINITY;
@@ -518,23 +542,26 @@ __global__ __launch_bounds__(kThreads) void topk_chain_kernel(TopkArgs a, int tp
       s_wm[wv] = m;
       s_wnan[wv] = anynan;
     }
-    __syncthreads();
-    s = s_ws[0];
-    c = s_wc[0];
+    __syncthreads();  // every thread merges the four waves' results
+    Score sw = s_ws[0];
+    int cw = s_wc[0];
     m = s_wm[0];
     anynan = s_wnan[0];
     for (int u = 1; u < 4; ++u) {
-      better(s, c, s_ws[u], s_wc[u]);
+      better(sw, cw, s_ws[u], s_wc[u]);
       m = fmaxf(m, s_wm[u]);
       anynan |= s_wnan[u];
     }
     // an all -inf row: every column ties at -inf and the first column wins
-    const int token = (c < 0 || (s == -(Score)INFINITY)) ? 0 : c;
+    const int token = (cw < 0 || (sw == -(Score)INFINITY)) ? 0 : cw;
+    // the next step's loads (also for an inert step, which keeps the
+    // candidate prefetch in order), before this step's log-sum-exp
+    if (k + 1 < K) issue(k + 1, token);
     float lse = NAN;
     if (samp && !anynan && (m == INFINITY || m == -INFINITY)) {
       lse = m;
     } else if (samp && !anynan) {
-      float e = (has && part == 0 && x > -INFINITY) ? __expf(x - m) : 0.0f;
+      float e = (mine && x > -INFINITY) ? __expf(x - m) : 0.0f;
       e = wave_sum_dpp(e);
       if (lane == 0) s_wsum[wv] = e;
       __syncthreads();
@@ -543,7 +570,6 @@ __global__ __launch_bounds__(kThreads) void topk_chain_kernel(TopkArgs a, int tp
     if (tid == 0) {
       a.tokens[row] = token;
       if (a.lse) a.lse[row] = lse;
-      s_prev = token;
     }
   }
 }
