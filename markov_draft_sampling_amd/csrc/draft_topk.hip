@@ -77,17 +77,19 @@ __device__ void block_select_top(const unsigned long long* keys, int n, int k, u
 }
 
 // ------------------------------------------------------------ loads --
+// Four base logits of a chunk; the vector form is non-temporal (each base
+// row is read once here, and the chain reads only its candidates)
 template <bool BF16>
 __device__ __forceinline__ void load4(const void* row, int c, int V, bool vec, float v[4]) {
   if (vec && c + 3 < V) {
     if (BF16) {
-      const u32x2 x = *(const u32x2*)((const uint16_t*)row + c);
+      const u32x2 x = __builtin_nontemporal_load((const u32x2*)((const uint16_t*)row + c));
       v[0] = __uint_as_float(x.x << 16);
       v[1] = __uint_as_float(x.x & 0xFFFF0000u);
       v[2] = __uint_as_float(x.y << 16);
       v[3] = __uint_as_float(x.y & 0xFFFF0000u);
     } else {
-      const f32x4 x = *(const f32x4*)((const float*)row + c);
+      const f32x4 x = __builtin_nontemporal_load((const f32x4*)((const float*)row + c));
       v[0] = x.x;
       v[1] = x.y;
       v[2] = x.z;
