@@ -165,6 +165,57 @@ def test_topk_indexed_with_padding():
     assert np.isnan(lse[~live_steps]).all()
 
 
+@pytest.mark.parametrize("K", [1, 5])
+def test_topk_inert_steps_anywhere(K):
+    # inert steps first, last, two in a row and alternating (the chain issues
+    # a step's loads before it knows the step is live, and a live step after
+    # an inert one has no previous token: token 0, flagged); K = 1 as well
+    import torch
+    import markov_draft_sampling_amd as mds
+    print(f"top-k inert steps: K={K}", flush=True)
+    wl = workloads.make_custom(9000, 64, K, 6, seed=33)
+    B = wl.B
+    idx = np.repeat(np.arange(B, dtype=np.int32)[:, None], K, axis=1)
+    if K == 1:
+        idx[1, 0] = idx[4, 0] = -1
+    else:
+        idx[0, 0] = -1               # inert first step
+        idx[1, K - 1] = -1           # inert last step
+        idx[2, 1] = idx[2, 2] = -1   # two in a row
+        idx[3, 1::2] = -1            # alternating
+        idx[5, :] = -1               # a padding request
+    temp = wl.temperature.copy()
+    temp[4] = 0.0  # a greedy request
+    spos = (wl.anchor_pos[:, None] + 1 + np.arange(K)[None, :]).astype(np.int64)
+    d = dev_tensors(wl)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    cache = torch.full((B, K, wl.V), 2.5, dtype=torch.float32, device="cuda")
+    ws = mds.new_workspace(mds.draft_topk_workspace_bytes(B, K, wl.V, wl.r, 20), torch.device("cuda"))
+    mds.markov_draft_loop_topk(d["base"], d["w1"], d["w2"], d["anchor_tokens"], t(idx), t(spos), t(temp),
+                               d["seeds"], cache, d["draft_tokens"], 20, draft_lse=d["draft_lse"], workspace=ws)
+    torch.cuda.synchronize()
+    toks = d["draft_tokens"].cpu().numpy()
+    ref = oracle.draft_loop(wl.draft_base, wl.base_dtype, wl.w1, wl.w2, wl.anchor_tokens, wl.anchor_pos, wl.seeds,
+                            temp, "f32", teacher=toks, idx_map=idx, sample_pos=spos,
+                            cache_init=np.full((B, K, wl.V), 2.5, np.float32), topk=20)
+    mism = (ref["tokens"] != toks) & (ref["margin"] > 1e-3)
+    assert not mism.any(), np.argwhere(mism)[:5]
+    assert ((toks == -1) == (idx < 0)).all()
+    flagged = bool(mds.workspace_status(ws) & mds.STATUS_BAD_ANCHOR)
+    assert flagged == bool(ref["bad_prev"])
+    if K > 1:
+        assert flagged
+    g = cache.cpu().numpy().astype(np.float64)
+    o = ref["cache"].astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        assert ((np.abs(g - o) <= 2e-3) | (g == o)).all()
+    lse = d["draft_lse"].cpu().numpy()
+    live_steps = idx >= 0
+    samp = live_steps & (temp[:, None] > 0)
+    assert (np.abs(lse[samp] - ref["lse"][samp]) <= 1e-4 + 1e-5 * np.abs(ref["lse"][samp])).all()
+    assert np.isnan(lse[~live_steps]).all()
+
+
 def test_topk_headline_rows():
     wl = workloads.make_workload("headline_v200064", B=32)
     d = _run(wl, 64, verify=True)
