@@ -281,7 +281,9 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
     // the running maximum is scored at once, and anything below the margin is
     // beaten, in float64 too, by the element holding that maximum. After the
     // loop the two kept are scored, and all are merged by the winner rule:
-    // the first NaN, else the largest score, the lower column on a tie.
+    // the first NaN, else the largest score, the lower column on a tie. An
+    // element whose float32 score overflowed (a finite logit over a tiny
+    // temperature) is scored at once.
     float k2s[NT][2], k2z[NT][2];
     int k2c[NT][2], nanc[NT];
 #pragma unroll
@@ -370,6 +372,10 @@ __global__ __launch_bounds__(256) void draft_wave_kernel(DraftStepArgs a) {
             k2c[nt][0] = up0 ? c + i : k2c[nt][0];
             if (s32 != s32 && nanc[nt] < 0) nanc[nt] = c + i;
             if (dc >= 0 && ds > -INFINITY && ds >= margin(k2s[nt][0])) exact(t1_tag, nt, dz, dc);
+            // a finite logit whose float32 score overflowed (z / T past the
+            // float32 range) has a finite float64 score the filter cannot
+            // rank: it is scored at once
+            if (!T1 && fabsf(s32) == INFINITY && fabsf(z[i]) < INFINITY) exact(t1_tag, nt, z[i], c + i);
           } else {
             const Score sv = y[i] + gumbel_from_word(wd[i]);
             // the winner rule as one mask: a held NaN stays; otherwise a NaN

@@ -158,3 +158,31 @@ def test_fp64_near_ties_decided_exactly(V, T):
     # every row is a near-tie at float32 resolution (the general parity rule
     # would excuse any of them), yet each was decided exactly
     assert (ref["margin"] < 1e-5).all(), ref["margin"]
+
+
+def test_fp64_float32_overflow_decided_exactly():
+    # T = 1e-37: planted logits 100 .. 107.5 give float32 scores past the
+    # float32 range (+inf, all equal) and float64 scores ~1e39 that are far
+    # apart; the rest of the row scores -10. Sixteen planted columns per row
+    # sit in one lane, the largest logit last, so a filter that ranked the
+    # float32 scores would keep only the first two. V = 50016: the fast loop.
+    print("fp64 float32 overflow: V=50016 T=1e-37", flush=True)
+    wl = workloads.make_custom(50016, 64, 2, 4, seed=29, temperature=1e-37)
+    B, K = wl.B, wl.K
+    wl.base[:] = -1e-36
+    wl.w2[:] = 0  # no Markov bias: z is the base logit
+    planted = {}
+    for b in range(B):
+        for k in range(K):
+            c0 = 2048 + 1664 * (b * K + k)
+            cols = (c0 + 64 * np.arange(4)[:, None] + np.arange(4)).ravel()
+            wl.base[b, k, cols] = (100.0 + 0.5 * np.arange(16)).astype(np.float32)
+            planted[(b, k)] = cols
+    d = _run(wl)
+    toks = d["draft_tokens"].cpu().numpy()
+    with np.errstate(all="ignore"):
+        ref = oracle.draft_loop(wl.draft_base, wl.base_dtype, wl.w1, wl.w2, wl.anchor_tokens, wl.anchor_pos,
+                                wl.seeds, wl.temperature, wl.cache_dtype, teacher=toks, fp64_gumbel=True)
+    np.testing.assert_array_equal(toks, ref["tokens"])
+    for (b, k), cols in planted.items():
+        assert toks[b, k] == cols[-1]
