@@ -509,22 +509,27 @@ constexpr int kWavePer = kStatsChunk / 64;  // values per lane: columns c0 + 256
 // any value is used.
 template <bool BF16>
 __device__ __forceinline__ void load_wave_block(const void* rowp, int V, int c0, bool vec, float (&v)[kWavePer]) {
+  // a buffer over the row: 32-bit offsets from one base, and loads past the
+  // row's V elements return 0 (the pad of a partial block) without a test
+  constexpr int kEs = BF16 ? 2 : 4;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)rowp, (short)0, V * kEs, 0x00020000);  // raw, byte-addressed
   const int tc = c0 + (int)(threadIdx.x & 63) * 4;
   if (vec && c0 + kStatsChunk <= V) {
 #pragma unroll
     for (int i = 0; i < kWavePer / 4; ++i) {
       if (BF16) {
-        const u32x2 w = __builtin_nontemporal_load((const u32x2*)((const uint16_t*)rowp + tc + i * 256));
+        const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, (tc + i * 256) * kEs, 0, 2));
         v[4 * i + 0] = bf16_bits_to_f32(w.x & 0xFFFFu);
         v[4 * i + 1] = bf16_bits_to_f32(w.x >> 16);
         v[4 * i + 2] = bf16_bits_to_f32(w.y & 0xFFFFu);
         v[4 * i + 3] = bf16_bits_to_f32(w.y >> 16);
       } else {
-        const f32x4 w = __builtin_nontemporal_load((const f32x4*)((const float*)rowp + tc + i * 256));
-        v[4 * i + 0] = w.x;
-        v[4 * i + 1] = w.y;
-        v[4 * i + 2] = w.z;
-        v[4 * i + 3] = w.w;
+        const u32x4 w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (tc + i * 256) * kEs, 0, 2));
+        v[4 * i + 0] = __uint_as_float(w.x);
+        v[4 * i + 1] = __uint_as_float(w.y);
+        v[4 * i + 2] = __uint_as_float(w.z);
+        v[4 * i + 3] = __uint_as_float(w.w);
       }
     }
   } else {
@@ -532,8 +537,9 @@ __device__ __forceinline__ void load_wave_block(const void* rowp, int V, int c0,
     for (int i = 0; i < kWavePer / 4; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int c = tc + i * 256 + e;
-        v[4 * i + e] = c < V ? load_f32_or_bf16(rowp, c, BF16) : 0.0f;
+        const int off = (tc + i * 256 + e) * kEs;
+        v[4 * i + e] = BF16 ? bf16_bits_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 2))
+                            : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 2));
       }
   }
 }
