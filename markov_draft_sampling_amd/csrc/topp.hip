@@ -82,10 +82,31 @@ struct RowCtx {
   float T, invT, M;
 };
 
-// visit every column of the row with (column, logit); columns ascend per thread
+// visit every column of the row with (column, logit); columns ascend per
+// thread. Whole batches of kRowBatch vector loads go out before any of their
+// values is used (one load in flight per thread would leave the pass bound
+// by memory latency); the rest of the row follows one load at a time.
+constexpr int kRowBatch = 4;
 template <class F>
 __device__ __forceinline__ void for_row(const RowCtx& r, F&& f) {
-  for (int c = threadIdx.x * 4; c < r.V; c += kTp * 4) {
+  constexpr int kStep = kTp * 4;
+  int c0 = threadIdx.x * 4;
+  if (r.vec) {
+    for (; c0 + (kRowBatch - 1) * kStep + 4 <= r.V; c0 += kRowBatch * kStep) {
+      f32x4 w[kRowBatch];
+#pragma unroll
+      for (int u = 0; u < kRowBatch; ++u) w[u] = *(const f32x4*)(r.t + c0 + u * kStep);
+#pragma unroll
+      for (int u = 0; u < kRowBatch; ++u) {
+        const int c = c0 + u * kStep;
+        f(c, w[u].x);
+        f(c + 1, w[u].y);
+        f(c + 2, w[u].z);
+        f(c + 3, w[u].w);
+      }
+    }
+  }
+  for (int c = c0; c < r.V; c += kStep) {
     const int n = r.V - c >= 4 ? 4 : r.V - c;
     if (r.vec && n == 4) {
       const f32x4 w = *(const f32x4*)(r.t + c);
