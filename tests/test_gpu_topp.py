@@ -36,7 +36,10 @@ def _families(rng, V):
     yield "no_finite", z
 
 
-@pytest.mark.parametrize("V", [600, 8200, 151936])
+# 16380, 16388 and 20480 sit at the row passes' batches of four loads per
+# thread (16384 columns): a thread whose batch would pass V, one vector load
+# after the batch, a batch and then a remainder for every thread
+@pytest.mark.parametrize("V", [600, 8200, 16380, 16388, 20480, 151936])
 def test_top_p_kept_set_matches_oracle(V):
     import torch
     import markov_draft_sampling_amd as mds
