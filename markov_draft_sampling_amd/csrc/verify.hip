@@ -145,9 +145,42 @@ __device__ __forceinline__ void block_merge_ms(float& m, float& s) {
   }
 }
 
+// Largest 64-bit key over the wave, in every lane, without LDS permutes:
+// DPP within each row of 16 lanes (quad permutations, then rotations by 4
+// and 8), then the four rows' results read as scalars.
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+  return ((unsigned long long)hi << 32) | lo;
+}
+__device__ __forceinline__ unsigned long long lane_u64(unsigned long long v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((unsigned long long)hi << 32) | lo;
+}
+__device__ __forceinline__ unsigned long long wave_max_key(unsigned long long k) {
+  unsigned long long o;
+  o = dpp_u64<0xB1>(k);
+  k = o > k ? o : k;
+  o = dpp_u64<0x4E>(k);
+  k = o > k ? o : k;
+  o = dpp_u64<0x124>(k);
+  k = o > k ? o : k;
+  o = dpp_u64<0x128>(k);
+  k = o > k ? o : k;
+  unsigned long long r = lane_u64(k, 0);
+#pragma unroll
+  for (int l = 16; l < 64; l += 16) {
+    const unsigned long long x = lane_u64(k, l);
+    r = x > r ? x : r;
+  }
+  return r;
+}
+
 __device__ __forceinline__ unsigned long long block_max_key(unsigned long long key) {
   __shared__ unsigned long long sk[4];
-  key = wave_max_u64(key);
+  key = wave_max_key(key);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) sk[wave] = key;
   __syncthreads();
