@@ -432,7 +432,7 @@ __global__ __launch_bounds__(256) void draft_finalize_kernel(DraftFinalArgs a) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) lse_merge(m, s, p[u].x, p[u].y);
   }
-  wave_lse_merge(m, s);
+  wave_lse_merge_dpp(m, s);
   if (lane == 0) {
     float out;
     if (!(T > 0.0f) || s != s)

@@ -315,37 +315,8 @@ __device__ __forceinline__ void better(S& s, int& c, S s2, int c2) {
   c = take ? c2 : c;
 }
 
-// Reductions over a wave for the chain's steps, without LDS round trips:
-// DPP within each row of 16 lanes (the quad permutations, then rotations by
-// 4 and 8 lanes, so every lane holds its row's result), then the four rows'
-// results read as scalars. The operations are associative and commutative
-// (max, sum, the winner order), and every lane returns the same value.
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
-}
-template <int CTRL>
-__device__ __forceinline__ float dpp_val(float v) { return __uint_as_float(dpp32<CTRL>(__float_as_uint(v))); }
-template <int CTRL>
-__device__ __forceinline__ int dpp_val(int v) { return (int)dpp32<CTRL>((uint32_t)v); }
-template <int CTRL>
-__device__ __forceinline__ double dpp_val(double v) {
-  const uint64_t u = (uint64_t)__double_as_longlong(v);
-  const uint64_t lo = dpp32<CTRL>((uint32_t)u), hi = dpp32<CTRL>((uint32_t)(u >> 32));
-  return __longlong_as_double((long long)((hi << 32) | lo));
-}
-__device__ __forceinline__ float lane_val(float v, int l) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
-}
-__device__ __forceinline__ int lane_val(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
-__device__ __forceinline__ double lane_val(double v, int l) {
-  const uint64_t u = (uint64_t)__double_as_longlong(v);
-  const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
-  const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
-  return __longlong_as_double((long long)((hi << 32) | lo));
-}
-constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppRor4 = 0x124, kDppRor8 = 0x128;
-
+// The chain's winner over a wave by the DPP row operations of the shared
+// wave reductions (the winner order is associative and commutative).
 template <typename S>
 __device__ __forceinline__ void row_better(S& s, int& c) {
   better(s, c, dpp_val<kDppXor1>(s), dpp_val<kDppXor1>(c));
@@ -363,21 +334,6 @@ __device__ __forceinline__ void wave_better_dpp(S& s, int& c) {
   s = s0;
   c = c0;
 }
-__device__ __forceinline__ float wave_max_dpp(float x) {
-  x = fmaxf(x, dpp_val<kDppXor1>(x));
-  x = fmaxf(x, dpp_val<kDppXor2>(x));
-  x = fmaxf(x, dpp_val<kDppRor4>(x));
-  x = fmaxf(x, dpp_val<kDppRor8>(x));
-  return fmaxf(fmaxf(lane_val(x, 0), lane_val(x, 16)), fmaxf(lane_val(x, 32), lane_val(x, 48)));
-}
-__device__ __forceinline__ float wave_sum_dpp(float x) {
-  x += dpp_val<kDppXor1>(x);
-  x += dpp_val<kDppXor2>(x);
-  x += dpp_val<kDppRor4>(x);
-  x += dpp_val<kDppRor8>(x);
-  return (lane_val(x, 0) + lane_val(x, 16)) + (lane_val(x, 32) + lane_val(x, 48));
-}
-
 __device__ __forceinline__ float dot8(u32x4 w, const float* e) {
   float acc = 0.0f;
 #pragma unroll

@@ -190,4 +190,84 @@ __device__ __forceinline__ float wave_sum_f32(float x) {
   return x;
 }
 
+// Wave reductions without LDS permutes: DPP within each row of 16 lanes (the
+// quad permutations, then rotations by 4 and 8 lanes, so every lane holds its
+// row's result), then the four rows' results read as scalars and combined in
+// a fixed order; every lane returns the same value. All 64 lanes must be
+// active. For associative, commutative operations (max, the winner order);
+// sums and log-sum-exp merges come out in one fixed order.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_val(float v) { return __uint_as_float(dpp32<CTRL>(__float_as_uint(v))); }
+template <int CTRL>
+__device__ __forceinline__ int dpp_val(int v) { return (int)dpp32<CTRL>((uint32_t)v); }
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_val(unsigned long long v) {
+  return ((unsigned long long)dpp32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp32<CTRL>((uint32_t)v);
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_val(double v) {
+  return __longlong_as_double((long long)dpp_val<CTRL>((unsigned long long)__double_as_longlong(v)));
+}
+__device__ __forceinline__ int lane_val(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+__device__ __forceinline__ float lane_val(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ unsigned long long lane_val(unsigned long long v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((unsigned long long)hi << 32) | lo;
+}
+__device__ __forceinline__ double lane_val(double v, int l) {
+  return __longlong_as_double((long long)lane_val((unsigned long long)__double_as_longlong(v), l));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppRor4 = 0x124, kDppRor8 = 0x128;
+
+__device__ __forceinline__ float wave_max_dpp(float x) {
+  x = fmaxf(x, dpp_val<kDppXor1>(x));
+  x = fmaxf(x, dpp_val<kDppXor2>(x));
+  x = fmaxf(x, dpp_val<kDppRor4>(x));
+  x = fmaxf(x, dpp_val<kDppRor8>(x));
+  return fmaxf(fmaxf(lane_val(x, 0), lane_val(x, 16)), fmaxf(lane_val(x, 32), lane_val(x, 48)));
+}
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+  x += dpp_val<kDppXor1>(x);
+  x += dpp_val<kDppXor2>(x);
+  x += dpp_val<kDppRor4>(x);
+  x += dpp_val<kDppRor8>(x);
+  return (lane_val(x, 0) + lane_val(x, 16)) + (lane_val(x, 32) + lane_val(x, 48));
+}
+__device__ __forceinline__ unsigned long long wave_max_key(unsigned long long k) {
+  unsigned long long o;
+  o = dpp_val<kDppXor1>(k);
+  k = o > k ? o : k;
+  o = dpp_val<kDppXor2>(k);
+  k = o > k ? o : k;
+  o = dpp_val<kDppRor4>(k);
+  k = o > k ? o : k;
+  o = dpp_val<kDppRor8>(k);
+  k = o > k ? o : k;
+  unsigned long long r = lane_val(k, 0);
+#pragma unroll
+  for (int l = 16; l < 64; l += 16) {
+    const unsigned long long x = lane_val(k, l);
+    r = x > r ? x : r;
+  }
+  return r;
+}
+__device__ __forceinline__ void wave_lse_merge_dpp(float& m, float& s) {
+  lse_merge(m, s, dpp_val<kDppXor1>(m), dpp_val<kDppXor1>(s));
+  lse_merge(m, s, dpp_val<kDppXor2>(m), dpp_val<kDppXor2>(s));
+  lse_merge(m, s, dpp_val<kDppRor4>(m), dpp_val<kDppRor4>(s));
+  lse_merge(m, s, dpp_val<kDppRor8>(m), dpp_val<kDppRor8>(s));
+  float rm = lane_val(m, 0), rs = lane_val(s, 0);
+#pragma unroll
+  for (int l = 16; l < 64; l += 16) lse_merge(rm, rs, lane_val(m, l), lane_val(s, l));
+  m = rm;
+  s = rs;
+}
+
 }  // namespace mds

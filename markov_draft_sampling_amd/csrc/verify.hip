@@ -129,73 +129,6 @@ __device__ __forceinline__ unsigned long long thread_key(const float (&v)[kPerTh
   return bi >= 0 ? win_key(bv, (uint32_t)bi) : 0ull;
 }
 
-// Wave reductions without LDS permutes: DPP within each row of 16 lanes
-// (quad permutations, then rotations by 4 and 8), then the four rows'
-// results read as scalars and combined in a fixed order, so every lane
-// returns the same value.
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-template <int CTRL>
-__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long v) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
-  return ((unsigned long long)hi << 32) | lo;
-}
-__device__ __forceinline__ float lane_f32(float v, int l) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
-}
-__device__ __forceinline__ unsigned long long lane_u64(unsigned long long v, int l) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
-  return ((unsigned long long)hi << 32) | lo;
-}
-__device__ __forceinline__ unsigned long long wave_max_key(unsigned long long k) {
-  unsigned long long o;
-  o = dpp_u64<0xB1>(k);
-  k = o > k ? o : k;
-  o = dpp_u64<0x4E>(k);
-  k = o > k ? o : k;
-  o = dpp_u64<0x124>(k);
-  k = o > k ? o : k;
-  o = dpp_u64<0x128>(k);
-  k = o > k ? o : k;
-  unsigned long long r = lane_u64(k, 0);
-#pragma unroll
-  for (int l = 16; l < 64; l += 16) {
-    const unsigned long long x = lane_u64(k, l);
-    r = x > r ? x : r;
-  }
-  return r;
-}
-__device__ __forceinline__ float wave_max_dpp(float x) {
-  x = fmaxf(x, dpp_f32<0xB1>(x));
-  x = fmaxf(x, dpp_f32<0x4E>(x));
-  x = fmaxf(x, dpp_f32<0x124>(x));
-  x = fmaxf(x, dpp_f32<0x128>(x));
-  return fmaxf(fmaxf(lane_f32(x, 0), lane_f32(x, 16)), fmaxf(lane_f32(x, 32), lane_f32(x, 48)));
-}
-__device__ __forceinline__ float wave_sum_dpp(float x) {
-  x += dpp_f32<0xB1>(x);
-  x += dpp_f32<0x4E>(x);
-  x += dpp_f32<0x124>(x);
-  x += dpp_f32<0x128>(x);
-  return (lane_f32(x, 0) + lane_f32(x, 16)) + (lane_f32(x, 32) + lane_f32(x, 48));
-}
-__device__ __forceinline__ void wave_lse_merge_dpp(float& m, float& s) {
-  auto step = [&](float m2, float s2) { lse_merge(m, s, m2, s2); };
-  step(dpp_f32<0xB1>(m), dpp_f32<0xB1>(s));
-  step(dpp_f32<0x4E>(m), dpp_f32<0x4E>(s));
-  step(dpp_f32<0x124>(m), dpp_f32<0x124>(s));
-  step(dpp_f32<0x128>(m), dpp_f32<0x128>(s));
-  float rm = lane_f32(m, 0), rs = lane_f32(s, 0);
-#pragma unroll
-  for (int l = 16; l < 64; l += 16) lse_merge(rm, rs, lane_f32(m, l), lane_f32(s, l));
-  m = rm;
-  s = rs;
-}
-
 // block-wide merge over the 4 waves; the result is valid in thread 0
 __device__ __forceinline__ void block_merge_ms(float& m, float& s) {
   __shared__ float sm[4], ss[4];
