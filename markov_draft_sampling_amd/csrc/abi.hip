@@ -284,15 +284,14 @@ int verify_impl(int B, int K, int V, const float* target, int64_t target_row_str
   a.n_slots = ix.idx_map ? ix.n_slots : B;
   a.n_rows = n_rows;
   hipError_t e;
-  // Without top-p the statistics pass only streams, and one work-group per
-  // request then combines and decides; with top-p its last arrivals combine
-  // and the decision waits for the top-p pass.
-  if ((e = mds::launch_verify_stats(a, top_p != nullptr, st)) != hipSuccess) return hip_fail(e, "verify stats launch");
+  // The statistics pass only streams; one wave per request then combines
+  // (and, without top-p, decides); with top-p the decision waits for the
+  // top-p pass.
+  if ((e = mds::launch_verify_stats(a, st)) != hipSuccess) return hip_fail(e, "verify stats launch");
+  if ((e = mds::launch_combine(a, st)) != hipSuccess) return hip_fail(e, "combine launch");
   if (top_p) {
     if ((e = mds::launch_top_p(a, st)) != hipSuccess) return hip_fail(e, "top-p launch");
     if ((e = mds::launch_decide(a, st)) != hipSuccess) return hip_fail(e, "decide launch");
-  } else if ((e = mds::launch_combine(a, st)) != hipSuccess) {
-    return hip_fail(e, "combine launch");
   }
   if ((e = mds::launch_residual(a, st)) != hipSuccess) return hip_fail(e, "residual launch");
   return ok();
@@ -719,7 +718,8 @@ int mds_debug_top_p(int rows, int V, const float* target, int64_t row_stride, co
   a.top_p = top_p;
   verify_workspace_args(a, ws, L, true, true);
   hipError_t e;
-  if ((e = mds::launch_verify_stats(a, true, st)) != hipSuccess) return hip_fail(e, "verify stats launch");
+  if ((e = mds::launch_verify_stats(a, st)) != hipSuccess) return hip_fail(e, "verify stats launch");
+  if ((e = mds::launch_combine(a, st)) != hipSuccess) return hip_fail(e, "combine launch");
   if ((e = mds::launch_top_p(a, st)) != hipSuccess) return hip_fail(e, "top-p launch");
   if ((e = mds::launch_debug_top_p_out(rows, a.topp, tau, cut, log_z, on, st)) != hipSuccess)
     return hip_fail(e, "top-p output launch");

@@ -269,9 +269,9 @@ __device__ __forceinline__ int verify_cache_row(const VerifyArgs& a, int b, int 
 
 constexpr int kResCols = 2048;  // columns per residual work-group
 
-// last_arrival: the statistics pass combines (and decides) in each request's
-// last-arriving work-group; otherwise launch_combine must follow it.
-hipError_t launch_verify_stats(const VerifyArgs& a, bool last_arrival, hipStream_t st);
+// The statistics pass; launch_combine must follow it (it also decides when
+// a.decide, i.e. without top-p).
+hipError_t launch_verify_stats(const VerifyArgs& a, hipStream_t st);
 hipError_t launch_combine(const VerifyArgs& a, hipStream_t st);
 hipError_t launch_top_p(const VerifyArgs& a, hipStream_t st);
 hipError_t launch_decide(const VerifyArgs& a, hipStream_t st);

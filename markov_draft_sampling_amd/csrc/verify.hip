@@ -19,16 +19,15 @@
 //                    residual max(0, p - q) of the first rejected row, or
 //                    from p for the bonus token; the last one of a request
 //                    writes the output tokens.
-// With top-p, stats_count_kernel's last-arriving work-group per request
-// combines, top_p_kernel (topp.hip) finds the kept sets, decide_kernel runs
-// the accept tests, then the residual pass.
+// With top-p the same statistics pass and combine (without the accept tests)
+// come first; top_p_kernel (topp.hip) then finds the kept sets from the row
+// maxima, decide_kernel runs the accept tests, then the residual pass.
 //
-// Cross-work-group hand-off inside a launch (the counting statistics pass and
-// the residual pass): partials and winner keys are published with
-// device-scope atomic read-modify-writes whose completion the publishing
+// Cross-work-group hand-off inside a launch (the residual pass): winner keys
+// are published with device-scope atomics whose completion the publishing
 // thread waits for before it bumps the request's arrival counter; the last
-// arrival reads them back with read-modify-writes as well. Every counter
-// returns to zero before the call ends.
+// arrival reads them back with read-modify-writes. Every counter returns to
+// zero before the call ends.
 #include "mds_device.h"
 #include "mds_internal.h"
 
@@ -39,7 +38,6 @@ namespace mds {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPerThread = kStatsChunk / kThreads;  // columns c0 + 1024 i + 4 tid + e
 constexpr int kMaxK = 32;
 
 __device__ __forceinline__ float load_f32_or_bf16(const void* p, long long off, int bf16) {
@@ -56,94 +54,6 @@ __device__ __forceinline__ unsigned long long pack_ms(float m, float s) {
 }
 __device__ __forceinline__ float unpack_m(unsigned long long p) { return __uint_as_float((uint32_t)p); }
 __device__ __forceinline__ float unpack_s(unsigned long long p) { return __uint_as_float((uint32_t)(p >> 32)); }
-__device__ __forceinline__ unsigned long long rmw_read(unsigned long long* p) { return atomicAdd(p, 0ull); }
-
-// The kPerThread values of one statistics block that this thread owns. When
-// the whole block exists and vector access is allowed (a block-uniform test)
-// all its loads are issued before any value is used.
-template <bool BF16>
-__device__ __forceinline__ void load_block(const void* rowp, int V, int c0, bool vec, float pad,
-                                           float (&v)[kPerThread]) {
-  const int tc = c0 + (int)threadIdx.x * 4;
-  if (vec && c0 + kStatsChunk <= V) {
-#pragma unroll
-    for (int i = 0; i < kPerThread / 4; ++i) {
-      if (BF16) {
-        const u32x2 w = __builtin_nontemporal_load((const u32x2*)((const uint16_t*)rowp + tc + i * 1024));
-        v[4 * i + 0] = bf16_bits_to_f32(w.x & 0xFFFFu);
-        v[4 * i + 1] = bf16_bits_to_f32(w.x >> 16);
-        v[4 * i + 2] = bf16_bits_to_f32(w.y & 0xFFFFu);
-        v[4 * i + 3] = bf16_bits_to_f32(w.y >> 16);
-      } else {
-        const f32x4 w = __builtin_nontemporal_load((const f32x4*)((const float*)rowp + tc + i * 1024));
-        v[4 * i + 0] = w.x;
-        v[4 * i + 1] = w.y;
-        v[4 * i + 2] = w.z;
-        v[4 * i + 3] = w.w;
-      }
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < kPerThread / 4; ++i) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int c = tc + i * 1024 + e;
-        v[4 * i + e] = c < V ? load_f32_or_bf16(rowp, c, BF16) : pad;
-      }
-    }
-  }
-}
-
-// (max, sum exp) of x = v / T over the thread's columns, NaN sum if one is NaN
-__device__ __forceinline__ void thread_stats(float (&v)[kPerThread], int c0, int V, float T, float invT, float& m,
-                                             float& s) {
-  const int tc = c0 + (int)threadIdx.x * 4;
-  m = -INFINITY;
-  s = 0.0f;
-  bool has_nan = false;
-#pragma unroll
-  for (int j = 0; j < kPerThread; ++j) {
-    const bool valid = tc + (j >> 2) * 1024 + (j & 3) < V;
-    const float x = valid ? div_t(v[j], T, invT) : -INFINITY;
-    has_nan |= x != x;
-    v[j] = (x == x) ? x : -INFINITY;
-    m = fmaxf(m, v[j]);
-  }
-  if (m != -INFINITY) {
-#pragma unroll
-    for (int j = 0; j < kPerThread; ++j) s += fast_exp(v[j] - m);
-  }
-  if (has_nan) s = NAN;
-}
-
-// winner key of the raw values over the thread's columns
-__device__ __forceinline__ unsigned long long thread_key(const float (&v)[kPerThread], int c0, int V) {
-  const int tc = c0 + (int)threadIdx.x * 4;
-  float bv = -INFINITY;
-  int bi = -1;
-#pragma unroll
-  for (int j = 0; j < kPerThread; ++j) {
-    const int c = tc + (j >> 2) * 1024 + (j & 3);
-    if (c < V) win_update(bv, bi, v[j], c);
-  }
-  return bi >= 0 ? win_key(bv, (uint32_t)bi) : 0ull;
-}
-
-// block-wide merge over the 4 waves; the result is valid in thread 0
-__device__ __forceinline__ void block_merge_ms(float& m, float& s) {
-  __shared__ float sm[4], ss[4];
-  wave_lse_merge_dpp(m, s);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) {
-    sm[wave] = m;
-    ss[wave] = s;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-#pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w) lse_merge(m, s, sm[w], ss[w]);
-  }
-}
 
 __device__ __forceinline__ unsigned long long block_max_key(unsigned long long key) {
   __shared__ unsigned long long sk[4];
@@ -216,15 +126,13 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 // One wave combines nrows consecutive rows of NC packed partials, partial
 // (row, chunk) at p[chunk * cstride + row]: the max of the words (keys) or
-// their (max, sum exp) merge. Partials are read with device-scope atomic
-// loads when coherent (published inside the same launch), else with plain
-// loads (stored by an earlier launch), and staged in LDS a page at a time (all loads of a page in flight
-// together); each row of the page is then merged by a group of lanes (a
+// their (max, sum exp) merge. Partials are plain loads (stored by the
+// statistics launch before), staged in LDS a page at a time (all loads of a
+// page in flight together); each row of the page is then merged by a group of lanes (a
 // power of two) and the group's results by shuffles. Results go to
 // om / os / okey [row].
 __device__ void wave_combine(const unsigned long long* p, size_t cstride, int nrows, int NC, bool keys,
-                             unsigned long long* stage, float* om, float* os, unsigned long long* okey,
-                             bool coherent) {
+                             unsigned long long* stage, float* om, float* os, unsigned long long* okey) {
   const int lane = threadIdx.x & 63;
   const int cpp = NC < kStage ? NC : kStage;  // chunks per page
   const int rpp = kStage / cpp;               // rows per page, >= 1
@@ -248,7 +156,7 @@ __device__ void wave_combine(const unsigned long long* p, size_t cstride, int nr
             t = t < n ? t : n - 1;
             const int rr = t / nc, cc = t - rr * nc;
             const unsigned long long* q = p + (size_t)(c0 + cc) * cstride + (r0 + rr);
-            w[u] = coherent ? __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *q;
+            w[u] = *q;
           }
         }
 #pragma unroll
@@ -356,17 +264,13 @@ __device__ void decide(const VerifyArgs& a, int b, int sl, ReqLds& L) {
 }
 
 // Combine every partial of request b, write the row statistics and, without
-// top-p, decide. Run by one wave: either wave 0 of the statistics pass's last
-// work-group of the request (counted: it resets the request's arrival
-// counter), or a work-group of its own after the whole pass (the partials are
-// then plain stores of the finished pass). Either way block 0 of each target
-// row has recorded the target and cache logits at the draft tokens.
-__device__ void combine_request(const VerifyArgs& a, int b, int sl, ReqLds& L, unsigned long long* stage,
-                                bool counted) {
+// top-p, decide. Run by one wave after the whole statistics pass; block 0 of
+// each target row has recorded the target and cache logits at the draft
+// tokens.
+__device__ void combine_request(const VerifyArgs& a, int b, int sl, ReqLds& L, unsigned long long* stage) {
   const int K = a.K, NC = a.NC;
   const int lane = threadIdx.x & 63;
   if (sl < 0) {  // padding request: nothing was published
-    if (counted && lane == 0) atomicExch(a.cnt + verify_counter_index(b), 0u);
     if (a.decide) finish_padding(a, b);
     return;
   }
@@ -389,15 +293,13 @@ __device__ void combine_request(const VerifyArgs& a, int b, int sl, ReqLds& L, u
     if (greedy) {
       L.x[lane] = x0;
     } else {
-      const unsigned long long w =
-          counted ? __hip_atomic_load(a.tq + b * K + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : a.tq[b * K + lane];
+      const unsigned long long w = a.tq[b * K + lane];
       L.x[lane] = (x0 == -1) ? -1 : ((x0 < 0 || x0 >= a.V) ? 0 : x0);
       L.tx[lane] = unpack_m(w);
       L.cx[lane] = unpack_s(w);
     }
   }
-  wave_combine(a.tpart + (size_t)b * (K + 1), (size_t)a.B * (K + 1), K + 1, NC, greedy, stage, L.m, L.lz, L.key,
-               counted);
+  wave_combine(a.tpart + (size_t)b * (K + 1), (size_t)a.B * (K + 1), K + 1, NC, greedy, stage, L.m, L.lz, L.key);
   if (lane <= K) {
     const float s = L.lz[lane];
     const float lz = (s != s) ? NAN : __logf(s);
@@ -405,7 +307,7 @@ __device__ void combine_request(const VerifyArgs& a, int b, int sl, ReqLds& L, u
     a.rowstat[b * (K + 1) + lane] = RowStat{L.m[lane], lz, L.key[lane]};
   }
   if (a.qpart && !greedy) {
-    wave_combine(a.qpart + (size_t)b * K, (size_t)a.B * K, K, NC, false, stage, L.qm, L.lq, L.qkey, counted);
+    wave_combine(a.qpart + (size_t)b * K, (size_t)a.B * K, K, NC, false, stage, L.qm, L.lq, L.qkey);
     if (lane < K) {
       const float s = L.lq[lane];
       const float lq = (s != s) ? NAN : L.qm[lane] + __logf(s);
@@ -417,91 +319,11 @@ __device__ void combine_request(const VerifyArgs& a, int b, int sl, ReqLds& L, u
     L.lq[lane] = lq;
     a.qlse[b * K + lane] = lq;
   }
-  if (counted && lane == 0) atomicExch(a.cnt + verify_counter_index(b), 0u);
   wave_lds_sync();
   if (a.decide) decide(a, b, sl, L);
 }
 
-// The counting statistics pass (top-p path): one work-group per (row,
-// block); grid (NC, rows) with rows = B(K+1) target rows, then B*K cache
-// rows when draft_lse is null, split over y and z (y at most 32768). The
-// request's last-arriving work-group combines.
-__global__ __launch_bounds__(kThreads) void stats_count_kernel(VerifyArgs a) {
-  const int chunk = blockIdx.x;
-  const int row = (int)blockIdx.z * (int)gridDim.y + (int)blockIdx.y;
-  const int K = a.K, V = a.V, NC = a.NC;
-  const int n_t = a.B * (K + 1);
-  const int n_rows = n_t + (a.qpart ? a.B * K : 0);
-  if (row >= n_rows) return;
-  const bool is_target = row < n_t;
-  const int b = is_target ? row / (K + 1) : (row - n_t) / K;
-  const int c0 = chunk * kStatsChunk;
-  unsigned long long* slot = nullptr;
-  unsigned long long word = 0ull;
-  const int sl = verify_slot(a, b);  // -1: padding request (its blocks only arrive)
-  if (is_target && sl >= 0) {
-    // the row's loads go out first: nothing about them depends on T, and a
-    // branch on T placed above them would hold them behind the load of T
-    float v[kPerThread];
-    load_block<false>(a.target + (long long)row * a.target_rs, V, c0, a.vec_target != 0, 0.0f, v);
-    asm volatile("" ::: "memory");
-    const float T = a.temp[sl];
-    const bool greedy = !(T > 0.0f);
-    if (greedy) {
-      word = block_max_key(thread_key(v, c0, V));
-    } else {
-      float m, s;
-      thread_stats(v, c0, V, T, 1.0f / T, m, s);
-      block_merge_ms(m, s);
-      word = pack_ms(m, s);
-    }
-    slot = a.tpart + (size_t)chunk * n_t + row;
-  } else if (!is_target && sl >= 0 && a.temp[sl] > 0.0f) {
-    const float T = a.temp[sl];
-    const int q = row - n_t, k = q - b * K;
-    const long long off = (long long)verify_cache_row(a, b, sl) * a.cache_rs + (long long)k * a.cache_ss;
-    float v[kPerThread];
-    if (a.cache_bf16)
-      load_block<true>((const uint16_t*)a.cache + off, V, c0, a.vec_cache != 0, 0.0f, v);
-    else
-      load_block<false>((const float*)a.cache + off, V, c0, a.vec_cache != 0, 0.0f, v);
-    float m, s;
-    thread_stats(v, c0, V, T, 1.0f / T, m, s);
-    block_merge_ms(m, s);
-    word = pack_ms(m, s);
-    slot = a.qpart + (size_t)chunk * ((size_t)a.B * K) + q;
-  }
-  // waves 1..3 are done; wave 0 publishes and, if it is the request's last
-  // arrival, combines
-  if (threadIdx.x >= 64) return;
-  __shared__ ReqLds L;
-  __shared__ unsigned long long stage[kStage];
-  int last = 0;
-  if (threadIdx.x == 0) {
-    if (slot) {
-      const unsigned long long prev = atomicExch(slot, word);
-      asm volatile("" ::"v"(prev));  // keep the returning form
-    }
-    // block 0 of target row k < K of a sampled request also publishes the
-    // target and cache logits at draft token k, for the accept test
-    const int k = row - b * (K + 1);
-    if (is_target && chunk == 0 && k < K && sl >= 0 && a.temp[sl] > 0.0f) {
-      int x;
-      float tx, cx;
-      draft_point(a, b, sl, k, x, tx, cx);
-      const unsigned long long prev = atomicExch(a.tq + b * K + k, pack_ms(tx, cx));
-      asm volatile("" ::"v"(prev));
-    }
-    wait_vmem();
-    const unsigned n_wg = (unsigned)NC * (unsigned)(K + 1 + (a.qpart ? K : 0));
-    last = atomicAdd(a.cnt + verify_counter_index(b), 1u) == n_wg - 1;
-  }
-  last = __shfl(last, 0);
-  if (!last) return;
-  combine_request(a, b, sl, L, stage, true);
-}
-
-// ---- statistics without arrival counting: one wave per (row, block) ----
+// ---- statistics: one wave per (row, block) ----
 constexpr int kWavePer = kStatsChunk / 64;  // values per lane: columns c0 + 256 i + 4 lane + e
 
 // The lane's kWavePer values of one block; when the whole block exists and
@@ -646,7 +468,7 @@ __global__ __launch_bounds__(64) void combine_kernel(VerifyArgs a) {
   __shared__ ReqLds L;
   __shared__ unsigned long long stage[kStage];
   const int b = blockIdx.x;
-  combine_request(a, b, verify_slot(a, b), L, stage, false);
+  combine_request(a, b, verify_slot(a, b), L, stage);
 }
 
 // With top-p: one wave per request after the top-p kernel.
@@ -901,14 +723,11 @@ __global__ void debug_gumbel_kernel(int n, const uint32_t* words, float* g) {
 
 }  // namespace
 
-hipError_t launch_verify_stats(const VerifyArgs& a, bool last_arrival, hipStream_t st) {
+hipError_t launch_verify_stats(const VerifyArgs& a, hipStream_t st) {
   const int rows = a.B * (a.K + 1) + (a.qpart ? a.B * a.K : 0);
   const int gy = rows < 32768 ? rows : 32768;
   const int gz = (rows + gy - 1) / gy;
-  if (last_arrival)
-    hipLaunchKernelGGL(stats_count_kernel, dim3(a.NC, gy, gz), dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL(stats_wave_kernel, dim3((a.NC + 3) / 4, gy, gz), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL(stats_wave_kernel, dim3((a.NC + 3) / 4, gy, gz), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
